@@ -1,0 +1,325 @@
+"""Pins of the oracle's RMSNorm family against things other than the oracle itself: torch CPU
+float64 library routines (rms_norm, autograd), closed forms, invariants, central finite
+differences, exactly rounded sums (math.fsum), and reductions of one operation to another."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import rmsnorm as O
+
+RNG = np.random.default_rng(7)
+
+
+def bf16_values(shape, std=1.0, mean=0.0):
+    return F.bf16_round(RNG.normal(mean, std, shape))
+
+
+def torch_rms_norm64(x, w_eff, eps):
+    """torch CPU float64 RMSNorm with the same FP32 eps (library routine)."""
+    eps32 = float(np.float32(eps))
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return torch.nn.functional.rms_norm(t, (x.shape[-1],), weight=torch.from_numpy(w_eff),
+                                        eps=eps32).numpy()
+
+
+# ----------------------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("hidden", [8, 128, 3072, 4096])
+@pytest.mark.parametrize("bias", [0.0, 1.0])
+def test_rmsnorm_matches_torch_rms_norm(hidden, bias):
+    x = bf16_values((33, hidden))
+    w = bf16_values((hidden,), std=0.3, mean=0.2)
+    n = O.rmsnorm(x, w, bias, 1e-6)
+    ref = torch_rms_norm64(x, F.f32_round(w + bias), 1e-6)
+    np.testing.assert_allclose(n.y_exact, ref, rtol=1e-13, atol=0)
+    # rstd is the FP32 rounding of the reciprocal RMS torch would use.
+    r = 1 / np.sqrt(np.mean(x * x, axis=1) + float(np.float32(1e-6)))
+    np.testing.assert_allclose(n.r64, r, rtol=1e-14)
+    assert (n.rstd == r.astype(np.float32).astype(np.float64)).all()
+
+
+def test_constant_row_closed_form():
+    # x_j = c, eps = 0: r = 1/|c| exactly and y_j = sign(c) * w_j exactly.
+    for c in [1.0, -2.0, 0.25, 2.0 ** -20, -(2.0 ** 40)]:
+        x = np.full((1, 256), c)
+        w = bf16_values((256,))
+        n = O.rmsnorm(x, w, 0.0, 0.0)
+        assert n.rstd[0] == 1 / abs(c)
+        assert (n.y == np.sign(c) * w).all()
+
+
+def test_zero_row_gives_rstd_of_eps_and_zero_output():
+    # Zero input (the pages' test grid): r = 1/sqrt(FP32(1e-6)) which rounds to 1000.0 in FP32.
+    n = O.rmsnorm(np.zeros((3, 64)), bf16_values((64,)), 0.0, 1e-6)
+    assert (n.rstd == 1000.0).all()
+    assert (n.y == 0).all()
+
+
+@pytest.mark.parametrize("k", [-30, -7, 1, 13, 40])
+def test_power_of_two_scale_invariance_is_exact(k):
+    # With eps = 0, y(2^k x) is bit-identical to y(x) and rstd scales by exactly 2^-k.
+    x = bf16_values((16, 512))
+    w = bf16_values((512,))
+    a = O.rmsnorm(x, w, 0.0, 0.0)
+    b = O.rmsnorm(x * 2.0 ** k, w, 0.0, 0.0)
+    assert (a.y == b.y).all()
+    assert (b.rstd == a.rstd * 2.0 ** -k).all()
+
+
+@pytest.mark.parametrize("k", [-10, 10])
+def test_scale_invariance_with_eps_scaled_alongside(k):
+    # The pages test inputs scaled by about 1e-3 and 1e3 (norm guide §6.5).  Exactly:
+    # y(2^k x, 4^k eps) is bit-identical to y(x, eps), and rstd scales by 2^-k.
+    x = bf16_values((64, 1024))
+    w = bf16_values((1024,))
+    a = O.rmsnorm(x, w, 0.0, 1e-6)
+    b = O.rmsnorm(x * 2.0 ** k, w, 0.0, float(np.float32(1e-6)) * 4.0 ** k)
+    assert (a.y == b.y).all()
+    assert (b.rstd == a.rstd * 2.0 ** -k).all()
+
+
+def test_hidden_one_brute_force_over_every_bf16_value():
+    # H = 1, eps = 0: x / sqrt(x^2) = sign(x), so y = sign(x) * w for every finite nonzero x.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = F.bf16_bits_to_f64(bits)
+    x = x[np.isfinite(x) & (x != 0)].reshape(-1, 1)
+    w = np.array([0.75])
+    n = O.rmsnorm(x, w, 0.0, 0.0)
+    assert (n.y[:, 0] == np.sign(x[:, 0]) * 0.75).all()
+
+
+def test_gemma_bias_is_weight_plus_one():
+    # gemma_rmsnorm = rmsnorm with (w + 1) (norm guide §2.2): checked against torch with the
+    # weight w+1, and equal bitwise to the plain form given FP32(w + 1) as the weight.
+    x = bf16_values((20, 768))
+    w = bf16_values((768,), std=0.1)
+    g = O.rmsnorm(x, w, 1.0, 1e-6)
+    np.testing.assert_allclose(g.y_exact, torch_rms_norm64(x, w + 1.0, 1e-6), rtol=1e-13)
+    p = O.rmsnorm(x, F.f32_round(w + 1.0), 0.0, 1e-6)
+    assert (g.y == p.y).all() and (g.rstd == p.rstd).all()
+
+
+def test_residual_add_matches_torch_bf16_add_and_add_then_norm():
+    xt = torch.randn(64, 1024).to(torch.bfloat16)
+    rt = (torch.randn(64, 1024) * 3).to(torch.bfloat16)
+    xt[0, :8] = torch.tensor([1e-30, -1e30, 3.0, 0.0, -0.0, 2.0 ** -8, 1.0, 65504.0])
+    rt[0, :8] = torch.tensor([1.0, 1e30, -3.0, -0.0, -0.0, 1.0, 2.0 ** -9, 1.0])
+    x = xt.double().numpy()
+    r = rt.double().numpy()
+    w = bf16_values((1024,), mean=1.0, std=0.1)
+    fa = O.fused_add_rmsnorm(x, r, w, 0.0, 1e-6)
+    ref = (xt + rt).double().numpy()  # torch CPU BF16 add: FP32 sum rounded once to BF16
+    assert (fa.h_new == ref).all()
+    # "add, then rmsnorm": the fused result equals rmsnorm of the BF16 sum.
+    assert (fa.norm.y == O.rmsnorm(ref, w, 0.0, 1e-6).y).all()
+
+
+def test_static_fp8_known_codes():
+    # Constant positive row, eps = 0: y_j = w_j exactly, scale 1 -> code = e4m3(w_j).
+    w = np.array([1.0625, 432.0, 500.0, -1.1875, 0.5, 2.0 ** -10, 3 * 2.0 ** -10, 448.0])
+    x = np.full((2, w.size), 3.0)
+    n, q = O.rmsnorm_quant(x, w, 1.0, 0.0, 0.0)
+    assert list(q.q[0]) == [0x38, 0x7E, 0x7E, 0xBA, 0x30, 0x00, 0x02, 0x7E]
+    assert q.tie[0].tolist() == [True, True, False, True, False, True, True, False]
+    # Division by the scale: scale 2 halves every value before rounding.
+    _, q2 = O.rmsnorm_quant(x, w * 2, 2.0, 0.0, 0.0)
+    assert (q2.q == q.q).all()
+
+
+def test_static_fp8_against_torch_cast_in_range():
+    x = bf16_values((32, 512))
+    w = bf16_values((512,), mean=1.0, std=0.1)
+    fa, q = O.fused_add_rmsnorm_quant(x, bf16_values((32, 512)), w, 0.04, 0.0, 1e-6)
+    v32 = (fa.norm.y_exact / float(np.float32(0.04)))
+    assert np.abs(v32).max() < 448
+    ref = torch.from_numpy(v32.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    agree = F.codes_equal_e4m3(q.q, ref)
+    assert (agree | q.tie).all()
+
+
+# ----------------------------------------------------------------------------- 1x128 blocks
+
+def test_block_quant_properties():
+    x = bf16_values((24, 1024))
+    r = bf16_values((24, 1024))
+    x[3, :128] = 5.0                     # a block of one repeated value
+    r[3, :128] = 0.0
+    w = bf16_values((1024,), mean=1.0, std=0.1)
+    w[:128] = 1.0
+    b = O.fused_add_rmsnorm_fp8_block_quant(x, r, w, 0.0, 1e-6)
+    vals = F.e4m3_code_to_f64(b.q)
+    assert np.abs(vals).max() <= 448
+    blocks = np.abs(b.normed.reshape(24, 8, 128))
+    amax = blocks.max(axis=2)
+    # The amax element maps to exactly +-448.
+    qa = np.abs(vals.reshape(24, 8, 128))
+    at_max = blocks == amax[:, :, None]
+    assert (qa[at_max] == 448).all()
+    assert (qa[3, 0] == 448).all()
+    # The scale is the FP32 rounding of amax/448, checked with exact rationals.
+    from fractions import Fraction
+    for a, s in zip(amax.ravel()[:64], b.scale.ravel()[:64]):
+        exact = Fraction(float(a)) / 448
+        lo = np.float32(float(exact))
+        cands = [np.nextafter(lo, np.float32(-1)), lo, np.nextafter(lo, np.float32(1e30))]
+        best = min(cands, key=lambda c: abs(Fraction(float(c)) - exact))
+        assert s == float(best)
+    # Dequantised codes reproduce the BF16 normed values to FP8 precision (3 fraction bits).
+    deq = O.dequantize_blocks(b.q, b.scale)
+    big = np.abs(b.normed) > amax.repeat(128, axis=1) * 2.0 ** -6
+    rel = np.abs(deq - b.normed)[big] / np.abs(b.normed)[big]
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
+def test_block_quant_zero_block():
+    x = np.zeros((2, 256))
+    b = O.fused_add_rmsnorm_fp8_block_quant(x, np.zeros((2, 256)), np.ones(256), 0.0, 1e-6)
+    assert (b.scale == 0).all() and (b.q == 0).all()
+
+
+# ----------------------------------------------------------------------------- AdaRMSNorm
+
+def test_ada_matches_torch_float64():
+    rows, dim = 12, 384
+    x = bf16_values((rows, dim))
+    w = bf16_values((dim,), mean=1.0, std=0.1)
+    style = bf16_values((rows, 3 * dim))
+    a, out = O.ada_rms_norm(x, w, style, 1e-6)
+    n = torch_rms_norm64(x, w, 1e-6)
+    ref = n * (1 + style[:, :dim]) + style[:, dim:2 * dim]
+    np.testing.assert_allclose(a.o_exact, ref, rtol=1e-12, atol=1e-14)
+    assert (a.gate_out == style[:, 2 * dim:]).all()
+    assert (out == F.bf16_round(a.o_exact)).all()
+
+
+def test_ada_reduces_to_fused_add_quant():
+    # style scale = shift = 0 and gate = 1: the gated path is fused_add_rmsnorm_quant.
+    rows, dim = 16, 512
+    x, r = bf16_values((rows, dim)), bf16_values((rows, dim))
+    w = bf16_values((dim,), mean=1.0, std=0.1)
+    style = np.zeros((rows, 3 * dim))
+    style[:, 2 * dim:] = bf16_values((rows, dim))
+    a, q = O.gate_residual_ada_norm_fp8(r, x, np.ones((rows, dim)), w, style, 0.04, 1e-6)
+    fa, qf = O.fused_add_rmsnorm_quant(x, r, w, 0.04, 0.0, 1e-6)
+    assert (a.h == fa.h_new).all()
+    assert (q.q == qf.q).all()
+
+
+def test_ada_broadcast_equals_repeated_style():
+    rows, dim = 9, 256
+    x, r, g = bf16_values((rows, dim)), bf16_values((rows, dim)), bf16_values((rows, dim))
+    w = bf16_values((dim,))
+    s1 = bf16_values((1, 3 * dim))
+    a1, q1 = O.gate_residual_ada_norm_fp8(r, x, g, w, s1, 0.04, 1e-6)
+    a2, q2 = O.gate_residual_ada_norm_fp8(r, x, g, w, np.repeat(s1, rows, 0), 0.04, 1e-6)
+    assert (q1.q == q2.q).all() and (a1.gate_out == a2.gate_out).all()
+
+
+def test_gated_residual_matches_torch_fp32_fma():
+    # residual + x*gate: the BF16*BF16 product is exact in FP32, so torch's FP32
+    # r + x*g has one rounding, like an FMA; then BF16.
+    xt, gt, rt = (torch.randn(50000) * 4).to(torch.bfloat16), torch.randn(50000).to(torch.bfloat16), \
+        torch.randn(50000).to(torch.bfloat16)
+    ref = (rt.float() + xt.float() * gt.float()).to(torch.bfloat16).double().numpy()
+    got = O.gated_residual(rt.double().numpy(), xt.double().numpy(), gt.double().numpy())
+    assert (got == ref).all()
+
+
+# ----------------------------------------------------------------------------- training
+
+def _autograd64(x, w_eff, g, eps):
+    xt = torch.from_numpy(x.copy()).requires_grad_(True)
+    wt = torch.from_numpy(w_eff.copy()).requires_grad_(True)
+    eps32 = float(np.float32(eps))
+    y = xt * torch.rsqrt((xt * xt).mean(dim=1, keepdim=True) + eps32) * wt
+    y.backward(torch.from_numpy(g))
+    return xt.grad.numpy(), wt.grad.numpy()
+
+
+@pytest.mark.parametrize("bias", [0.0, 1.0])
+def test_backward_matches_torch_autograd(bias):
+    rows, hidden = 40, 640
+    x, g = bf16_values((rows, hidden)), bf16_values((rows, hidden))
+    w = bf16_values((hidden,), std=0.02) if bias else bf16_values((hidden,), mean=1.0, std=0.1)
+    w_eff = F.f32_round(w + bias)
+    fwd = O.train_forward(x, w, bias, 1e-6)
+    # With the unrounded r the oracle's formulas must equal autograd's gradients.
+    b = O.train_backward(g, x, w, fwd.r64, bias)
+    dx_ref, dw_ref = _autograd64(x, w_eff, g, 1e-6)
+    np.testing.assert_allclose(b.dx_exact, dx_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(b.dw_exact, dw_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_backward_orthogonality_invariant():
+    # sum_j x_j dx_j = r * sum_j g_j w_j x_j * eps / (ms + eps): zero at eps = 0.
+    x, g = bf16_values((8, 256)), bf16_values((8, 256))
+    w = bf16_values((256,), mean=1.0, std=0.1)
+    for eps in [0.0, 0.5]:
+        eps32 = float(np.float32(eps))
+        r = O.rms_reciprocal(x, eps)
+        b = O.train_backward(g, x, w, r)
+        lhs = np.sum(x * b.dx_exact, axis=1)
+        ms = np.mean(x * x, axis=1)
+        rhs = r * np.sum(g * w * x, axis=1) * eps32 / (ms + eps32)
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-9, atol=1e-9)
+
+
+def test_backward_central_finite_differences():
+    # Brute force on tiny rows: d/dx_k of sum_j g_j y_j and d/dw_k, in FP64.
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(3, 6))
+    w = rng.normal(size=6)
+    g = rng.normal(size=(3, 6))
+    eps = 0.25
+
+    def loss(xx, ww):
+        r = 1 / np.sqrt(np.mean(xx * xx, axis=1) + eps)
+        return np.sum(g * xx * r[:, None] * ww[None, :])
+
+    r = O.rms_reciprocal(x, eps)
+    b = O.train_backward(g, x, w, r)
+    h = 1e-6
+    for t in range(3):
+        for k in range(6):
+            e = np.zeros_like(x)
+            e[t, k] = h
+            fd = (loss(x + e, w) - loss(x - e, w)) / (2 * h)
+            assert abs(fd - b.dx_exact[t, k]) < 1e-7
+    for k in range(6):
+        e = np.zeros(6)
+        e[k] = h
+        fd = (loss(x, w + e) - loss(x, w - e)) / (2 * h)
+        assert abs(fd - b.dw_exact[k]) < 1e-7
+
+
+def test_dw_is_the_exactly_rounded_column_sum():
+    rows, hidden = 200, 64
+    x, g = bf16_values((rows, hidden)), bf16_values((rows, hidden))
+    rstd = F.f32_round(O.rms_reciprocal(x, 1e-6))
+    b = O.train_backward(g, x, np.ones(hidden), rstd)
+    for j in range(hidden):
+        s = math.fsum(float(g[t, j]) * float(x[t, j]) * float(rstd[t]) for t in range(rows))
+        assert b.dw[j] == float(np.float32(s))
+
+
+def test_backward_g_residual_adds_before_rounding():
+    x, g, gr = bf16_values((5, 128)), bf16_values((5, 128)), bf16_values((5, 128))
+    r = F.f32_round(O.rms_reciprocal(x, 1e-6))
+    a = O.train_backward(g, x, np.ones(128), r)
+    b = O.train_backward(g, x, np.ones(128), r, 0.0, gr)
+    assert np.allclose(b.dx_exact, a.dx_exact + gr, rtol=0, atol=1e-12)
+    assert (b.dw == a.dw).all()
+
+
+def test_train_forward_residual_route_is_fused_add():
+    h, u = bf16_values((10, 256)), bf16_values((10, 256))
+    w = RNG.normal(0, 0.02, 256).astype(np.float32).astype(np.float64)
+    t = O.train_forward(h, w, 1.0, 1e-6, residual=u)
+    ref = torch_rms_norm64(F.bf16_round(h + u), F.f32_round(1.0 + w), 1e-6)
+    np.testing.assert_allclose(t.y_exact, ref, rtol=1e-13)
+    assert (t.h_new == F.bf16_round(h + u)).all()

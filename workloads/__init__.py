@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+Shared by the GPU parity tests, the oracle pins, ``__graft_entry__.smoke()`` and ``bench.py``.
+This module holds none of the method's arithmetic: it draws Gaussian tensors with torch's
+CPU generator and stores them in the dtype the kernels read (BF16, or FP32 for a
+zero-centred training weight).  Nothing here normalises, adds residuals or quantises.
+
+The pages' workloads are LLM / DiT activations; Gaussians of the stated mean and spread
+stand in for them (there is no public dataset behind the pages' figures).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+BF16 = torch.bfloat16
+F32 = torch.float32
+
+
+def _gen(seed: int, tensor_id: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000003 + tensor_id)
+    return g
+
+
+def normal(shape, seed: int, tensor_id: int, mean: float = 0.0, std: float = 1.0,
+           dtype=BF16) -> torch.Tensor:
+    """N(mean, std^2) drawn in FP32 from a generator keyed by (seed, tensor_id), then stored
+    in ``dtype`` (round to nearest even for BF16)."""
+    t = torch.randn(tuple(shape), generator=_gen(seed, tensor_id), dtype=F32)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t.to(dtype)
+
+
+def with_outliers(t: torch.Tensor, seed: int, tensor_id: int, frac: float = 0.01,
+                  factor: float = 50.0) -> torch.Tensor:
+    """Scale an independent Bernoulli(frac) subset of the elements by ``factor``
+    (activation outliers), re-stored in the tensor's dtype."""
+    u = torch.rand(tuple(t.shape), generator=_gen(seed, tensor_id))
+    scaled = (t.float() * factor).to(t.dtype)
+    return torch.where(u < frac, scaled, t)
+
+
+@dataclass
+class Workload:
+    name: str
+    tensors: dict = field(default_factory=dict)
+    params: dict = field(default_factory=dict)
+
+
+# --- the five workloads ------------------------------------------------------------------
+# Each takes optional row overrides so tests can draw the same distributions at smaller
+# sizes (the oracle then finishes in seconds).
+
+def rmsnorm_fwd(rows: int = 32, hidden: int = 4096, seed: int = 1) -> Workload:
+    """rmsnorm forward: x ~ N(0,1), w ~ N(0,1), eps 1e-6 (the norm guide's §2.1 example)."""
+    return Workload("rmsnorm", {
+        "x": normal((rows, hidden), seed, 0),
+        "w": normal((hidden,), seed, 1),
+    }, {"eps": 1e-6, "rows": rows, "hidden": hidden})
+
+
+def fused_add_quant(rows: int = 8192, hidden: int = 4096, seed: int = 2,
+                    heads: int | None = None) -> Workload:
+    """fused add + RMSNorm + static FP8: x, residual ~ N(0,1); w ~ N(1, 0.1); scale 0.04.
+    With ``heads`` the activations are [rows, heads, hidden] (per-head rows)."""
+    shape = (rows, hidden) if heads is None else (rows, heads, hidden)
+    return Workload("fused_add_rmsnorm_quant", {
+        "x": normal(shape, seed, 0),
+        "residual": normal(shape, seed, 1),
+        "w": normal((hidden,), seed, 2, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "scale": 0.04, "rows": rows, "hidden": hidden, "heads": heads})
+
+
+def block_quant(rows: int = 16384, hidden: int = 7168, seed: int = 3) -> Workload:
+    """fused add + RMSNorm + 1x128 FP8 blocks: x, residual ~ N(0,1) with 1 % of the elements
+    scaled by 50; w ~ N(1, 0.1)."""
+    return Workload("fused_add_rmsnorm_fp8_block_quant", {
+        "x": with_outliers(normal((rows, hidden), seed, 0), seed, 10),
+        "residual": with_outliers(normal((rows, hidden), seed, 1), seed, 11),
+        "w": normal((hidden,), seed, 2, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "rows": rows, "hidden": hidden})
+
+
+def train(rows: int = 16384, hidden: int = 8192, seed: int = 4) -> Workload:
+    """training forward + backward with residual: h, residual, g ~ N(0,1); FP32 w ~
+    N(0, 0.02) used as the effective weight 1 + w."""
+    return Workload("train", {
+        "h": normal((rows, hidden), seed, 0),
+        "residual": normal((rows, hidden), seed, 1),
+        "w": normal((hidden,), seed, 2, std=0.02, dtype=F32),
+        "g": normal((rows, hidden), seed, 3),
+    }, {"eps": 1e-6, "w_bias": 1.0, "rows": rows, "hidden": hidden})
+
+
+def ada(rows: int = 2520, dim: int = 3072, seed: int = 5, broadcast: bool = False) -> Workload:
+    """AdaRMSNorm gated residual + static FP8: x, residual, gate ~ N(0,1); weight ones;
+    style ~ N(0,1) of (rows, 3*dim), or (1, 3*dim) when broadcast; scale 0.04."""
+    style_rows = 1 if broadcast else rows
+    return Workload("ada", {
+        "x": normal((rows, dim), seed, 0),
+        "residual": normal((rows, dim), seed, 1),
+        "gate": normal((rows, dim), seed, 2),
+        "w": torch.ones((dim,), dtype=BF16),
+        "style": normal((style_rows, 3 * dim), seed, 3 + (100 if broadcast else 0)),
+    }, {"eps": 1e-6, "scale": 0.04, "rows": rows, "dim": dim, "broadcast": broadcast})
