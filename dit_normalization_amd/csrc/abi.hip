@@ -1,0 +1,488 @@
+// C ABI of the RMSNorm family (include/dnorm.h): host-side argument checks, row-tier
+// selection by hidden size, persistent-grid sizing, and the kernel launches.
+//
+// Every check runs before the first HIP call, so a rejected call touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "dn_launch.h"
+#include "dnorm.h"
+
+using namespace dn;
+
+namespace {
+
+constexpr int kMaxHidden = 32768;
+// Row strides are bounded so that the rows one wave touches in a step (at most 32) span
+// less than 2^30 bytes: buffer descriptors carry 32-bit record counts.
+constexpr int64_t kMaxStride = (int64_t)1 << 24;
+// The effective weight is staged in LDS up to this many 16-byte column vectors (32 KiB
+// of FP32 per block); wider rows read it from global memory (L2-resident) instead.
+constexpr int kMaxLdsWeightVectors = 1024;
+
+thread_local std::string g_error;
+std::atomic<int> g_force_tpr{0};
+
+dn_status fail(dn_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dn_status check_shape(int64_t rows, int64_t hidden, int64_t multiple, const char* what) {
+  if (rows < 0) return fail(DN_ERR_SHAPE, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (hidden <= 0 || hidden > kMaxHidden)
+    return fail(DN_ERR_SHAPE, "%s must be in [1, %d] (got %lld)", what, kMaxHidden,
+                (long long)hidden);
+  if (hidden % multiple != 0)
+    return fail(DN_ERR_UNSUPPORTED, "%s must be a multiple of %lld (got %lld)", what,
+                (long long)multiple, (long long)hidden);
+  return DN_OK;
+}
+
+// A [rows, hidden] matrix of BF16 (elem = 2) or FP8 (elem = 1) with a row stride in
+// elements: 16-byte vectors of the row must stay aligned.
+dn_status check_matrix(const void* p, int64_t stride, int64_t hidden, int elem,
+                       const char* name) {
+  if (!p) return fail(DN_ERR_NULL, "%s must not be NULL", name);
+  if (stride < hidden)
+    return fail(DN_ERR_SHAPE, "%s row stride %lld is smaller than the row width %lld", name,
+                (long long)stride, (long long)hidden);
+  const size_t base_align = elem == 2 ? 16 : 8;
+  if (!aligned(p, base_align))
+    return fail(DN_ERR_ALIGN, "%s must be %zu-byte aligned", name, base_align);
+  if (stride % 8 != 0)
+    return fail(DN_ERR_ALIGN, "%s row stride %lld must be a multiple of 8 elements", name,
+                (long long)stride);
+  if (stride > kMaxStride)
+    return fail(DN_ERR_SHAPE, "%s row stride %lld exceeds %lld elements", name,
+                (long long)stride, (long long)kMaxStride);
+  return DN_OK;
+}
+
+dn_status check_weight(const void* w, int w_dtype) {
+  if (w_dtype != DN_WEIGHT_BF16 && w_dtype != DN_WEIGHT_F32)
+    return fail(DN_ERR_DTYPE, "w_dtype must be DN_WEIGHT_BF16 (0) or DN_WEIGHT_F32 (1), got %d",
+                w_dtype);
+  if (!w) return fail(DN_ERR_NULL, "w must not be NULL");
+  if (!aligned(w, 16)) return fail(DN_ERR_ALIGN, "w must be 16-byte aligned");
+  return DN_OK;
+}
+
+dn_status check_f32(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(DN_ERR_NULL, "%s must not be NULL", name) : DN_OK;
+  if (!aligned(p, 4)) return fail(DN_ERR_ALIGN, "%s must be 4-byte aligned", name);
+  return DN_OK;
+}
+
+#define DN_CHECK(expr)              \
+  do {                              \
+    const dn_status s_ = (expr);    \
+    if (s_ != DN_OK) return s_;     \
+  } while (0)
+
+// ------------------------------------------------------------------ device properties
+
+struct DeviceCache {
+  std::mutex mu;
+  std::map<int, int> cus;
+  std::map<std::tuple<int, const void*, size_t>, int> occ;
+};
+
+DeviceCache& cache() {
+  static DeviceCache c;
+  return c;
+}
+
+dn_status resident_blocks(const void* kernel, int nt, size_t lds, int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DN_ERR_HIP, "hipGetDevice failed");
+  DeviceCache& c = cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  auto it = c.cus.find(dev);
+  if (it == c.cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return fail(DN_ERR_HIP, "cannot read the compute-unit count of device %d", dev);
+    it = c.cus.emplace(dev, n).first;
+  }
+  const auto key = std::make_tuple(dev, kernel, lds);
+  auto ot = c.occ.find(key);
+  if (ot == c.occ.end()) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, lds) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    ot = c.occ.emplace(key, per_cu).first;
+  }
+  *out = it->second * ot->second;
+  return DN_OK;
+}
+
+// ------------------------------------------------------------------ forward dispatch
+
+int pick_fwd_tier(int nvec, int limit, int forced) {
+  for (int t = 0; t < kFwdTierCount; ++t) {
+    const TierShape s = fwd_tier_shape(t);
+    if (s.vmax > limit || s.tpr * s.vmax < nvec) continue;
+    if (forced && s.tpr != forced) continue;
+    return t;
+  }
+  return forced ? pick_fwd_tier(nvec, limit, 0) : -1;
+}
+
+template <int IN, int EPI>
+dn_status launch_fwd(FwdParams p, hipStream_t stream) {
+  p.nvec = p.hidden / 8;
+  const int tier = pick_fwd_tier(p.nvec, fwd_vmax_limit(IN, EPI), g_force_tpr.load());
+  if (tier < 0) return fail(DN_ERR_SHAPE, "hidden %d is too wide", p.hidden);
+  const TierShape s = fwd_tier_shape(tier);
+  const int g = s.nt / s.tpr;
+  const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;
+  p.w_in_lds = p.nvec <= kMaxLdsWeightVectors;
+  const size_t lds = fwd_lds_bytes(p.nvec, p.w_in_lds, g, wpr, s.r);
+
+  const void* kernel = nullptr;
+  if (fwd_launch<IN, EPI>(p, tier, 0, 0, nullptr, &kernel) != hipSuccess || !kernel)
+    return fail(DN_ERR_HIP, "no kernel instance for tier %d", tier);
+  int capacity = 0;
+  DN_CHECK(resident_blocks(kernel, s.nt, lds, &capacity));
+  const int64_t per_iter = (int64_t)g * s.r;
+  const int64_t needed = (p.rows + per_iter - 1) / per_iter;
+  const int grid = (int)(needed < capacity ? needed : capacity);
+  const hipError_t e = fwd_launch<IN, EPI>(p, tier, grid > 0 ? grid : 1, lds, stream, nullptr);
+  if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return DN_OK;
+}
+
+FwdParams base_params(int64_t rows, int64_t hidden, float eps) {
+  FwdParams p{};
+  p.rows = rows;
+  p.hidden = (int)hidden;
+  p.eps = eps;
+  return p;
+}
+
+// ------------------------------------------------------------------ backward dispatch
+
+int pick_bwd_tier(int nvec) {
+  for (int t = 0; t < kBwdTierCount; ++t) {
+    const TierShape s = bwd_tier_shape(t);
+    if (s.tpr * s.vmax >= nvec) return t;
+  }
+  return -1;
+}
+
+size_t workspace_bytes(int64_t hidden) {
+  if (hidden <= 0 || hidden > kMaxHidden) return 0;
+  return (size_t)kMaxChunks * (size_t)hidden * sizeof(double);
+}
+
+dn_status check_workspace(const void* ws, size_t bytes, int64_t hidden) {
+  if (!ws) return fail(DN_ERR_NULL, "workspace must not be NULL");
+  if (!aligned(ws, 256)) return fail(DN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = workspace_bytes(hidden);
+  if (bytes < need)
+    return fail(DN_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed for hidden %lld", bytes,
+                need, (long long)hidden);
+  return DN_OK;
+}
+
+int chunk_count(int64_t rows) { return (int)(rows < kMaxChunks ? rows : kMaxChunks); }
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* dn_last_error(void) { return g_error.c_str(); }
+
+int dn_max_hidden(void) { return kMaxHidden; }
+
+const char* dn_version(void) { return "dnorm 0.1 (gfx950)"; }
+
+dn_status dn_force_threads_per_row(int threads) {
+  switch (threads) {
+    case 0: case 8: case 16: case 32: case 64: case 128: case 256: case 512: case 1024:
+      g_force_tpr.store(threads);
+      return DN_OK;
+    default:
+      return fail(DN_ERR_SHAPE, "threads per row must be 0 or a power of two in [8, 1024]");
+  }
+}
+
+dn_status dn_rmsnorm(void* y, int64_t y_stride, float* rstd, const void* x, int64_t x_stride,
+                     const void* w, int w_dtype, float w_bias, int64_t rows, int64_t hidden,
+                     float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(y, y_stride, hidden, 2, "y"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(rstd, "rstd", false));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.y = static_cast<uint16_t*>(y); p.sy = y_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.rstd = rstd;
+  return launch_fwd<IN_PLAIN, EPI_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_rmsnorm_quant(uint8_t* out, int64_t out_stride, const void* x, int64_t x_stride,
+                           const void* w, int w_dtype, float w_bias, const float* scale,
+                           int64_t rows, int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(scale, "scale", true));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.q = out; p.sq = out_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.scale = scale;
+  return launch_fwd<IN_PLAIN, EPI_FP8>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_add_rmsnorm(void* x, int64_t x_stride, void* residual,
+                               int64_t residual_stride, const void* w, int w_dtype,
+                               float w_bias, float* rstd, int64_t rows, int64_t hidden,
+                               float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(rstd, "rstd", false));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.h = static_cast<uint16_t*>(residual); p.sh = residual_stride;
+  p.y = static_cast<uint16_t*>(x); p.sy = x_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.rstd = rstd;
+  return launch_fwd<IN_ADD, EPI_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_add_rmsnorm_quant(uint8_t* out, int64_t out_stride, const void* x,
+                                     int64_t x_stride, void* residual, int64_t residual_stride,
+                                     const void* w, int w_dtype, float w_bias,
+                                     const float* scale, int64_t rows, int64_t hidden,
+                                     float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(scale, "scale", true));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.h = static_cast<uint16_t*>(residual); p.sh = residual_stride;
+  p.q = out; p.sq = out_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.scale = scale;
+  return launch_fwd<IN_ADD, EPI_FP8>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_add_rmsnorm_fp8_block_quant(uint8_t* out, int64_t out_stride,
+                                               float* block_scale, int64_t scale_ld,
+                                               void* normed_out, int64_t normed_stride,
+                                               const void* x, int64_t x_stride, void* residual,
+                                               int64_t residual_stride, const void* w,
+                                               int w_dtype, float w_bias, int64_t rows,
+                                               int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 128, "hidden (1x128 blocks)"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
+  if (normed_out) DN_CHECK(check_matrix(normed_out, normed_stride, hidden, 2, "normed_out"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(block_scale, "block_scale", true));
+  if (scale_ld < rows)
+    return fail(DN_ERR_SHAPE, "scale_ld %lld is smaller than rows %lld", (long long)scale_ld,
+                (long long)rows);
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.h = static_cast<uint16_t*>(residual); p.sh = residual_stride;
+  p.y = static_cast<uint16_t*>(normed_out); p.sy = normed_stride;
+  p.q = out; p.sq = out_stride;
+  p.bscale = block_scale; p.bld = scale_ld;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  return launch_fwd<IN_ADD, EPI_FP8_BLOCK>(p, static_cast<hipStream_t>(stream));
+}
+
+static dn_status check_style(const void* style, int64_t style_stride, int64_t style_rows,
+                             int64_t rows, int64_t dim) {
+  if (!style) return fail(DN_ERR_NULL, "style must not be NULL");
+  if (style_rows != 1 && style_rows != rows)
+    return fail(DN_ERR_SHAPE, "style_rows must be 1 or rows (%lld), got %lld", (long long)rows,
+                (long long)style_rows);
+  return check_matrix(style, style_stride, 3 * dim, 2, "style");
+}
+
+dn_status dn_ada_rms_norm(void* out, int64_t out_stride, void* gate_out,
+                          int64_t gate_out_stride, const void* x, int64_t x_stride,
+                          const void* w, const void* style, int64_t style_stride,
+                          int64_t style_rows, int64_t rows, int64_t dim, float eps,
+                          dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, dim, 8, "dim"));
+  DN_CHECK(check_matrix(x, x_stride, dim, 2, "x"));
+  DN_CHECK(check_matrix(out, out_stride, dim, 2, "out"));
+  if (gate_out) DN_CHECK(check_matrix(gate_out, gate_out_stride, dim, 2, "gate_out"));
+  DN_CHECK(check_weight(w, DN_WEIGHT_BF16));
+  DN_CHECK(check_style(style, style_stride, style_rows, rows, dim));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, dim, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.y = static_cast<uint16_t*>(out); p.sy = out_stride;
+  p.gate_out = static_cast<uint16_t*>(gate_out); p.sgo = gate_out_stride;
+  p.style = static_cast<const uint16_t*>(style); p.sst = style_stride;
+  p.style_bcast = style_rows == 1;
+  p.w = w; p.w_f32 = 0; p.w_bias = 0.0f;
+  return launch_fwd<IN_PLAIN, EPI_ADA_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_gate_residual_ada_norm_fp8(void* residual, int64_t residual_stride, uint8_t* out,
+                                        int64_t out_stride, void* gate_out,
+                                        int64_t gate_out_stride, const void* x,
+                                        int64_t x_stride, const void* gate, int64_t gate_stride,
+                                        const void* w, const void* style, int64_t style_stride,
+                                        int64_t style_rows, const float* scale, int64_t rows,
+                                        int64_t dim, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, dim, 8, "dim"));
+  DN_CHECK(check_matrix(residual, residual_stride, dim, 2, "residual"));
+  DN_CHECK(check_matrix(x, x_stride, dim, 2, "x"));
+  DN_CHECK(check_matrix(gate, gate_stride, dim, 2, "gate"));
+  DN_CHECK(check_matrix(out, out_stride, dim, 1, "out"));
+  if (gate_out) DN_CHECK(check_matrix(gate_out, gate_out_stride, dim, 2, "gate_out"));
+  DN_CHECK(check_weight(w, DN_WEIGHT_BF16));
+  DN_CHECK(check_style(style, style_stride, style_rows, rows, dim));
+  DN_CHECK(check_f32(scale, "scale", true));
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, dim, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.gate = static_cast<const uint16_t*>(gate); p.sg = gate_stride;
+  p.h = static_cast<uint16_t*>(residual); p.sh = residual_stride;
+  p.q = out; p.sq = out_stride;
+  p.gate_out = static_cast<uint16_t*>(gate_out); p.sgo = gate_out_stride;
+  p.style = static_cast<const uint16_t*>(style); p.sst = style_stride;
+  p.style_bcast = style_rows == 1;
+  p.w = w; p.w_f32 = 0; p.w_bias = 0.0f;
+  p.scale = scale;
+  return launch_fwd<IN_GATED, EPI_ADA_FP8>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd, void* h_new,
+                           int64_t h_new_stride, const void* x, int64_t x_stride,
+                           const void* residual, int64_t residual_stride, const void* w,
+                           int w_dtype, float w_bias, int64_t rows, int64_t hidden, float eps,
+                           dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(y, y_stride, hidden, 2, "y"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(rstd, "rstd", true));
+  if (residual) {
+    DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+    DN_CHECK(check_matrix(h_new, h_new_stride, hidden, 2, "h_new"));
+  }
+  if (rows == 0) return DN_OK;
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.y = static_cast<uint16_t*>(y); p.sy = y_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.rstd = rstd;
+  if (!residual) return launch_fwd<IN_PLAIN, EPI_BF16>(p, static_cast<hipStream_t>(stream));
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.h = static_cast<uint16_t*>(h_new); p.sh = h_new_stride;
+  return launch_fwd<IN_ADD, EPI_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+size_t dn_train_backward_workspace_bytes(int64_t hidden) { return workspace_bytes(hidden); }
+
+dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
+                                     int64_t g_stride, const void* x, int64_t x_stride,
+                                     const void* w, int w_dtype, float w_bias,
+                                     const float* rstd, const void* g_residual,
+                                     int64_t g_residual_stride, void* workspace,
+                                     size_t workspace_bytes_, int64_t rows, int64_t hidden,
+                                     dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_matrix(dx, dx_stride, hidden, 2, "dx"));
+  DN_CHECK(check_matrix(g, g_stride, hidden, 2, "g"));
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  if (g_residual) DN_CHECK(check_matrix(g_residual, g_residual_stride, hidden, 2, "g_residual"));
+  DN_CHECK(check_weight(w, w_dtype));
+  DN_CHECK(check_f32(rstd, "rstd", true));
+  DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
+  if (rows == 0) return DN_OK;
+  BwdParams p{};
+  p.dx = static_cast<uint16_t*>(dx); p.sdx = dx_stride;
+  p.g = static_cast<const uint16_t*>(g); p.sg = g_stride;
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.gres = static_cast<const uint16_t*>(g_residual); p.sgr = g_residual_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.rstd = rstd;
+  p.part = static_cast<double*>(workspace);
+  p.rows = rows;
+  p.hidden = (int)hidden;
+  p.nvec = (int)(hidden / 8);
+  p.chunks = chunk_count(rows);
+  const int tier = pick_bwd_tier(p.nvec);
+  if (tier < 0) return fail(DN_ERR_SHAPE, "hidden %lld is too wide", (long long)hidden);
+  const TierShape s = bwd_tier_shape(tier);
+  const int gcount = s.nt / s.tpr;
+  const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;
+  const size_t lds = bwd_lds_bytes(gcount, wpr, s.r, s.nt, s.vmax);
+  const hipError_t e = bwd_partials_launch(p, tier, lds, static_cast<hipStream_t>(stream), nullptr);
+  if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return DN_OK;
+}
+
+dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes_,
+                                   int64_t rows, int64_t hidden, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  DN_CHECK(check_f32(dw, "dw", true));
+  DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
+  if (rows == 0) return DN_OK;
+  const hipError_t e = bwd_reduce_launch(dw, static_cast<const double*>(workspace), (int)hidden,
+                                         chunk_count(rows), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return DN_OK;
+}
+
+dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw, const void* g,
+                            int64_t g_stride, const void* x, int64_t x_stride, const void* w,
+                            int w_dtype, float w_bias, const float* rstd,
+                            const void* g_residual, int64_t g_residual_stride,
+                            void* workspace, size_t workspace_bytes_, int64_t rows,
+                            int64_t hidden, dn_stream_t stream) {
+  DN_CHECK(check_f32(dw, "dw", true));
+  DN_CHECK(dn_train_backward_partials(dx, dx_stride, g, g_stride, x, x_stride, w, w_dtype,
+                                      w_bias, rstd, g_residual, g_residual_stride, workspace,
+                                      workspace_bytes_, rows, hidden, stream));
+  return dn_train_backward_reduce(dw, workspace, workspace_bytes_, rows, hidden, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,247 @@
+// Training backward of RMSNorm for gfx950: dx plus a bitwise-deterministic FP32 dw.
+//
+// Stage 1 (bwd_partials_kernel): one block per fixed chunk of rows.  Every thread owns a
+// fixed set of 16-byte column vectors for the whole chunk, so its slice of dw stays in
+// FP64 registers while the block streams the chunk's rows:
+//     per row t:  c_t  = (1/H) sum_j g*w_eff*x         (lane partials in FP32, then FP64)
+//                 dx   = BF16(r*g*w_eff - x*(r^3*c_t) [+ g_residual])
+//     per column: P[chunk][j] += (g*x) * r              (exact products, FP64 sums)
+// A row is split over TPR threads (over several waves for wide rows, meeting in LDS); for
+// narrow rows several row groups run side by side and their FP64 sums are added in group
+// order at the end.  The chunk's FP64 column sums are written as one workspace row.
+//
+// Stage 2 (bwd_reduce_kernel): dw_j = FP32(sum over chunks of P[chunk][j]) in a fixed
+// order -- each wave adds a fixed contiguous range of chunk rows, then the waves' sums are
+// added in wave order.  The chunk table depends only on (rows, hidden), never on the
+// device, so dw is bitwise reproducible on any MI355X.
+#pragma once
+
+#include "dn_device.h"
+
+namespace dn {
+
+// Fixed upper bound on the number of row chunks (the workspace holds this many rows of
+// FP64 column sums).  chunks = min(rows, kMaxChunks).
+constexpr int kMaxChunks = 256;
+
+struct BwdParams {
+  uint16_t* dx;          int64_t sdx;
+  const uint16_t* g;     int64_t sg;
+  const uint16_t* x;     int64_t sx;
+  const uint16_t* gres;  int64_t sgr;    // nullable
+  const void* w;         int w_f32;      float w_bias;
+  const float* rstd;
+  double* part;                          // [chunks][hidden]
+  int64_t rows;
+  int hidden;
+  int nvec;
+  int chunks;
+};
+
+__device__ __forceinline__ void bwd_weff8(const BwdParams& p, int vec, float e[8]) {
+  if (p.w_f32) {
+    const float4* w = reinterpret_cast<const float4*>(p.w) + 2 * vec;
+    const float4 a = w[0], b = w[1];
+    e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
+    e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+  } else {
+    unpack8(ld16(reinterpret_cast<const uint16_t*>(p.w) + 8 * vec), e);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) e[k] += p.w_bias;
+}
+
+__host__ __device__ inline size_t bwd_lds_bytes(int g, int wpr, int rb, int nt, int vb) {
+  const size_t red = (size_t)2 * g * wpr * rb * sizeof(double);
+  const size_t comb = g > 1 ? (size_t)nt * vb * 8 * sizeof(double) : 0;
+  return red > comb ? red : comb;
+}
+
+template <int TPR, int VB, int RB, int NT>
+__global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
+  extern __shared__ __align__(16) unsigned char dn_lds[];
+  using Geom = RowGeom<TPR, RB, NT>;
+  constexpr int G = Geom::G;
+  constexpr int WPR = Geom::WPR;
+  constexpr int RPW = Geom::RPW;
+  constexpr int RW = TPR < 64 ? TPR : 64;
+  double* red = reinterpret_cast<double*>(dn_lds);
+
+  const Geom geo;
+  const int tid = threadIdx.x;
+  const int lane = geo.lane;
+  const int nvec = p.nvec;
+  const bool lane_ok = TPR >= 64 || lane < nvec;
+  const uint32_t row_bf16 = 2u * (uint32_t)p.hidden;
+  const int chunk = blockIdx.x;
+  const int64_t rb = (int64_t)chunk * p.rows / p.chunks;
+  const int64_t re = (int64_t)(chunk + 1) * p.rows / p.chunks;
+  const double inv_hidden = 1.0 / (double)p.hidden;
+
+  // This thread's columns are fixed for the whole chunk: weights and FP64 column sums
+  // stay in registers.
+  float we[VB][8];
+  double acc[VB][8];
+#pragma unroll
+  for (int v = 0; v < VB; ++v) {
+    const int idx = v * TPR + lane;
+    bwd_weff8(p, idx < nvec ? idx : nvec - 1, we[v]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[v][k] = 0.0;
+  }
+
+  int parity = 0;
+  for (int64_t base = rb; base < re; base += Geom::PER_ITER) {
+    const int64_t first = geo.first(base);
+    int64_t row[RB];
+    bool rok[RB];
+    float rs[RB];
+    v4u gv[RB][VB], xv[RB][VB], rv[RB][VB];
+    rsrc_t rg[RB], rx[RB], rr_[RB], rdx[RB];
+    uint32_t og[RB], ox[RB], or_[RB], odx[RB];
+    tensor_span<TPR, RB, RPW>(p.g, p.sg, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rg,
+                              og);
+    tensor_span<TPR, RB, RPW>(p.x, p.sx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rx,
+                              ox);
+    if (p.gres)
+      tensor_span<TPR, RB, RPW>(p.gres, p.sgr, 2, 16, row_bf16, first, re, lane, geo.j,
+                                lane_ok, rr_, or_);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      row[rr] = geo.row(first, rr);
+      rok[rr] = row[rr] < re;
+      rs[rr] = rok[rr] ? p.rstd[row[rr]] : 0.0f;
+#pragma unroll
+      for (int v = 0; v < VB; ++v) {
+        const uint32_t dv = (uint32_t)(v * TPR * 16);
+        gv[rr][v] = bload16(rg[rr], og[rr] + dv);
+        xv[rr][v] = bload16(rx[rr], ox[rr] + dv);
+        rv[rr][v] = v4u{0u, 0u, 0u, 0u};
+        if (p.gres) rv[rr][v] = bload16(rr_[rr], or_[rr] + dv);
+      }
+    }
+
+    // Row dot products sum_j g*w_eff*x (lanes past the row end loaded zeros).
+    double dot[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      float d = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VB; ++v) {
+        float fg[8], fx[8];
+        unpack8(gv[rr][v], fg);
+        unpack8(xv[rr][v], fx);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d = fmaf(fg[k] * we[v][k], fx[k], d);
+        keep_packed(gv[rr][v]);
+        keep_packed(xv[rr][v]);
+      }
+      dot[rr] = group_sum<RW>((double)d);
+    }
+    if constexpr (WPR > 1) {
+      const int wave_in_row = lane >> 6;
+      double* slot = red + (size_t)parity * G * WPR * RB + (size_t)geo.grp * WPR * RB;
+      if ((lane & 63) == 0) {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) slot[wave_in_row * RB + rr] = dot[rr];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        double s = 0.0;
+#pragma unroll
+        for (int w8 = 0; w8 < WPR; ++w8) s += slot[w8 * RB + rr];
+        dot[rr] = s;
+      }
+      parity ^= 1;
+    }
+
+    // dx and the FP64 column sums (rows past the chunk carry r = 0 and add nothing).
+    tensor_span<TPR, RB, RPW>(p.dx, p.sdx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok,
+                              rdx, odx);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const double r64 = (double)rs[rr];
+      const float coef = (float)(r64 * r64 * r64 * (dot[rr] * inv_hidden));
+#pragma unroll
+      for (int v = 0; v < VB; ++v) {
+        float fg[8], fx[8], fr[8], d[8];
+        unpack8(gv[rr][v], fg);
+        unpack8(xv[rr][v], fx);
+        unpack8(rv[rr][v], fr);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          d[k] = fmaf(-fx[k], coef, (fg[k] * we[v][k]) * rs[rr]) + fr[k];
+        bstore16(rdx[rr], odx[rr] + (uint32_t)(v * TPR * 16), pack8(d));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[v][k] = fma((double)(fg[k] * fx[k]), r64, acc[v][k]);
+      }
+    }
+  }
+
+  // The chunk's column sums: add the row groups' sums in group order, write one row.
+  double* out = p.part + (int64_t)chunk * p.hidden;
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int v = 0; v < VB; ++v) {
+      const int idx = v * TPR + lane;
+      if (idx < nvec) {
+        double2* o = reinterpret_cast<double2*>(out + 8 * (int64_t)idx);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = make_double2(acc[v][2 * k], acc[v][2 * k + 1]);
+      }
+    }
+  } else {
+    __syncthreads();                       // the dot-product slots are reused below
+    const int cols = TPR * VB * 8;         // columns held by one row group
+    double* comb = red;                    // [G][cols]
+#pragma unroll
+    for (int v = 0; v < VB; ++v)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        comb[(size_t)geo.grp * cols + (v * TPR + lane) * 8 + k] = acc[v][k];
+    __syncthreads();
+    for (int col = tid; col < cols && col < p.hidden; col += NT) {
+      double s = 0.0;
+      for (int gg = 0; gg < G; ++gg) s += comb[(size_t)gg * cols + col];
+      out[col] = s;
+    }
+  }
+}
+
+// Stage 2: one block per 64 columns; wave wv adds chunk rows [wv*C/NW, (wv+1)*C/NW) in
+// order, then wave 0 adds the NW wave sums in order and rounds once to FP32.
+template <int NT>
+__global__ void __launch_bounds__(NT) bwd_reduce_kernel(float* dw, const double* part,
+                                                        int hidden, int chunks) {
+  constexpr int NW = NT / 64;
+  __shared__ double red[NW][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  const int cb = wv * chunks / NW, ce = (wv + 1) * chunks / NW;
+  double s = 0.0;
+  if (col < hidden) {
+#pragma unroll 8
+    for (int c = cb; c < ce; ++c) s += part[(int64_t)c * hidden + col];
+  }
+  red[wv][lane] = s;
+  __syncthreads();
+  if (wv == 0 && col < hidden) {
+    double t = 0.0;
+#pragma unroll
+    for (int w8 = 0; w8 < NW; ++w8) t += red[w8][lane];
+    dw[col] = (float)t;
+  }
+}
+
+// (threads per row, vectors per thread, rows per group per iteration, threads per block)
+#define DN_BWD_TIERS(X)                                                         \
+  X(0, 8, 1, 4, 256)     X(1, 16, 1, 4, 256)    X(2, 32, 1, 4, 256)            \
+  X(3, 64, 1, 4, 256)    X(4, 128, 1, 4, 256)   X(5, 256, 1, 4, 256)           \
+  X(6, 512, 1, 4, 512)   X(7, 1024, 1, 4, 1024) X(8, 1024, 2, 2, 1024)         \
+  X(9, 1024, 4, 1, 1024)
+
+constexpr int kBwdTierCount = 10;
+
+}  // namespace dn

@@ -1,0 +1,212 @@
+// Device helpers for the gfx950 RMSNorm kernels: BF16 / FP8 packing, 16-byte row access,
+// and lane-group reductions.  Everything here is written for CDNA4 wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dn {
+
+// 16-byte and 8-byte register vectors (clang ext-vectors: usable in any address space).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ BF16 packing
+// A 16-byte vector holds 8 BF16 values: 4 dwords, each a pair (low half = even element).
+
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const v4u& v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values to a BF16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Hides a packed vector's value from the optimiser so that a later pass unpacks it again
+// (two VALU ops per pair) instead of keeping eight unpacked FP32 values live across a
+// reduction: halves the row's register footprint.
+__device__ __forceinline__ void keep_packed(v4u& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ v4u pack8(const float f[8]) {
+  v4u v;
+  v.x = pack_bf16x2(f[0], f[1]);
+  v.y = pack_bf16x2(f[2], f[3]);
+  v.z = pack_bf16x2(f[4], f[5]);
+  v.w = pack_bf16x2(f[6], f[7]);
+  return v;
+}
+
+// ------------------------------------------------------------------ FP8 e4m3fn packing
+// Largest finite e4m3fn magnitude; inputs are clamped to it first so every out-of-range
+// value saturates (v_med3_f32), then converted with round-to-nearest-even
+// (v_cvt_pk_fp8_f32: two values into one 16-bit half of a dword, first operand in the
+// lower byte).
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float clamp_e4m3(float v) {
+  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+}
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ v2u pack_fp8x8(const float f[8]) {
+  v2u v;
+  v.x = pack_fp8x4(f[0], f[1], f[2], f[3]);
+  v.y = pack_fp8x4(f[4], f[5], f[6], f[7]);
+  return v;
+}
+
+// ------------------------------------------------------------------ memory access
+// Rows are read and written through raw buffer descriptors (SGPRs): the descriptor's base
+// is the first row a wave touches and its record count bounds the bytes that belong to
+// the rows in flight.  Each access needs one 32-bit per-lane offset; the hardware range
+// check returns zeros for loads past the bound and drops stores past it, which is how
+// ragged row tails and rows beyond the matrix are handled without branches.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Descriptor word 3 for a raw (unswizzled, stride 0) buffer of 32-bit data on gfx9-family
+// parts (CDNA included).
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// A per-lane offset that no descriptor built here reaches (record counts stay below 2^30).
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferWord3);
+}
+
+__device__ __forceinline__ v4u bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const v4u& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off,
+      0, 0);
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, const v2u& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(
+      __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off,
+      0, 0);
+}
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Plain (flat) accesses for small side arrays (weights, per-row scalars).
+__device__ __forceinline__ v4u ld16(const uint16_t* p) {
+  return *reinterpret_cast<const v4u*>(p);
+}
+
+// Row-group geometry shared by the forward and backward kernels.
+//   TPR threads own one row; a block of NT threads has G = NT/TPR row groups and each
+//   walks R rows per step.  When TPR < 64 a wave holds RPW = 64/TPR rows side by side
+//   and takes R*RPW consecutive rows per step; when TPR >= 64 a group takes R
+//   consecutive rows, one per row slot.
+template <int TPR, int R, int NT>
+struct RowGeom {
+  static constexpr int G = NT / TPR;
+  static constexpr int RPW = TPR < 64 ? 64 / TPR : 1;
+  static constexpr int WPR = TPR > 64 ? TPR / 64 : 1;
+  static constexpr int PER_ITER = G * R;
+  int lane;   // column lane inside the row group, 0..TPR-1
+  int j;      // row slot inside the wave (TPR < 64), else 0
+  int grp;    // row group (wave-uniform when TPR >= 64)
+  int wave;   // wave inside the block (uniform)
+  __device__ __forceinline__ RowGeom() {
+    const int tid = threadIdx.x;
+    lane = tid % TPR;
+    j = TPR < 64 ? (tid & 63) / TPR : 0;
+    wave = wave_uniform(tid >> 6);
+    grp = TPR >= 64 ? wave_uniform(tid / TPR) : tid / TPR;
+  }
+  // First row of the span this wave (TPR < 64) or row group (TPR >= 64) owns in a step.
+  __device__ __forceinline__ int64_t first(int64_t base) const {
+    return TPR < 64 ? base + (int64_t)wave * R * RPW : base + (int64_t)grp * R;
+  }
+  // Row slot rr of this lane.
+  __device__ __forceinline__ int64_t row(int64_t first_row, int rr) const {
+    return TPR < 64 ? first_row + rr * RPW + j : first_row + rr;
+  }
+};
+
+// Buffer descriptors and lane offsets of one row-major tensor for the R row slots of a
+// step.  `elem` is the element size, `vec` the bytes one lane moves per access (16 for
+// BF16 vectors, 8 for FP8), `span` the bytes of a row that belong to it, `end` the first
+// row that must not be touched, and `lane_ok` false for lanes past the row's last vector.
+template <int TPR, int R, int RPW>
+__device__ __forceinline__ void tensor_span(const void* t, int64_t stride, int elem, int vec,
+                                            uint32_t span, int64_t first, int64_t end,
+                                            int lane, int j, bool lane_ok, rsrc_t (&rs)[R],
+                                            uint32_t (&off)[R]) {
+  const char* base = static_cast<const char*>(t);
+  if constexpr (TPR < 64) {
+    int64_t nvalid = end - first;
+    nvalid = nvalid < 0 ? 0 : (nvalid > R * RPW ? R * RPW : nvalid);
+    const rsrc_t r = make_rsrc(base + first * stride * elem, (uint32_t)(nvalid * stride * elem));
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      rs[rr] = r;
+      off[rr] = lane_ok ? (uint32_t)((rr * RPW + j) * stride * elem) + (uint32_t)(lane * vec)
+                        : kOutOfRange;
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int64_t row = first + rr;
+      rs[rr] = make_rsrc(base + row * stride * elem, row < end ? span : 0u);
+      off[rr] = (uint32_t)(lane * vec);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ sums of squares
+// Squares of BF16 values are exact in FP32.  Eight of them are added as a 3-level tree
+// (every product passes through at most three FP32 roundings, relative error <= 3*2^-24),
+// and the per-vector sums are carried in FP64 from there on.
+__device__ __forceinline__ float sumsq8(const float f[8]) {
+  float s01 = fmaf(f[1], f[1], f[0] * f[0]);
+  float s23 = fmaf(f[3], f[3], f[2] * f[2]);
+  float s45 = fmaf(f[5], f[5], f[4] * f[4]);
+  float s67 = fmaf(f[7], f[7], f[6] * f[6]);
+  return (s01 + s23) + (s45 + s67);
+}
+
+// Butterfly sum over aligned groups of WIDTH lanes (WIDTH a power of two <= 64).  Addition
+// is commutative, so every lane of a group ends with the same bits.
+template <int WIDTH>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_sum_f(float v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+}  // namespace dn

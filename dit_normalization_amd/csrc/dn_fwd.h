@@ -1,0 +1,350 @@
+// Forward row engine of the RMSNorm family for gfx950.
+//
+// One template covers every forward variant; two compile-time kinds select what a row
+// reads and what its epilogue writes:
+//   input  : x | x + residual (fused add) | FMA(x, gate, residual) (gated residual)
+//   output : BF16 y | FP8 at a static scale | FP8 with 1x128 block scales |
+//            AdaRMSNorm (style scale/shift, gate copy) in BF16 or FP8
+//
+// Row mapping (chosen on the host by hidden size): a row is owned by a group of TPR
+// threads.  Thread `lane` of the group owns the 16-byte column vectors lane, lane+TPR,
+// lane+2*TPR, ... (VMAX of them at most), so every load instruction of a wave reads TPR
+// consecutive 16-byte vectors of a row: fully coalesced.  TPR < 64 packs 64/TPR rows into
+// a wave; TPR = 64 gives a wave one row; TPR > 64 spreads a row over TPR/64 waves whose
+// partial sums meet in LDS.  The whole row stays in VGPRs across the reduction, so every
+// input byte is read from HBM exactly once.
+//
+// Memory traffic goes through raw buffer descriptors (see dn_device.h): one descriptor per
+// row (or per wave span of small rows) and one offset VGPR per lane; the descriptor's
+// range check zero-fills ragged tails and drops their stores.
+//
+// Blocks are persistent: the grid is sized to the resident capacity of the chip and each
+// block walks row groups with a grid stride.  The effective weight FP32(w + bias) is staged
+// once per block into LDS (two planes of float4, so lanes read consecutive 16-byte words:
+// conflict-free ds_read_b128) and read from there for every row.
+#pragma once
+
+#include "dn_device.h"
+
+namespace dn {
+
+enum InKind { IN_PLAIN = 0, IN_ADD = 1, IN_GATED = 2 };
+enum EpiKind { EPI_BF16 = 0, EPI_FP8 = 1, EPI_FP8_BLOCK = 2, EPI_ADA_BF16 = 3, EPI_ADA_FP8 = 4 };
+
+struct FwdParams {
+  const uint16_t* x;     int64_t sx;
+  const uint16_t* r;     int64_t sr;     // residual (IN_ADD, IN_GATED)
+  const uint16_t* gate;  int64_t sg;     // IN_GATED
+  const uint16_t* style; int64_t sst;    // Ada: [style_rows, 3*hidden]
+  int style_bcast;                       // Ada: one style row for every token
+  const void* w;         int w_f32;      float w_bias;
+  const float* scale;                    // FP8 static: device FP32 [1]
+  uint16_t* y;           int64_t sy;     // BF16 output (y, normed_out, Ada out); nullable
+  uint16_t* h;           int64_t sh;     // h_new output; nullable
+  uint8_t* q;            int64_t sq;     // FP8 output
+  float* bscale;         int64_t bld;    // 1x128 block scales [hidden/128][bld]
+  uint16_t* gate_out;    int64_t sgo;    // Ada gate copy; nullable
+  float* rstd;                           // nullable
+  int64_t rows;
+  int hidden;
+  int nvec;                              // hidden / 8
+  float eps;
+  int w_in_lds;                          // effective weight staged in LDS
+};
+
+// Effective weight FP32(w + bias) of one 16-byte column vector, read from global memory.
+__device__ __forceinline__ void load_weff8(const FwdParams& p, int vec, float e[8]) {
+  if (p.w_f32) {
+    const float4* w = reinterpret_cast<const float4*>(p.w) + 2 * vec;
+    const float4 a = w[0], b = w[1];
+    e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
+    e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+  } else {
+    unpack8(ld16(reinterpret_cast<const uint16_t*>(p.w) + 8 * vec), e);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) e[k] += p.w_bias;
+}
+
+// Bytes of dynamic LDS a forward launch needs.
+__host__ __device__ inline size_t fwd_lds_bytes(int nvec, int w_in_lds, int g, int wpr, int r) {
+  return (w_in_lds ? (size_t)32 * nvec : 0) + (size_t)2 * g * wpr * r * sizeof(double);
+}
+
+template <int IN, int EPI, int TPR, int VMAX, int R, int NT>
+__global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
+  extern __shared__ __align__(16) unsigned char dn_lds[];
+  using Geom = RowGeom<TPR, R, NT>;
+  constexpr int G = Geom::G;
+  constexpr int WPR = Geom::WPR;
+  constexpr int RPW = Geom::RPW;
+  constexpr int RW = TPR < 64 ? TPR : 64;        // lanes of a row inside one wave
+  constexpr bool kAda = (EPI == EPI_ADA_BF16 || EPI == EPI_ADA_FP8);
+  constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8);
+  constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8);
+
+  const Geom geo;
+  const int tid = threadIdx.x;
+  const int lane = geo.lane;
+  const int nvec = p.nvec;
+  const uint32_t row_bf16 = 2u * (uint32_t)p.hidden;   // bytes of a BF16 row
+  const uint32_t row_fp8 = (uint32_t)p.hidden;         // bytes of an FP8 row
+  // Sub-wave rows: lanes past the row's last vector take an out-of-range offset.
+  const bool lane_ok = TPR >= 64 || lane < nvec;
+  float4* wl = reinterpret_cast<float4*>(dn_lds);
+  double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)32 * nvec : 0));
+
+  if (p.w_in_lds) {
+    for (int i = tid; i < nvec; i += NT) {
+      float e[8];
+      load_weff8(p, i, e);
+      wl[i] = make_float4(e[0], e[1], e[2], e[3]);
+      wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
+    }
+    __syncthreads();
+  }
+
+  if constexpr (EPI == EPI_FP8_BLOCK) {
+    // Pad entries [rows, bld) of every block-scale column are written as zeros.
+    const int64_t pad = p.bld - p.rows;
+    if (blockIdx.x == 0 && pad > 0) {
+      const int nb = p.hidden / 128;
+      for (int64_t i = tid; i < (int64_t)nb * pad; i += NT)
+        p.bscale[(i / pad) * p.bld + p.rows + (i % pad)] = 0.0f;
+    }
+  }
+
+  float inv_scale = 1.0f;
+  if constexpr (kStaticFp8) inv_scale = 1.0f / *p.scale;
+
+  const double inv_hidden = 1.0 / (double)p.hidden;
+  const double eps = (double)p.eps;
+  int parity = 0;
+
+  for (int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER; base < p.rows;
+       base += (int64_t)gridDim.x * Geom::PER_ITER) {
+    const int64_t first = geo.first(base);
+    int64_t row[R];
+    bool rok[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      row[rr] = geo.row(first, rr);
+      rok[rr] = row[rr] < p.rows;
+    }
+
+    // 1) Issue every load of the step before any use.
+    v4u a[R][VMAX];                               // x, then h
+    v4u b[R][VMAX];                               // residual
+    v4u c[R][VMAX];                               // gate
+    v4u ssc[R][VMAX], ssh[R][VMAX], sgt[R][VMAX]; // Ada style chunks
+    {
+      rsrc_t rx[R], rres[R], rg[R], rst[R];
+      uint32_t ox[R], ores[R], og[R], ost[R];
+      tensor_span<TPR, R, RPW>(p.x, p.sx, 2, 16, row_bf16, first, p.rows, lane, geo.j, lane_ok,
+                               rx, ox);
+      if constexpr (IN != IN_PLAIN)
+        tensor_span<TPR, R, RPW>(p.r, p.sr, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                                 lane_ok, rres, ores);
+      if constexpr (IN == IN_GATED)
+        tensor_span<TPR, R, RPW>(p.gate, p.sg, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                                 lane_ok, rg, og);
+      if constexpr (kAda) {
+        if (p.style_bcast) {
+          // Every row reads the single style row.
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+            rst[rr] = make_rsrc(p.style, 3u * row_bf16);
+            ost[rr] = lane_ok ? (uint32_t)(lane * 16) : kOutOfRange;
+          }
+        } else {
+          tensor_span<TPR, R, RPW>(p.style, p.sst, 2, 16, 3u * row_bf16, first, p.rows, lane,
+                                   geo.j, lane_ok, rst, ost);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+        for (int v = 0; v < VMAX; ++v) {
+          const uint32_t dv = (uint32_t)(v * TPR * 16);
+          a[rr][v] = bload16(rx[rr], ox[rr] + dv);
+          if constexpr (IN != IN_PLAIN) b[rr][v] = bload16(rres[rr], ores[rr] + dv);
+          if constexpr (IN == IN_GATED) c[rr][v] = bload16(rg[rr], og[rr] + dv);
+          if constexpr (kAda) {
+            ssc[rr][v] = bload16(rst[rr], ost[rr] + dv);
+            ssh[rr][v] = bload16(rst[rr], ost[rr] + dv + row_bf16);
+            sgt[rr][v] = bload16(rst[rr], ost[rr] + dv + 2u * row_bf16);
+          }
+        }
+      }
+    }
+
+    // 2) h (rounded to BF16, stored early) and per-lane sums of squares of that BF16 h.
+    double ss[R];
+    {
+      rsrc_t rh[R];
+      uint32_t oh[R];
+      if constexpr (IN != IN_PLAIN)
+        tensor_span<TPR, R, RPW>(p.h, p.sh, 2, 16, p.h ? row_bf16 : 0u, first,
+                                 p.h ? p.rows : first, lane, geo.j, lane_ok, rh, oh);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        ss[rr] = 0.0;
+#pragma unroll
+        for (int v = 0; v < VMAX; ++v) {
+          float fh[8];
+          unpack8(a[rr][v], fh);
+          if constexpr (IN == IN_ADD) {
+            float fr[8];
+            unpack8(b[rr][v], fr);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) fh[k] = fh[k] + fr[k];
+          } else if constexpr (IN == IN_GATED) {
+            float fr[8], fg[8];
+            unpack8(b[rr][v], fr);
+            unpack8(c[rr][v], fg);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) fh[k] = fmaf(fh[k], fg[k], fr[k]);
+          }
+          if constexpr (IN != IN_PLAIN) {
+            a[rr][v] = pack8(fh);
+            unpack8(a[rr][v], fh);       // the norm sees the BF16 h_new
+            bstore16(rh[rr], oh[rr] + (uint32_t)(v * TPR * 16), a[rr][v]);
+          }
+          // Lanes past the row end loaded zeros: they add nothing.
+          ss[rr] += (double)sumsq8(fh);
+        }
+      }
+    }
+
+    // 3) Row sums: butterfly inside the wave, then (rows over several waves) through LDS.
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v) keep_packed(a[rr][v]);
+      ss[rr] = group_sum<RW>(ss[rr]);
+    }
+    if constexpr (WPR > 1) {
+      const int wave_in_row = lane >> 6;
+      double* slot = red + (size_t)parity * G * WPR * R + (size_t)geo.grp * WPR * R;
+      if ((lane & 63) == 0) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) slot[wave_in_row * R + rr] = ss[rr];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        double s = 0.0;
+#pragma unroll
+        for (int w8 = 0; w8 < WPR; ++w8) s += slot[w8 * R + rr];
+        ss[rr] = s;
+      }
+      parity ^= 1;
+    }
+
+    // 4) rstd = 1/sqrt(mean + eps): IEEE FP64 divide and square root, one FP32 rounding.
+    float rs[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const double r64 = 1.0 / sqrt(ss[rr] * inv_hidden + eps);
+      rs[rr] = (float)r64;
+      if (p.rstd && lane == 0 && rok[rr]) p.rstd[row[rr]] = rs[rr];
+    }
+
+    // 5) Epilogue: y = (h * r) * w_eff in FP32, then the output format.
+    rsrc_t ry[R], rq[R], rgo[R];
+    uint32_t oy[R], oq[R], ogo[R];
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_ADA_BF16 || EPI == EPI_FP8_BLOCK)
+      tensor_span<TPR, R, RPW>(p.y, p.sy, 2, 16, p.y ? row_bf16 : 0u, first,
+                               p.y ? p.rows : first, lane, geo.j, lane_ok, ry, oy);
+    if constexpr (kFp8Out)
+      tensor_span<TPR, R, RPW>(p.q, p.sq, 1, 8, row_fp8, first, p.rows, lane, geo.j, lane_ok,
+                               rq, oq);
+    if constexpr (kAda)
+      tensor_span<TPR, R, RPW>(p.gate_out, p.sgo, 2, 16, p.gate_out ? row_bf16 : 0u, first,
+                               p.gate_out ? p.rows : first, lane, geo.j, lane_ok, rgo, ogo);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v) {
+        // Keep the scheduler from hoisting every vector's weight reads to the top.
+        __builtin_amdgcn_sched_barrier(0);
+        const int idx = v * TPR + lane;
+        const int widx = idx < nvec ? idx : nvec - 1;   // ragged lanes read a valid weight
+        const uint32_t d16 = (uint32_t)(v * TPR * 16);
+        const uint32_t d8 = (uint32_t)(v * TPR * 8);
+        float fh[8], we[8], yv[8];
+        unpack8(a[rr][v], fh);
+        if (p.w_in_lds) {
+          const float4 lo = wl[widx], hi = wl[nvec + widx];
+          we[0] = lo.x; we[1] = lo.y; we[2] = lo.z; we[3] = lo.w;
+          we[4] = hi.x; we[5] = hi.y; we[6] = hi.z; we[7] = hi.w;
+        } else {
+          load_weff8(p, widx, we);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
+
+        if constexpr (EPI == EPI_BF16) {
+          bstore16(ry[rr], oy[rr] + d16, pack8(yv));
+        } else if constexpr (EPI == EPI_FP8) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
+          bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(yv));
+        } else if constexpr (EPI == EPI_FP8_BLOCK) {
+          // The BF16 normalised value is both normed_out and the quantiser's input.
+          const v4u nv = pack8(yv);
+          bstore16(ry[rr], oy[rr] + d16, nv);
+          float fn[8];
+          unpack8(nv, fn);
+          float amax = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(fn[k]));
+          amax = group_max<16>(amax);           // one 1x128 block = 16 lanes x 8 values
+          const float s = amax / kE4M3Max;      // IEEE divide: FP32(amax / 448)
+          const float rcp = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) fn[k] *= rcp;
+          bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(fn));
+          if ((lane & 15) == 0 && rok[rr] && idx < nvec)
+            p.bscale[(int64_t)(idx >> 4) * p.bld + row[rr]] = s;
+        } else {  // AdaRMSNorm epilogue
+          float fsc[8], fsh[8], o[8];
+          unpack8(ssc[rr][v], fsc);
+          unpack8(ssh[rr][v], fsh);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = fmaf(yv[k], 1.0f + fsc[k], fsh[k]);
+          if constexpr (EPI == EPI_ADA_BF16) {
+            bstore16(ry[rr], oy[rr] + d16, pack8(o));
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] *= inv_scale;
+            bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(o));
+          }
+          bstore16(rgo[rr], ogo[rr] + d16, sgt[rr][v]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- row tiers
+// (threads per row, 16-byte vectors per thread at most, rows per group per step, threads
+//  per block).  The host picks the first tier whose TPR*VMAX covers hidden/8.
+#define DN_FWD_TIERS(X)                                                         \
+  X(0, 8, 1, 4, 256)    X(1, 16, 1, 4, 256)   X(2, 32, 1, 2, 256)              \
+  X(3, 64, 1, 2, 256)   X(4, 64, 2, 1, 256)   X(5, 64, 3, 1, 256)              \
+  X(6, 64, 4, 1, 256)   X(7, 64, 6, 1, 256)   X(8, 64, 8, 1, 256)              \
+  X(9, 64, 10, 1, 256)  X(10, 64, 12, 1, 256) X(11, 64, 14, 1, 256)            \
+  X(12, 64, 16, 1, 256) X(13, 128, 4, 1, 256) X(14, 128, 8, 1, 256)            \
+  X(15, 256, 4, 1, 256) X(16, 256, 8, 1, 256) X(17, 512, 4, 1, 512)            \
+  X(18, 512, 8, 1, 512) X(19, 1024, 4, 1, 1024)
+
+constexpr int kFwdTierCount = 20;
+
+// Largest VMAX an input/epilogue combination is built with: the Ada and gated routes
+// keep up to six 16-byte vectors per column in flight, so they stop at 6.
+constexpr int fwd_vmax_limit(int in, int epi) {
+  return (in == IN_GATED || epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8) ? 6 : 16;
+}
+
+}  // namespace dn

@@ -1,0 +1,49 @@
+// Host-side launch interface between the C-ABI layer (abi.hip) and the translation units
+// that instantiate the kernels (fwd_*.hip, bwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "dn_bwd.h"
+#include "dn_fwd.h"
+
+namespace dn {
+
+struct TierShape {
+  int tpr, vmax, r, nt;
+};
+
+// Forward tier table in host form (mirrors DN_FWD_TIERS).
+inline TierShape fwd_tier_shape(int tier) {
+  switch (tier) {
+#define DN_X(i, tpr, v, r, nt) \
+  case i: return TierShape{tpr, v, r, nt};
+    DN_FWD_TIERS(DN_X)
+#undef DN_X
+  }
+  return TierShape{0, 0, 0, 0};
+}
+
+inline TierShape bwd_tier_shape(int tier) {
+  switch (tier) {
+#define DN_X(i, tpr, v, r, nt) \
+  case i: return TierShape{tpr, v, r, nt};
+    DN_BWD_TIERS(DN_X)
+#undef DN_X
+  }
+  return TierShape{0, 0, 0, 0};
+}
+
+// Launch one forward kernel instance (IN, EPI) of the given tier.  Returns the HIP error
+// of the launch.  `kernel_out`, when non-null, receives the kernel's address instead of
+// launching (used for occupancy queries).
+template <int IN, int EPI>
+hipError_t fwd_launch(const FwdParams& p, int tier, int grid, size_t lds, hipStream_t s,
+                      const void** kernel_out);
+
+hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStream_t s,
+                               const void** kernel_out);
+hipError_t bwd_reduce_launch(float* dw, const double* part, int hidden, int chunks,
+                             hipStream_t s);
+
+}  // namespace dn

@@ -1,0 +1,387 @@
+"""Thin Python binding of ``libdnorm.so`` (include/dnorm.h): argument marshalling only.
+
+Each ``dn_*`` function here has the name of the C entry point it calls.  It takes torch
+tensors (PyTorch serves only for device memory and streams), collapses N-D activations to
+rows, allocates omitted outputs, passes raw device pointers, strides and the current HIP
+stream, and raises ``DnormError`` with the library's message on any failed check.  Every
+computation happens in the HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdnorm.so")
+
+DN_WEIGHT_BF16 = 0
+DN_WEIGHT_F32 = 1
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+# C signatures (argument types in order), mirroring include/dnorm.h.
+SIGNATURES = {
+    "dn_last_error": ([], ctypes.c_char_p),
+    "dn_max_hidden": ([], _I32),
+    "dn_version": ([], ctypes.c_char_p),
+    "dn_force_threads_per_row": ([_I32], _I32),
+    "dn_rmsnorm": ([_P, _I64, _P, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
+    "dn_rmsnorm_quant": ([_P, _I64, _P, _I64, _P, _I32, _F32, _P, _I64, _I64, _F32, _P], _I32),
+    "dn_fused_add_rmsnorm": ([_P, _I64, _P, _I64, _P, _I32, _F32, _P, _I64, _I64, _F32, _P], _I32),
+    "dn_fused_add_rmsnorm_quant": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _I64, _I64, _F32, _P], _I32),
+    "dn_fused_add_rmsnorm_fp8_block_quant": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P],
+        _I32),
+    "dn_ada_rms_norm": ([_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _F32, _P],
+                        _I32),
+    "dn_gate_residual_ada_norm_fp8": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I64, _P, _I64, _I64,
+         _F32, _P], _I32),
+    "dn_train_forward": (
+        [_P, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
+    "dn_train_backward_workspace_bytes": ([_I64], _SZ),
+    "dn_train_backward": (
+        [_P, _I64, _P, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
+        _I32),
+    "dn_train_backward_partials": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
+        _I32),
+    "dn_train_backward_reduce": ([_P, _P, _SZ, _I64, _I64, _P], _I32),
+}
+
+
+class DnormError(RuntimeError):
+    """A dnorm call was rejected (bad shape, dtype, alignment, workspace) or failed."""
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdnorm.so and declare its C signatures.  Raises ImportError if it is not
+    built (``python -m dit_normalization_amd.build``)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m dit_normalization_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = load_library()
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = lib.dn_last_error().decode(errors="replace")
+        raise DnormError(f"{name} failed ({status}): {msg}")
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str, dtype=torch.bfloat16):
+    """(tensor, rows, row_stride) of an activation [..., H] read row by row.
+
+    Leading dimensions collapse into rows when the feature dimension is contiguous and the
+    leading dimensions are contiguous with one another (stride(i) == stride(i+1)*size(i+1));
+    any other layout is copied once, the rule of cake_rmsnorm_det_train_forward (x).
+    """
+    if not t.is_cuda:
+        raise DnormError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise DnormError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() == 1:
+        t = t.unsqueeze(0)
+    ok = t.stride(-1) == 1 and all(
+        t.stride(i) == t.stride(i + 1) * t.size(i + 1) for i in range(t.dim() - 2))
+    if not ok or (t.dim() >= 2 and t.size(-2) > 1 and t.stride(-2) % 8 != 0) or \
+            t.data_ptr() % 16 != 0:
+        t = t.contiguous()
+    rows = 1
+    for s in t.shape[:-1]:
+        rows *= s
+    stride = t.stride(-2) if t.dim() >= 2 and t.size(-2) > 1 else t.size(-1)
+    return t, rows, stride
+
+
+def _weight(w: torch.Tensor):
+    if w.dtype == torch.bfloat16:
+        code = DN_WEIGHT_BF16
+    elif w.dtype == torch.float32:
+        code = DN_WEIGHT_F32
+    else:
+        raise DnormError(f"weight must be bfloat16 or float32, got {w.dtype}")
+    if not w.is_contiguous() or w.data_ptr() % 16 != 0:
+        w = w.contiguous().clone()
+    return w, code
+
+
+def _scale_tensor(scale, device):
+    """Static FP8 scale as a device FP32 tensor of shape (1,) (a Python float is moved once)."""
+    if isinstance(scale, torch.Tensor):
+        s = scale.to(device=device, dtype=torch.float32).reshape(1).contiguous()
+    else:
+        s = torch.tensor([float(scale)], dtype=torch.float32, device=device)
+    return s
+
+
+def _out_like(t, shape, dtype):
+    return torch.empty(shape, dtype=dtype, device=t.device)
+
+
+def _writeback(dst, src):
+    if dst is not None and dst is not src and dst.data_ptr() != src.data_ptr():
+        dst.copy_(src.view(dst.shape))
+
+
+# ---------------------------------------------------------------------------------------------
+
+def dn_rmsnorm(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=None, rstd=None,
+               return_rstd: bool = False):
+    """y = BF16(x * r * (w + w_bias)) per row; returns y (and rstd)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    w, wcode = _weight(w)
+    y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
+    yr, _, sy = _rows(y, "out")
+    if return_rstd and rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib.dn_rmsnorm(yr.data_ptr(), sy, _ptr(rstd), xr.data_ptr(), sx, w.data_ptr(), wcode,
+                          w_bias, rows, H, eps, _stream(x)), "dn_rmsnorm")
+    _writeback(y, yr)
+    return (y, rstd) if return_rstd else y
+
+
+def dn_rmsnorm_quant(x, w, scale, eps: float = 1e-6, *, w_bias: float = 0.0, out=None):
+    """out = e4m3fn(rmsnorm(x) / scale)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    w, wcode = _weight(w)
+    q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    s = _scale_tensor(scale, x.device)
+    _check(lib.dn_rmsnorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, w.data_ptr(), wcode, w_bias,
+                                s.data_ptr(), rows, H, eps, _stream(x)), "dn_rmsnorm_quant")
+    _writeback(q, qr)
+    return q
+
+
+def dn_fused_add_rmsnorm(x, residual, w, eps: float = 1e-6, *, w_bias: float = 0.0, rstd=None):
+    """In place: residual <- x + residual; x <- rmsnorm(residual).  Both must be views the
+    kernel can address directly (leading dimensions collapsible)."""
+    xr, rows, sx = _rows(x, "x")
+    rr, rows_r, sr = _rows(residual, "residual")
+    if xr.data_ptr() != x.data_ptr() or rr.data_ptr() != residual.data_ptr():
+        raise DnormError("fused_add_rmsnorm works in place: x and residual need row-addressable layouts")
+    if rows_r != rows or rr.size(-1) != xr.size(-1):
+        raise DnormError("x and residual must have the same shape")
+    w, wcode = _weight(w)
+    _check(lib.dn_fused_add_rmsnorm(xr.data_ptr(), sx, rr.data_ptr(), sr, w.data_ptr(), wcode,
+                                    w_bias, _ptr(rstd), rows, xr.size(-1), eps, _stream(x)),
+           "dn_fused_add_rmsnorm")
+
+
+def dn_fused_add_rmsnorm_quant(x, residual, w, scale, eps: float = 1e-6, *, w_bias: float = 0.0,
+                               out=None):
+    """residual <- x + residual (in place); returns out = e4m3fn(rmsnorm(residual) / scale)."""
+    xr, rows, sx = _rows(x, "x")
+    rr, _, sr = _rows(residual, "residual")
+    if rr.data_ptr() != residual.data_ptr():
+        raise DnormError("residual is updated in place: it needs a row-addressable layout")
+    w, wcode = _weight(w)
+    q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    s = _scale_tensor(scale, x.device)
+    _check(lib.dn_fused_add_rmsnorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, rr.data_ptr(), sr,
+                                          w.data_ptr(), wcode, w_bias, s.data_ptr(), rows,
+                                          xr.size(-1), eps, _stream(x)),
+           "dn_fused_add_rmsnorm_quant")
+    _writeback(q, qr)
+    return q
+
+
+def dn_fused_add_rmsnorm_fp8_block_quant(x, residual, w, eps: float = 1e-6, *, w_bias: float = 0.0,
+                                         out=None, block_scale=None, normed_out=None):
+    """residual <- x + residual (in place); returns (out, block_scale) with block_scale of
+    shape (hidden/128, round_up(rows, 4)) -- column-major per row, the logical
+    [rows, hidden/128] scales being block_scale.T[:rows]."""
+    xr, rows, sx = _rows(x, "x")
+    rr, _, sr = _rows(residual, "residual")
+    if rr.data_ptr() != residual.data_ptr():
+        raise DnormError("residual is updated in place: it needs a row-addressable layout")
+    H = xr.size(-1)
+    w, wcode = _weight(w)
+    q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    ld = (rows + 3) // 4 * 4
+    if block_scale is None:
+        block_scale = torch.empty((H // 128, ld), dtype=torch.float32, device=x.device)
+    else:
+        ld = block_scale.stride(0)
+    nr, sn = None, 0
+    if normed_out is not None:
+        nr, _, sn = _rows(normed_out, "normed_out")
+    _check(lib.dn_fused_add_rmsnorm_fp8_block_quant(
+        qr.data_ptr(), sq, block_scale.data_ptr(), ld, _ptr(nr), sn, xr.data_ptr(), sx,
+        rr.data_ptr(), sr, w.data_ptr(), wcode, w_bias, rows, H, eps, _stream(x)),
+        "dn_fused_add_rmsnorm_fp8_block_quant")
+    _writeback(q, qr)
+    if normed_out is not None:
+        _writeback(normed_out, nr)
+    return q, block_scale
+
+
+def dn_ada_rms_norm(x, w, style, eps: float = 1e-6, *, out=None, gate_out=None):
+    """out = BF16(rmsnorm(x, w) * (1 + style_scale) + style_shift); returns (out, gate_out)."""
+    xr, rows, sx = _rows(x, "x")
+    dim = xr.size(-1)
+    w, _ = _weight(w)
+    st, srows, sst = _rows(style, "style")
+    o = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
+    orr, _, so = _rows(o, "out")
+    g = gate_out if gate_out is not None else _out_like(x, x.shape, torch.bfloat16)
+    gr, _, sg = _rows(g, "gate_out")
+    _check(lib.dn_ada_rms_norm(orr.data_ptr(), so, gr.data_ptr(), sg, xr.data_ptr(), sx,
+                               w.data_ptr(), st.data_ptr(), sst, srows, rows, dim, eps,
+                               _stream(x)), "dn_ada_rms_norm")
+    _writeback(o, orr)
+    _writeback(g, gr)
+    return o, g
+
+
+def dn_gate_residual_ada_norm_fp8(residual, x, gate, w, style, scale, eps: float = 1e-6, *,
+                                  out=None, gate_out=None):
+    """residual <- residual + x*gate (in place); returns (residual, out_fp8, gate_out)."""
+    rr, rows, sr = _rows(residual, "residual")
+    if rr.data_ptr() != residual.data_ptr():
+        raise DnormError("residual is updated in place: it needs a row-addressable layout")
+    dim = rr.size(-1)
+    xr, _, sx = _rows(x, "x")
+    gtr, _, sgt = _rows(gate, "gate")
+    w, _ = _weight(w)
+    st, srows, sst = _rows(style, "style")
+    q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    g = gate_out if gate_out is not None else _out_like(x, x.shape, torch.bfloat16)
+    gr, _, sg = _rows(g, "gate_out")
+    s = _scale_tensor(scale, x.device)
+    _check(lib.dn_gate_residual_ada_norm_fp8(
+        rr.data_ptr(), sr, qr.data_ptr(), sq, gr.data_ptr(), sg, xr.data_ptr(), sx,
+        gtr.data_ptr(), sgt, w.data_ptr(), st.data_ptr(), sst, srows, s.data_ptr(), rows, dim,
+        eps, _stream(x)), "dn_gate_residual_ada_norm_fp8")
+    _writeback(q, qr)
+    _writeback(g, gr)
+    return residual, q, g
+
+
+def dn_train_forward(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, residual=None, out=None,
+                     rstd=None, residual_out=None):
+    """(y, rstd) or, with a residual, (y, rstd, h_new)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    w, wcode = _weight(w)
+    y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
+    yr, _, sy = _rows(y, "out")
+    if rstd is None:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    hr, sh, rsr, srs = None, 0, None, 0
+    if residual is not None:
+        rsr, _, srs = _rows(residual, "residual")
+        if residual_out is None:
+            residual_out = _out_like(x, x.shape, torch.bfloat16)
+        hr, _, sh = _rows(residual_out, "residual_out")
+    _check(lib.dn_train_forward(yr.data_ptr(), sy, rstd.data_ptr(), _ptr(hr), sh, xr.data_ptr(), sx,
+                                _ptr(rsr), srs, w.data_ptr(), wcode, w_bias, rows, H, eps,
+                                _stream(x)), "dn_train_forward")
+    _writeback(y, yr)
+    if residual is None:
+        return y, rstd
+    _writeback(residual_out, hr)
+    return y, rstd, residual_out
+
+
+def dn_train_backward_workspace_bytes(hidden: int) -> int:
+    return int(lib.dn_train_backward_workspace_bytes(int(hidden)))
+
+
+def train_backward_workspace(hidden: int, device) -> torch.Tensor:
+    """A zeroed uint8 workspace of dn_train_backward_workspace_bytes(hidden) bytes (torch's
+    allocator returns 256-byte aligned blocks)."""
+    n = dn_train_backward_workspace_bytes(hidden)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _bwd_common(g, x, w, rstd, g_residual, dx):
+    gr, rows, sg = _rows(g, "g")
+    xr, _, sx = _rows(x, "x")
+    w, wcode = _weight(w)
+    if rstd.dtype != torch.float32 or not rstd.is_contiguous():
+        raise DnormError("rstd must be a contiguous float32 tensor")
+    d = dx if dx is not None else _out_like(x, x.shape, torch.bfloat16)
+    dr, _, sd = _rows(d, "dx")
+    grr, sgr = None, 0
+    if g_residual is not None:
+        grr, _, sgr = _rows(g_residual, "g_residual")
+    return gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr
+
+
+def dn_train_backward(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, workspace=None,
+                      dx=None, dw=None):
+    """(dx, dw): dx BF16 like x, dw FP32 [hidden], deterministic."""
+    gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr = _bwd_common(g, x, w, rstd, g_residual, dx)
+    H = xr.size(-1)
+    if workspace is None:
+        workspace = train_backward_workspace(H, x.device)
+    if dw is None:
+        dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    _check(lib.dn_train_backward(dr.data_ptr(), sd, dw.data_ptr(), gr.data_ptr(), sg, xr.data_ptr(),
+                                 sx, w.data_ptr(), wcode, w_bias, rstd.data_ptr(), _ptr(grr), sgr,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 rows, H, _stream(x)), "dn_train_backward")
+    _writeback(d, dr)
+    return d, dw
+
+
+def dn_train_backward_partials(g, x, w, rstd, workspace, *, w_bias: float = 0.0, g_residual=None,
+                               dx=None):
+    """Stage 1 of the backward: dx, and the FP64 per-chunk column sums in `workspace`."""
+    gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr = _bwd_common(g, x, w, rstd, g_residual, dx)
+    H = xr.size(-1)
+    _check(lib.dn_train_backward_partials(dr.data_ptr(), sd, gr.data_ptr(), sg, xr.data_ptr(), sx,
+                                          w.data_ptr(), wcode, w_bias, rstd.data_ptr(), _ptr(grr),
+                                          sgr, workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), rows, H,
+                                          _stream(x)), "dn_train_backward_partials")
+    _writeback(d, dr)
+    return d
+
+
+def dn_train_backward_reduce(workspace, rows: int, hidden: int, *, dw=None):
+    """Stage 2 of the backward: dw from the chunk sums of a partials call with `rows`."""
+    if dw is None:
+        dw = torch.empty(hidden, dtype=torch.float32, device=workspace.device)
+    _check(lib.dn_train_backward_reduce(dw.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), rows, hidden,
+                                        _stream(workspace)), "dn_train_backward_reduce")
+    return dw
+
+
+def dn_force_threads_per_row(threads: int):
+    """Test / tuning hook: force the forward row mapping (0 = automatic)."""
+    _check(lib.dn_force_threads_per_row(int(threads)), "dn_force_threads_per_row")
+
+
+def dn_max_hidden() -> int:
+    return int(lib.dn_max_hidden())

@@ -1,0 +1,250 @@
+/*
+ * dnorm.h -- C ABI of the row-wise RMSNorm family on AMD Instinct MI355X (gfx950).
+ *
+ * Every operation normalises rows of a [rows, hidden] matrix independently:
+ *
+ *     r_t  = 1 / sqrt(mean_j h_tj^2 + eps)        (FP32 statistics, eps an FP32 number)
+ *     y_tj = BF16((h_tj * r_t) * w_eff_j),  w_eff_j = FP32(w_j + w_bias)
+ *
+ * Pages cited (by title and section):
+ *   [norm docs]   "flashinfer.norm" API reference: the API table and the section
+ *                 "Training RMSNorm (Cake)".
+ *   [norm guide]  "FlashInfer 归一化算子库全解 ..." walk-through article, by section number.
+ *   [cake docs]   "flashinfer.cake_rmsnorm_det_train.cake_rmsnorm_det_train_forward":
+ *                 Parameters, Returns, Notes.
+ *   [flashrt]     "flashrt-adaptive-norms" README: Exported APIs, Tensor Conventions.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers on the current HIP device.  Matrices are
+ *     row-major with an explicit row stride counted in ELEMENTS (>= hidden); the feature
+ *     dimension is contiguous.  A 3-D [T, heads, hd] tensor whose leading dimensions are
+ *     contiguous with one another is passed as rows = T*heads, hidden = hd ([norm guide]
+ *     §2.1: 3-D input is normalised per (batch, head) row; [cake docs] Parameters: x).
+ *   - BF16 and FP32 tensors need 16-byte aligned bases and row strides that are multiples
+ *     of 8 elements; FP8 outputs need 8-byte aligned bases and strides that are multiples
+ *     of 8; per-row FP32 vectors (rstd, block scales, dw) need 4-byte alignment.  Row
+ *     strides are at most 2^24 elements.
+ *   - hidden must be a positive multiple of 8 and at most dn_max_hidden().
+ *   - rows == 0 is valid: the call returns DN_OK and launches nothing ([norm guide] §6.1).
+ *   - Outputs are caller-owned and preallocated (destination passing, [norm guide] §2.1).
+ *     An output may alias an input exactly (same pointer, same stride) -- that is how the
+ *     in-place calls work -- but must not overlap it in any other way.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).  The
+ *     library never allocates device memory and never synchronises; FP8 scales are read
+ *     from device memory, so no host round trip happens.
+ *   - Errors: every argument check runs on the host before anything is launched.  A failed
+ *     check returns a negative dn_status, records a message for dn_last_error(), and
+ *     launches nothing.  DN_ERR_HIP reports a failed HIP call or launch.
+ *   - Rounding: round-to-nearest-even for BF16, FP32 and FP8.  FP8 is OCP e4m3fn; values
+ *     beyond +-448 saturate to +-448.  NaN or infinite inputs give unspecified outputs.
+ */
+#ifndef DNORM_H
+#define DNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* dn_stream_t; /* hipStream_t */
+
+typedef enum dn_status {
+  DN_OK = 0,
+  DN_ERR_NULL = -1,        /* a required pointer is NULL */
+  DN_ERR_SHAPE = -2,       /* negative rows, hidden out of range, stride < hidden, ... */
+  DN_ERR_ALIGN = -3,       /* a pointer or stride breaks the alignment rules above */
+  DN_ERR_DTYPE = -4,       /* unknown weight dtype code */
+  DN_ERR_WORKSPACE = -5,   /* backward workspace too small or not 256-byte aligned */
+  DN_ERR_UNSUPPORTED = -6, /* hidden not a multiple of 8 (or of 128 for 1x128 blocks) */
+  DN_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+} dn_status;
+
+/* Weight dtypes: BF16 [hidden], or FP32 [hidden] (a zero-centred weight whose effective
+ * value 1 + w is formed in FP32 with w_bias = 1; [cake docs] Parameters: w). */
+enum { DN_WEIGHT_BF16 = 0, DN_WEIGHT_F32 = 1 };
+
+/* Message of the last failed call made on this host thread ("" if none). */
+const char* dn_last_error(void);
+
+/* Largest supported hidden size (32768). */
+int dn_max_hidden(void);
+
+/* Library version string. */
+const char* dn_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * rmsnorm / gemma_rmsnorm   ([norm docs] API table; [norm guide] §2.1, §2.2)
+ *   y = BF16(x * r * FP32(w + w_bias)); rstd[t] = FP32(r_t) when rstd != NULL.
+ *   w_bias = 0 is rmsnorm, w_bias = 1 the Gemma form (w + 1).
+ *   x: BF16 [rows, hidden] (stride x_stride); w: [hidden] of dtype w_dtype;
+ *   y: BF16 [rows, hidden] (stride y_stride; may be x itself); rstd: FP32 [rows] or NULL.
+ */
+dn_status dn_rmsnorm(void* y, int64_t y_stride, float* rstd,
+                     const void* x, int64_t x_stride,
+                     const void* w, int w_dtype, float w_bias,
+                     int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * rmsnorm_quant   ([norm docs] API table: rmsnorm_quant(out, input, weight, scale))
+ *   out = e4m3fn((x * r * w_eff) / scale), from the unrounded FP32 normalised value.
+ *   scale: device FP32 [1] ([norm guide] §3.2).  out: FP8 [rows, hidden] (stride out_stride).
+ */
+dn_status dn_rmsnorm_quant(uint8_t* out, int64_t out_stride,
+                           const void* x, int64_t x_stride,
+                           const void* w, int w_dtype, float w_bias, const float* scale,
+                           int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * fused_add_rmsnorm / gemma_fused_add_rmsnorm   ([norm docs] API table; [norm guide] §3.1)
+ *   In place: residual <- h_new = BF16(x + residual); x <- BF16(h_new * r * w_eff).
+ *   The norm is taken over the BF16 h_new ([cake docs] Parameters: x).
+ *   rstd: FP32 [rows] or NULL.
+ */
+dn_status dn_fused_add_rmsnorm(void* x, int64_t x_stride,
+                               void* residual, int64_t residual_stride,
+                               const void* w, int w_dtype, float w_bias, float* rstd,
+                               int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * fused_add_rmsnorm_quant   ([norm docs] API table; [norm guide] §3.2)
+ *   residual <- h_new = BF16(x + residual); out = e4m3fn((h_new * r * w_eff) / scale).
+ *   x is read only.  scale: device FP32 [1].
+ */
+dn_status dn_fused_add_rmsnorm_quant(uint8_t* out, int64_t out_stride,
+                                     const void* x, int64_t x_stride,
+                                     void* residual, int64_t residual_stride,
+                                     const void* w, int w_dtype, float w_bias,
+                                     const float* scale,
+                                     int64_t rows, int64_t hidden, float eps,
+                                     dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * fused_add_rmsnorm_fp8_block_quant   ([norm docs] API table; [norm guide] §3.3)
+ *   One pass: residual <- h_new = BF16(x + residual); n = BF16(h_new * r * w_eff);
+ *   for each 1x128 block k of a row: s = FP32(max|n| / 448), out = e4m3fn(n / s)
+ *   (s = 0 and out = 0 for an all-zero block).
+ *   block_scale: FP32, column-major "MN-major" [hidden/128][scale_ld]: the scale of row t,
+ *   block k is block_scale[k * scale_ld + t]; scale_ld >= rows (the pages use
+ *   round_up(rows, 4)); entries t in [rows, scale_ld) are written as 0.
+ *   normed_out: BF16 [rows, hidden] receiving n, or NULL.  hidden % 128 == 0.
+ */
+dn_status dn_fused_add_rmsnorm_fp8_block_quant(uint8_t* out, int64_t out_stride,
+                                               float* block_scale, int64_t scale_ld,
+                                               void* normed_out, int64_t normed_stride,
+                                               const void* x, int64_t x_stride,
+                                               void* residual, int64_t residual_stride,
+                                               const void* w, int w_dtype, float w_bias,
+                                               int64_t rows, int64_t hidden, float eps,
+                                               dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * ada_rms_norm   ([flashrt] Exported APIs: ada_rms_norm_style_bf16; Tensor Conventions)
+ *   n = x * r * w (BF16 weight, no bias); out = BF16(n * (1 + style_scale) + style_shift);
+ *   gate_out = the style's third chunk (a bit copy).
+ *   style: BF16 [style_rows, 3*dim] with chunks [scale | shift | gate]; style_rows is
+ *   rows (one style row per token) or 1 (one row broadcast to every token).
+ *   gate_out: BF16 [rows, dim] or NULL.  Every rows x dim matrix has its own stride.
+ */
+dn_status dn_ada_rms_norm(void* out, int64_t out_stride,
+                          void* gate_out, int64_t gate_out_stride,
+                          const void* x, int64_t x_stride,
+                          const void* w,
+                          const void* style, int64_t style_stride, int64_t style_rows,
+                          int64_t rows, int64_t dim, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * gate_residual_ada_norm_fp8   ([flashrt] Exported APIs:
+ *                                gate_residual_ada_norm_fp8_static_bf16)
+ *   residual <- h = BF16(FP32-FMA(x, gate, residual));
+ *   out = e4m3fn((h * r * w * (1 + style_scale) + style_shift) / scale);
+ *   gate_out = the style's third chunk.  scale: device FP32 [1].
+ */
+dn_status dn_gate_residual_ada_norm_fp8(void* residual, int64_t residual_stride,
+                                        uint8_t* out, int64_t out_stride,
+                                        void* gate_out, int64_t gate_out_stride,
+                                        const void* x, int64_t x_stride,
+                                        const void* gate, int64_t gate_stride,
+                                        const void* w,
+                                        const void* style, int64_t style_stride,
+                                        int64_t style_rows, const float* scale,
+                                        int64_t rows, int64_t dim, float eps,
+                                        dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * train_forward   ([norm docs] "Training RMSNorm (Cake)": cake_rmsnorm_train_forward;
+ *                  [cake docs] Parameters, Returns; [norm guide] §6.1, §6.2)
+ *   Without residual: y = BF16(x * r * w_eff), rstd = FP32(r).
+ *   With residual (non-NULL): h_new = BF16(x + residual) is written to h_new and is the
+ *   normalised value.  rstd (FP32 [rows]) is required: it is what the backward needs.
+ *   w: BF16, or FP32 with w_bias = 1 for the zero-centred form.
+ */
+dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd,
+                           void* h_new, int64_t h_new_stride,
+                           const void* x, int64_t x_stride,
+                           const void* residual, int64_t residual_stride,
+                           const void* w, int w_dtype, float w_bias,
+                           int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Training backward   ([norm docs] cake_rmsnorm_train_backward, ..._workspace_bytes;
+ *                      [norm guide] §6.1-6.3)
+ *   dx = BF16(r*g*w_eff - x*r^3*mean_j(g*w_eff*x) [+ g_residual])
+ *   dw = FP32(sum_t g*x*r)     -- the gradient with respect to w_eff (= w + w_bias)
+ *   x is the tensor the forward normalised (h_new on the residual route) and rstd the FP32
+ *   tensor the forward returned.  g_residual (nullable) is the gradient reaching h_new
+ *   directly; dx is then the gradient of both residual inputs.
+ *
+ *   dw is bitwise deterministic: rows are cut into min(rows, 256) fixed chunks that depend
+ *   on rows only (not on the device); each chunk's column sums are carried in FP64 from
+ *   exact products into one workspace row, and a second kernel adds the chunk rows in a
+ *   fixed order before one rounding to FP32.
+ *
+ *   workspace: caller-owned device memory of at least
+ *   dn_train_backward_workspace_bytes(hidden) bytes, 256-byte aligned.  It needs no
+ *   zeroing; every call rewrites what it reads, so one buffer serves every call, token
+ *   count and stream-ordered replay.  Calls sharing a workspace must be stream-ordered.
+ */
+size_t dn_train_backward_workspace_bytes(int64_t hidden);
+
+dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw,
+                            const void* g, int64_t g_stride,
+                            const void* x, int64_t x_stride,
+                            const void* w, int w_dtype, float w_bias, const float* rstd,
+                            const void* g_residual, int64_t g_residual_stride,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t rows, int64_t hidden, dn_stream_t stream);
+
+/* The two stages of dn_train_backward, exposed so a caller can place the dw reduction
+ * elsewhere (e.g. after exchanging chunk rows between data-parallel ranks) or time the
+ * stages apart.  dn_train_backward == partials followed by reduce on the same stream.
+ *   partials: dx, and the FP64 per-chunk column sums in the workspace.
+ *   reduce:   dw[j] = FP32(sum over the chunk rows of column j, in chunk order); `rows`
+ *             must equal the rows given to the partials call (it fixes the chunk count). */
+dn_status dn_train_backward_partials(void* dx, int64_t dx_stride,
+                                     const void* g, int64_t g_stride,
+                                     const void* x, int64_t x_stride,
+                                     const void* w, int w_dtype, float w_bias,
+                                     const float* rstd,
+                                     const void* g_residual, int64_t g_residual_stride,
+                                     void* workspace, size_t workspace_bytes,
+                                     int64_t rows, int64_t hidden, dn_stream_t stream);
+
+dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes,
+                                   int64_t rows, int64_t hidden, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Test and tuning hook: force the threads that share one row (8, 16, 32, 64, 128, 256,
+ * 512 or 1024) in every forward launch of this process; 0 restores the automatic choice
+ * by hidden size.  Returns DN_ERR_SHAPE for other values or when the forced count cannot
+ * cover hidden in registers (then the automatic choice is used).  Results stay within
+ * the documented tolerances either way; bits may change with the row mapping.
+ */
+dn_status dn_force_threads_per_row(int threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DNORM_H */

@@ -1,0 +1,167 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every entry point that
+include/dnorm.h declares, and rejects bad arguments before touching any device state.
+Only argument checks and rows == 0 calls are made here (they return before any HIP call);
+nothing is computed."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_WS, E_UNSUP = 0, -1, -2, -3, -4, -5, -6
+
+A = 0x100000        # a 256-byte aligned stand-in address (never dereferenced here)
+B = 0x200000
+C = 0x300000
+D = 0x400000
+E = 0x500000
+
+
+@pytest.fixture(scope="module")
+def dn():
+    from dit_normalization_amd import dnorm
+    return dnorm
+
+
+@pytest.fixture(scope="module")
+def lib(dn):
+    return dn.lib
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "dnorm.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int|size_t|dn_status)\s+(dn_\w+)\(", text,
+                                 re.M)))
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_entry_points()
+    for n in ["dn_rmsnorm", "dn_rmsnorm_quant", "dn_fused_add_rmsnorm", "dn_fused_add_rmsnorm_quant",
+              "dn_fused_add_rmsnorm_fp8_block_quant", "dn_ada_rms_norm",
+              "dn_gate_residual_ada_norm_fp8", "dn_train_forward", "dn_train_backward",
+              "dn_train_backward_workspace_bytes", "dn_train_backward_partials",
+              "dn_train_backward_reduce", "dn_last_error"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(dn):
+    raw = ctypes.CDLL(dn.LIB_PATH)
+    for name in declared_entry_points():
+        assert hasattr(raw, name), name
+        assert name in dn.SIGNATURES, name
+
+
+def test_binding_names_match_the_c_entry_points(dn):
+    for name in declared_entry_points():
+        if name in ("dn_last_error", "dn_version"):
+            continue
+        assert callable(getattr(dn, name)), name
+
+
+def test_info_calls(lib):
+    assert lib.dn_max_hidden() == 32768
+    assert b"gfx950" in lib.dn_version()
+
+
+def test_workspace_bytes(lib):
+    assert lib.dn_train_backward_workspace_bytes(8192) == 256 * 8192 * 8
+    assert lib.dn_train_backward_workspace_bytes(0) == 0
+    assert lib.dn_train_backward_workspace_bytes(10 ** 6) == 0
+
+
+def rms(lib, y=A, ys=4096, rstd=0, x=B, xs=4096, w=C, wd=0, rows=4, h=4096):
+    return lib.dn_rmsnorm(y, ys, rstd, x, xs, w, wd, 0.0, rows, h, 1e-6, None)
+
+
+def test_rmsnorm_argument_checks(lib):
+    assert rms(lib, rows=0) == OK                          # empty: no launch
+    assert rms(lib, rows=-1) == E_SHAPE
+    assert b"rows" in lib.dn_last_error()
+    assert rms(lib, h=0) == E_SHAPE
+    assert rms(lib, h=40000, xs=40000, ys=40000) == E_SHAPE
+    assert rms(lib, h=12, xs=16, ys=16) == E_UNSUP
+    assert rms(lib, x=0) == E_NULL
+    assert b"x" in lib.dn_last_error()
+    assert rms(lib, y=0) == E_NULL
+    assert rms(lib, w=0) == E_NULL
+    assert rms(lib, x=B + 8) == E_ALIGN
+    assert rms(lib, xs=4000) == E_SHAPE                    # stride < hidden
+    assert rms(lib, xs=4100) == E_ALIGN                    # stride not a multiple of 8
+    assert rms(lib, xs=(1 << 24) + 8) == E_SHAPE           # stride beyond 2^24 elements
+    assert rms(lib, wd=7) == E_DTYPE
+    assert rms(lib, w=C + 4) == E_ALIGN
+    assert rms(lib, rstd=D + 2) == E_ALIGN
+    assert rms(lib, rows=0, rstd=D) == OK
+
+
+def test_quant_and_fused_add_checks(lib):
+    q = lib.dn_rmsnorm_quant
+    assert q(A, 4096, B, 4096, C, 0, 0.0, D, 0, 4096, 1e-6, None) == OK
+    assert q(A, 4096, B, 4096, C, 0, 0.0, 0, 4, 4096, 1e-6, None) == E_NULL       # scale
+    assert q(A + 4, 4096, B, 4096, C, 0, 0.0, D, 4, 4096, 1e-6, None) == E_ALIGN  # fp8 out
+    fa = lib.dn_fused_add_rmsnorm
+    assert fa(A, 4096, B, 4096, C, 0, 1.0, 0, 0, 4096, 1e-6, None) == OK
+    assert fa(A, 4096, 0, 4096, C, 0, 1.0, 0, 4, 4096, 1e-6, None) == E_NULL
+    faq = lib.dn_fused_add_rmsnorm_quant
+    assert faq(A, 4096, B, 4096, C, 4096, D, 0, 0.0, E, 0, 4096, 1e-6, None) == OK
+    assert faq(A, 4096, B, 4096, C, 4096, D, 2, 0.0, E, 4, 4096, 1e-6, None) == E_DTYPE
+
+
+def test_block_quant_checks(lib):
+    bq = lib.dn_fused_add_rmsnorm_fp8_block_quant
+    args = dict(out=A, os=7168, bs=B, ld=16384, no=0, ns=0, x=C, xs=7168, r=D, rs=7168, w=E,
+                wd=0, rows=16384, h=7168)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return bq(a["out"], a["os"], a["bs"], a["ld"], a["no"], a["ns"], a["x"], a["xs"], a["r"],
+                  a["rs"], a["w"], a["wd"], 0.0, a["rows"], a["h"], 1e-6, None)
+
+    assert call(rows=0) == OK
+    assert call(h=7160, os=7160, xs=7160, rs=7160) == E_UNSUP   # not a multiple of 128
+    assert call(ld=100) == E_SHAPE                              # scale_ld < rows
+    assert call(bs=0) == E_NULL
+    assert call(no=A + 16, ns=7000, rows=0) == E_SHAPE          # normed_out stride < hidden
+
+
+def test_ada_checks(lib):
+    ada = lib.dn_ada_rms_norm
+    assert ada(A, 3072, 0, 0, B, 3072, C, D, 9216, 1, 0, 3072, 1e-6, None) == OK
+    assert ada(A, 3072, 0, 0, B, 3072, C, D, 9216, 3, 10, 3072, 1e-6, None) == E_SHAPE
+    assert b"style_rows" in lib.dn_last_error()
+    assert ada(A, 3072, 0, 0, B, 3072, C, D, 9000, 1, 10, 3072, 1e-6, None) == E_SHAPE
+    g = lib.dn_gate_residual_ada_norm_fp8
+    assert g(A, 3072, B, 3072, 0, 0, C, 3072, D, 3072, E, A, 9216, 1, B, 0, 3072, 1e-6,
+             None) == OK
+    assert g(A, 3072, B, 3072, 0, 0, C, 3072, D, 3072, E, A, 9216, 1, 0, 5, 3072, 1e-6,
+             None) == E_NULL                                    # scale
+    assert g(A, 3072, B, 3072, 0, 0, C, 3072, 0, 3072, E, A, 9216, 1, B, 5, 3072, 1e-6,
+             None) == E_NULL                                    # gate
+
+
+def test_train_checks(lib):
+    f = lib.dn_train_forward
+    assert f(A, 8192, B, C, 8192, D, 8192, E, 8192, A, 1, 1.0, 0, 8192, 1e-6, None) == OK
+    assert f(A, 8192, 0, C, 8192, D, 8192, E, 8192, A, 1, 1.0, 5, 8192, 1e-6, None) == E_NULL
+    assert f(A, 8192, B, 0, 8192, D, 8192, E, 8192, A, 1, 1.0, 5, 8192, 1e-6, None) == E_NULL
+    ws = 256 * 8192 * 8
+    b = lib.dn_train_backward
+    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 0, 8192, None) == OK
+    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws - 8, 5, 8192,
+             None) == E_WS
+    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B + 64, ws, 5, 8192,
+             None) == E_WS
+    assert b(A, 8192, 0, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192, None) == E_NULL
+    r = lib.dn_train_backward_reduce
+    assert r(A, B, ws, 0, 8192, None) == OK
+    assert r(A, B, ws // 2, 5, 8192, None) == E_WS
+
+
+def test_force_threads_per_row(lib):
+    assert lib.dn_force_threads_per_row(3) == E_SHAPE
+    assert lib.dn_force_threads_per_row(128) == OK
+    assert lib.dn_force_threads_per_row(0) == OK
