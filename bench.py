@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the RMSNorm family's hot path on one MI355X, as achieved HBM GB/s.
+
+One step is one pass of the hot path over one batch of synthetic input:
+  1. fused_add_rmsnorm forward, in place, x/residual BF16 [8192, 4096]      (plain BF16 y)
+  2. training RMSNorm forward with residual, BF16 [16384, 8192], FP32 w = 1 + w0
+  3. fused_add_rmsnorm + static FP8 forward, BF16 [8192, 4096] -> e4m3fn    (scale 0.04)
+  4. training backward on (2)'s h_new and rstd: dx BF16 and deterministic FP32 dw
+     (stage 1: dx + per-chunk FP64 column sums; stage 2: fixed-order dw reduction)
+The order interleaves the two shapes so that each kernel's inputs have been pushed out of
+the 256 MB Infinity Cache by the previous kernel's traffic.
+
+`value` = algorithmic bytes of a step / wall time of a step (K steps between device
+synchronisations).  Algorithmic bytes count each tensor the definition reads or writes
+once; the backward's FP64 workspace traffic is not counted.  Per-kernel durations come from
+HIP events recorded on the stream the kernels run on.  `cpu_baseline` times the FP64 numpy
+oracle on a bounded sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s and % of peak, fused_add_rmsnorm fwd + train bwd"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (8 TB/s)
+C2 = (8192, 4096)
+C4 = (16384, 8192)
+
+
+def alg_bytes():
+    """Algorithmic HBM bytes per launch (each tensor of the definition once)."""
+    t2, h2 = C2
+    t4, h4 = C4
+    e2, e4 = t2 * h2, t4 * h4
+    return {
+        # read x, residual; write h_new (into residual) and y (into x); bf16 weight
+        "fused_add_rmsnorm": 8 * e2 + 2 * h2,
+        # read x, residual; write h_new and FP8 out; bf16 weight; scale
+        "fused_add_rmsnorm_quant": 7 * e2 + 2 * h2 + 4,
+        # read h, residual; write y, h_new; FP32 rstd out; FP32 weight
+        "train_forward": 8 * e4 + 4 * t4 + 4 * h4,
+        # stage 1: read g, x (h_new), rstd, FP32 weight; write dx
+        "train_backward_partials": 6 * e4 + 4 * t4 + 4 * h4,
+        # stage 2: write dw (its workspace reads are not algorithmic)
+        "train_backward_reduce": 4 * h4,
+    }
+
+
+def cpu_baseline(seconds: float = 10.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: row blocks of the
+    fused-add + static-FP8 forward [*, 4096] and of the training forward and backward
+    [*, 8192], repeated until `seconds` of CPU time have passed."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import formats as F
+    from oracle import rmsnorm as O
+
+    def vals(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return F.bf16_bits_to_f64(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+        return t.double().numpy()
+
+    fa = W.fused_add_quant(rows=256)
+    tr = W.train(rows=128)
+    x, r, w = vals(fa.tensors["x"]), vals(fa.tensors["residual"]), vals(fa.tensors["w"])
+    h, u, w4, g = (vals(tr.tensors[k]) for k in ("h", "residual", "w", "g"))
+    b2 = 256 * C2[1]
+    b4 = 128 * C4[1]
+    per_pass = (7 * b2 + 2 * C2[1]) + (8 * b4 + 4 * 128 + 4 * C4[1]) + (6 * b4 + 4 * 128 + 8 * C4[1])
+    done, t0 = 0, time.perf_counter()
+    while True:
+        O.fused_add_rmsnorm_quant(x, r, w, 0.04, 0.0, 1e-6)
+        tf = O.train_forward(h, w4, 1.0, 1e-6, residual=u)
+        O.train_backward(g, tf.h_new, w4, tf.rstd, 1.0)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(per_pass * done / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} passes of: fused add + RMSNorm + static FP8 on 256 rows x 4096, "
+                      f"training forward and backward on 128 rows x 8192 "
+                      f"({el:.1f} s, single-threaded numpy FP64)"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
+              f"MI355X (rows shard across GPUs with no communication except dw); --gpus {a.gpus} "
+              f"is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs", file=sys.stderr, flush=True)
+    c2 = W.fused_add_quant()
+    x2, r2, w2 = (c2.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    x2q, r2q = c2.tensors["x"].to(dev), c2.tensors["residual"].to(dev)
+    c4 = W.train()
+    h4, u4, w4, g4 = (c4.tensors[k].to(dev) for k in ("h", "residual", "w", "g"))
+    T4, H4 = C4
+    y4 = torch.empty_like(h4)
+    hn4 = torch.empty_like(h4)
+    rs4 = torch.empty(T4, dtype=torch.float32, device=dev)
+    dx4 = torch.empty_like(h4)
+    dw4 = torch.empty(H4, dtype=torch.float32, device=dev)
+    q2 = torch.empty(C2, dtype=torch.float8_e4m3fn, device=dev)
+    scale = torch.tensor([0.04], dtype=torch.float32, device=dev)
+    ws = dn.train_backward_workspace(H4, dev)
+
+    names = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
+             "train_backward_partials", "train_backward_reduce"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        dn.dn_fused_add_rmsnorm(x2, r2, w2, 1e-6)
+        mark(1)
+        dn.dn_train_forward(h4, w4, 1e-6, w_bias=1.0, residual=u4, out=y4, rstd=rs4,
+                            residual_out=hn4)
+        mark(2)
+        dn.dn_fused_add_rmsnorm_quant(x2q, r2q, w2, scale, 1e-6, out=q2)
+        mark(3)
+        dn.dn_train_backward_partials(g4, hn4, w4, rs4, ws, w_bias=1.0, dx=dx4)
+        mark(4)
+        dn.dn_train_backward_reduce(ws, T4, H4, dw=dw4)
+        mark(5)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between synchronisations (wall clock), with per-kernel events.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e-3)
+    ab = alg_bytes()
+    step_bytes = sum(ab.values())
+    ms_per_step = wall / a.steps * 1e3
+    value = step_bytes / (wall / a.steps) / 1e9
+
+    kernels = {}
+    for n in names:
+        avg = sum(per[n]) / len(per[n])
+        gbs = ab[n] / avg / 1e9
+        kernels[n] = {"us": round(avg * 1e6, 2), "bytes": ab[n], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    bwd_s = (sum(per["train_backward_partials"]) + sum(per["train_backward_reduce"])) / a.steps
+    bwd_b = ab["train_backward_partials"] + ab["train_backward_reduce"]
+    fa_s = sum(per["fused_add_rmsnorm"]) / a.steps
+    headline = {
+        "fused_add_rmsnorm_fwd_GB/s": round(ab["fused_add_rmsnorm"] / fa_s / 1e9, 1),
+        "train_bwd_GB/s": round(bwd_b / bwd_s / 1e9, 1),
+        "fused_add_fwd_plus_train_bwd_GB/s": round((ab["fused_add_rmsnorm"] + bwd_b) /
+                                                  (fa_s + bwd_s) / 1e9, 1),
+    }
+    dom = max(names, key=lambda n: sum(per[n]))
+    dom_avg = sum(per[dom]) / len(per[dom])
+    achieved = ab[dom] / dom_avg / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({a.cpu_seconds:.0f} s of oracle work)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(a.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "fused_add_rmsnorm fwd BF16 [8192,4096] (plain and static FP8) + "
+                               "training RMSNorm fwd+bwd with residual BF16 [16384,8192], "
+                               "FP32 weight 1+w",
+                   "storage": "bf16 activations, fp32 statistics/weights, e4m3fn outputs",
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "step_bytes": step_bytes, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "headline": headline,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -44,9 +44,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *COMPILE_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, extra=(), objdir: str = BUILD) -> str:
+    obj = os.path.join(objdir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *COMPILE_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,22 +60,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP unit for gfx950 and link libdnorm.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compile every HIP unit for gfx950 and link libdnorm.so (or `out`); returns its path.
+    `extra` adds compiler flags (tuning builds); objects then go to a separate folder."""
+    tag = "".join(c if c.isalnum() else "_" for c in "".join(extra))
+    objdir = BUILD if not extra else os.path.join(BUILD, "variant" + tag)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, extra, objdir), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None) -> int:

@@ -27,6 +27,17 @@ constexpr int64_t kMaxStride = (int64_t)1 << 24;
 // of FP32 per block); wider rows read it from global memory (L2-resident) instead.
 constexpr int kMaxLdsWeightVectors = 1024;
 
+// Persistent forward grids hold at most DN_BLOCKS_PER_CU blocks per compute unit: on
+// MI355X fewer streams in flight keep HBM more efficient (measured 2 blocks of 256 threads
+// per CU ahead of full occupancy).  Tuning builds can override it (0 = as many as are
+// resident) and the backward row tier (-1 = by hidden size).
+#ifndef DN_BLOCKS_PER_CU
+#define DN_BLOCKS_PER_CU 2
+#endif
+#ifndef DN_BWD_TIER
+#define DN_BWD_TIER -1
+#endif
+
 thread_local std::string g_error;
 std::atomic<int> g_force_tpr{0};
 
@@ -127,6 +138,7 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int* out) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, lds) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
+    if (DN_BLOCKS_PER_CU > 0 && per_cu > DN_BLOCKS_PER_CU) per_cu = DN_BLOCKS_PER_CU;
     ot = c.occ.emplace(key, per_cu).first;
   }
   *out = it->second * ot->second;
@@ -136,7 +148,8 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int* out) {
 // ------------------------------------------------------------------ forward dispatch
 
 int pick_fwd_tier(int nvec, int limit, int forced) {
-  for (int t = 0; t < kFwdTierCount; ++t) {
+  const int count = forced ? kFwdTierCount : kFwdAutoTiers;
+  for (int t = 0; t < count; ++t) {
     const TierShape s = fwd_tier_shape(t);
     if (s.vmax > limit || s.tpr * s.vmax < nvec) continue;
     if (forced && s.tpr != forced) continue;
@@ -180,6 +193,10 @@ FwdParams base_params(int64_t rows, int64_t hidden, float eps) {
 // ------------------------------------------------------------------ backward dispatch
 
 int pick_bwd_tier(int nvec) {
+  if (DN_BWD_TIER >= 0 && DN_BWD_TIER < kBwdTierCount) {
+    const TierShape s = bwd_tier_shape(DN_BWD_TIER);
+    if (s.tpr * s.vmax >= nvec) return DN_BWD_TIER;
+  }
   for (int t = 0; t < kBwdTierCount; ++t) {
     const TierShape s = bwd_tier_shape(t);
     if (s.tpr * s.vmax >= nvec) return t;
@@ -230,11 +247,11 @@ dn_status dn_rmsnorm(void* y, int64_t y_stride, float* rstd, const void* x, int6
                      const void* w, int w_dtype, float w_bias, int64_t rows, int64_t hidden,
                      float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(y, y_stride, hidden, 2, "y"));
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(rstd, "rstd", false));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.y = static_cast<uint16_t*>(y); p.sy = y_stride;
@@ -247,11 +264,11 @@ dn_status dn_rmsnorm_quant(uint8_t* out, int64_t out_stride, const void* x, int6
                            const void* w, int w_dtype, float w_bias, const float* scale,
                            int64_t rows, int64_t hidden, float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(scale, "scale", true));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.q = out; p.sq = out_stride;
@@ -265,11 +282,11 @@ dn_status dn_fused_add_rmsnorm(void* x, int64_t x_stride, void* residual,
                                float w_bias, float* rstd, int64_t rows, int64_t hidden,
                                float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(rstd, "rstd", false));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
@@ -286,12 +303,12 @@ dn_status dn_fused_add_rmsnorm_quant(uint8_t* out, int64_t out_stride, const voi
                                      const float* scale, int64_t rows, int64_t hidden,
                                      float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
   DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(scale, "scale", true));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
@@ -310,6 +327,7 @@ dn_status dn_fused_add_rmsnorm_fp8_block_quant(uint8_t* out, int64_t out_stride,
                                                int w_dtype, float w_bias, int64_t rows,
                                                int64_t hidden, float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 128, "hidden (1x128 blocks)"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
   DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
@@ -319,7 +337,6 @@ dn_status dn_fused_add_rmsnorm_fp8_block_quant(uint8_t* out, int64_t out_stride,
   if (scale_ld < rows)
     return fail(DN_ERR_SHAPE, "scale_ld %lld is smaller than rows %lld", (long long)scale_ld,
                 (long long)rows);
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
@@ -346,12 +363,12 @@ dn_status dn_ada_rms_norm(void* out, int64_t out_stride, void* gate_out,
                           int64_t style_rows, int64_t rows, int64_t dim, float eps,
                           dn_stream_t stream) {
   DN_CHECK(check_shape(rows, dim, 8, "dim"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, dim, 2, "x"));
   DN_CHECK(check_matrix(out, out_stride, dim, 2, "out"));
   if (gate_out) DN_CHECK(check_matrix(gate_out, gate_out_stride, dim, 2, "gate_out"));
   DN_CHECK(check_weight(w, DN_WEIGHT_BF16));
   DN_CHECK(check_style(style, style_stride, style_rows, rows, dim));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, dim, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.y = static_cast<uint16_t*>(out); p.sy = out_stride;
@@ -370,6 +387,7 @@ dn_status dn_gate_residual_ada_norm_fp8(void* residual, int64_t residual_stride,
                                         int64_t style_rows, const float* scale, int64_t rows,
                                         int64_t dim, float eps, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, dim, 8, "dim"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(residual, residual_stride, dim, 2, "residual"));
   DN_CHECK(check_matrix(x, x_stride, dim, 2, "x"));
   DN_CHECK(check_matrix(gate, gate_stride, dim, 2, "gate"));
@@ -378,7 +396,6 @@ dn_status dn_gate_residual_ada_norm_fp8(void* residual, int64_t residual_stride,
   DN_CHECK(check_weight(w, DN_WEIGHT_BF16));
   DN_CHECK(check_style(style, style_stride, style_rows, rows, dim));
   DN_CHECK(check_f32(scale, "scale", true));
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, dim, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
@@ -399,6 +416,7 @@ dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd, void* h_new,
                            int w_dtype, float w_bias, int64_t rows, int64_t hidden, float eps,
                            dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   DN_CHECK(check_matrix(y, y_stride, hidden, 2, "y"));
   DN_CHECK(check_weight(w, w_dtype));
@@ -407,7 +425,6 @@ dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd, void* h_new,
     DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
     DN_CHECK(check_matrix(h_new, h_new_stride, hidden, 2, "h_new"));
   }
-  if (rows == 0) return DN_OK;
   FwdParams p = base_params(rows, hidden, eps);
   p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
   p.y = static_cast<uint16_t*>(y); p.sy = y_stride;
@@ -429,6 +446,7 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
                                      size_t workspace_bytes_, int64_t rows, int64_t hidden,
                                      dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_matrix(dx, dx_stride, hidden, 2, "dx"));
   DN_CHECK(check_matrix(g, g_stride, hidden, 2, "g"));
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
@@ -436,7 +454,6 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(rstd, "rstd", true));
   DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
-  if (rows == 0) return DN_OK;
   BwdParams p{};
   p.dx = static_cast<uint16_t*>(dx); p.sdx = dx_stride;
   p.g = static_cast<const uint16_t*>(g); p.sg = g_stride;
@@ -463,9 +480,9 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
 dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes_,
                                    int64_t rows, int64_t hidden, dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
   DN_CHECK(check_f32(dw, "dw", true));
   DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
-  if (rows == 0) return DN_OK;
   const hipError_t e = bwd_reduce_launch(dw, static_cast<const double*>(workspace), (int)hidden,
                                          chunk_count(rows), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -240,8 +240,9 @@ __global__ void __launch_bounds__(NT) bwd_reduce_kernel(float* dw, const double*
   X(0, 8, 1, 4, 256)     X(1, 16, 1, 4, 256)    X(2, 32, 1, 4, 256)            \
   X(3, 64, 1, 4, 256)    X(4, 128, 1, 4, 256)   X(5, 256, 1, 4, 256)           \
   X(6, 512, 1, 4, 512)   X(7, 1024, 1, 4, 1024) X(8, 1024, 2, 2, 1024)         \
-  X(9, 1024, 4, 1, 1024)
+  X(9, 1024, 4, 1, 1024) X(10, 512, 2, 2, 512)   X(11, 512, 2, 4, 512)          \
+  X(12, 1024, 1, 2, 1024) X(13, 1024, 1, 1, 1024) X(14, 512, 2, 1, 512)
 
-constexpr int kBwdTierCount = 10;
+constexpr int kBwdTierCount = 15;
 
 }  // namespace dn

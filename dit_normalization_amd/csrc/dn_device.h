@@ -86,23 +86,37 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // A per-lane offset that no descriptor built here reaches (record counts stay below 2^30).
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 
+// Cache policy of streamed rows (the buffer instructions' cache-policy operand: bit 0 sc0,
+// bit 1 nt, bit 4 sc1).  Every activation byte is touched once, so rows are loaded and
+// stored non-temporally: on MI355X this lifts a streaming read from ~4.6 to ~6.9 TB/s and a
+// read+write copy from ~4.9 to ~5.9 TB/s (measured), where temporal hints only churn the
+// caches.
+#ifndef DN_LOAD_POLICY
+#define DN_LOAD_POLICY 2
+#endif
+#ifndef DN_STORE_POLICY
+#define DN_STORE_POLICY 2
+#endif
+constexpr int kLoadPolicy = DN_LOAD_POLICY;
+constexpr int kStorePolicy = DN_STORE_POLICY;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kRawBufferWord3);
 }
 
 __device__ __forceinline__ v4u bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy));
 }
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const v4u& v) {
   __builtin_amdgcn_raw_buffer_store_b128(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off,
-      0, 0);
+      0, kStorePolicy);
 }
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, const v2u& v) {
   __builtin_amdgcn_raw_buffer_store_b64(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off,
-      0, 0);
+      0, kStorePolicy);
 }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -25,7 +25,8 @@
  *     of 8; per-row FP32 vectors (rstd, block scales, dw) need 4-byte alignment.  Row
  *     strides are at most 2^24 elements.
  *   - hidden must be a positive multiple of 8 and at most dn_max_hidden().
- *   - rows == 0 is valid: the call returns DN_OK and launches nothing ([norm guide] §6.1).
+ *   - rows == 0 is valid: once rows and hidden pass their checks the call returns DN_OK
+ *     and launches nothing; pointers may then be NULL ([norm guide] §6.1).
  *   - Outputs are caller-owned and preallocated (destination passing, [norm guide] §2.1).
  *     An output may alias an input exactly (same pointer, same stride) -- that is how the
  *     in-place calls work -- but must not overlap it in any other way.

@@ -96,6 +96,7 @@ def test_rmsnorm_argument_checks(lib):
     assert rms(lib, w=C + 4) == E_ALIGN
     assert rms(lib, rstd=D + 2) == E_ALIGN
     assert rms(lib, rows=0, rstd=D) == OK
+    assert rms(lib, rows=0, x=0, y=0, w=0) == OK           # empty tensors carry NULL
 
 
 def test_quant_and_fused_add_checks(lib):
@@ -125,7 +126,8 @@ def test_block_quant_checks(lib):
     assert call(h=7160, os=7160, xs=7160, rs=7160) == E_UNSUP   # not a multiple of 128
     assert call(ld=100) == E_SHAPE                              # scale_ld < rows
     assert call(bs=0) == E_NULL
-    assert call(no=A + 16, ns=7000, rows=0) == E_SHAPE          # normed_out stride < hidden
+    assert call(no=A + 16, ns=7000, rows=5, ld=8) == E_SHAPE    # normed_out stride < hidden
+    assert call(out=0, bs=0, x=0, r=0, rows=0) == OK            # empty: NULL pointers allowed
 
 
 def test_ada_checks(lib):
