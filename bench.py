@@ -54,6 +54,34 @@ def alg_bytes():
     }
 
 
+def kernel_source_sha256() -> str:
+    """Fingerprint of the library's kernel sources (every file of dit_normalization_amd/csrc)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dit_normalization_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy), or None when the kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except OSError:
+        return None
+    if d.get("source_sha256") != kernel_source_sha256():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k["traffic_bytes"]
+
+
 def cpu_baseline(seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same workload: row blocks of the
     fused-add + static-FP8 forward [*, 4096] and of the training forward and backward
@@ -100,6 +128,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
+                         "times, to scale profiler byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
@@ -151,6 +182,13 @@ def main(argv=None) -> int:
         dn.dn_train_backward_reduce(ws, T4, H4, dw=dw4)
         mark(5)
 
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         step()
@@ -195,7 +233,7 @@ def main(argv=None) -> int:
     achieved = ab[dom] / dom_avg / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom]}
 
     cpu = None
     if not a.no_cpu_baseline:

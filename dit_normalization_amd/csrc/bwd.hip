@@ -6,15 +6,16 @@ namespace dn {
 hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStream_t s,
                                const void** kernel_out) {
   switch (tier) {
-#define DN_X(i, tpr, v, r, nt)                                         \
-  case i: {                                                           \
-    auto k = bwd_partials_kernel<tpr, v, r, nt>;                      \
-    if (kernel_out) {                                                 \
-      *kernel_out = reinterpret_cast<const void*>(k);                 \
-      return hipSuccess;                                              \
-    }                                                                 \
-    hipLaunchKernelGGL(k, dim3(p.chunks), dim3(nt), lds, s, p);       \
-    return hipGetLastError();                                         \
+#define DN_X(i, tpr, v, r, nt)                                                       \
+  case i: {                                                                         \
+    auto k = p.gres ? bwd_partials_kernel<tpr, v, r, nt, true>                      \
+                    : bwd_partials_kernel<tpr, v, r, nt, false>;                    \
+    if (kernel_out) {                                                               \
+      *kernel_out = reinterpret_cast<const void*>(k);                               \
+      return hipSuccess;                                                            \
+    }                                                                               \
+    hipLaunchKernelGGL(k, dim3(p.chunks), dim3(nt), lds, s, p);                     \
+    return hipGetLastError();                                                       \
   }
     DN_BWD_TIERS(DN_X)
 #undef DN_X

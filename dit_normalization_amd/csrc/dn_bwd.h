@@ -57,8 +57,31 @@ __host__ __device__ inline size_t bwd_lds_bytes(int g, int wpr, int rb, int nt, 
   return red > comb ? red : comb;
 }
 
-template <int TPR, int VB, int RB, int NT>
+// One step of stage 1: the RB row slots of this thread's row group and their data.
+template <int VB, int RB>
+struct BwdStep {
+  int64_t row[RB];
+  bool rok[RB];
+  float rs[RB];
+  v4u g[RB][VB], x[RB][VB], r[RB][VB];
+};
+
+// Two steps are kept in flight when both fit in the VGPRs a wave may use at this block size
+// (the data of a step, the FP64 column sums, the weights and ~64 working registers): a
+// block owns a whole CU here, so without the prefetch its memory pipe would idle through
+// every cross-wave barrier (measured 5.29 -> 5.42 TB/s for stage 1 at [16384, 8192]).
+constexpr bool bwd_double_buffer(int vb, int rb, int nt, bool gres) {
+#ifdef DN_NO_PREFETCH
+  return false;
+#endif
+  const int step = rb * vb * 4 * (gres ? 3 : 2);
+  const int budget = nt >= 1024 ? 128 : 256;
+  return 2 * step + vb * 16 + vb * 8 + 64 <= budget;
+}
+
+template <int TPR, int VB, int RB, int NT, bool GRES>
 __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
+  constexpr bool kDB = bwd_double_buffer(VB, RB, NT, GRES);
   extern __shared__ __align__(16) unsigned char dn_lds[];
   using Geom = RowGeom<TPR, RB, NT>;
   constexpr int G = Geom::G;
@@ -90,38 +113,37 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
     for (int k = 0; k < 8; ++k) acc[v][k] = 0.0;
   }
 
-  int parity = 0;
-  for (int64_t base = rb; base < re; base += Geom::PER_ITER) {
+  // Issue every load of the step starting at row `base` (rows past the chunk read zeros).
+  auto load = [&](BwdStep<VB, RB>& st, int64_t base) {
     const int64_t first = geo.first(base);
-    int64_t row[RB];
-    bool rok[RB];
-    float rs[RB];
-    v4u gv[RB][VB], xv[RB][VB], rv[RB][VB];
-    rsrc_t rg[RB], rx[RB], rr_[RB], rdx[RB];
-    uint32_t og[RB], ox[RB], or_[RB], odx[RB];
+    rsrc_t rg[RB], rx[RB], rr_[RB];
+    uint32_t og[RB], ox[RB], or_[RB];
     tensor_span<TPR, RB, RPW>(p.g, p.sg, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rg,
                               og);
     tensor_span<TPR, RB, RPW>(p.x, p.sx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rx,
                               ox);
-    if (p.gres)
+    if constexpr (GRES)
       tensor_span<TPR, RB, RPW>(p.gres, p.sgr, 2, 16, row_bf16, first, re, lane, geo.j,
                                 lane_ok, rr_, or_);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      row[rr] = geo.row(first, rr);
-      rok[rr] = row[rr] < re;
-      rs[rr] = rok[rr] ? p.rstd[row[rr]] : 0.0f;
+      st.row[rr] = geo.row(first, rr);
+      st.rok[rr] = st.row[rr] < re;
+      st.rs[rr] = st.rok[rr] ? p.rstd[st.row[rr]] : 0.0f;
 #pragma unroll
       for (int v = 0; v < VB; ++v) {
         const uint32_t dv = (uint32_t)(v * TPR * 16);
-        gv[rr][v] = bload16(rg[rr], og[rr] + dv);
-        xv[rr][v] = bload16(rx[rr], ox[rr] + dv);
-        rv[rr][v] = v4u{0u, 0u, 0u, 0u};
-        if (p.gres) rv[rr][v] = bload16(rr_[rr], or_[rr] + dv);
+        st.g[rr][v] = bload16(rg[rr], og[rr] + dv);
+        st.x[rr][v] = bload16(rx[rr], ox[rr] + dv);
+        if constexpr (GRES) st.r[rr][v] = bload16(rr_[rr], or_[rr] + dv);
       }
     }
+  };
 
-    // Row dot products sum_j g*w_eff*x (lanes past the row end loaded zeros).
+  int parity = 0;
+  // Row dot products, dx, and the FP64 column sums of one loaded step.
+  auto process = [&](BwdStep<VB, RB>& st, int64_t base) {
+    const int64_t first = geo.first(base);
     double dot[RB];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -129,12 +151,12 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
 #pragma unroll
       for (int v = 0; v < VB; ++v) {
         float fg[8], fx[8];
-        unpack8(gv[rr][v], fg);
-        unpack8(xv[rr][v], fx);
+        unpack8(st.g[rr][v], fg);
+        unpack8(st.x[rr][v], fx);
 #pragma unroll
         for (int k = 0; k < 8; ++k) d = fmaf(fg[k] * we[v][k], fx[k], d);
-        keep_packed(gv[rr][v]);
-        keep_packed(xv[rr][v]);
+        keep_packed(st.g[rr][v]);
+        keep_packed(st.x[rr][v]);
       }
       dot[rr] = group_sum<RW>((double)d);
     }
@@ -155,27 +177,57 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
       }
       parity ^= 1;
     }
-
-    // dx and the FP64 column sums (rows past the chunk carry r = 0 and add nothing).
+    rsrc_t rdx[RB];
+    uint32_t odx[RB];
     tensor_span<TPR, RB, RPW>(p.dx, p.sdx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok,
                               rdx, odx);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      const double r64 = (double)rs[rr];
+      // Rows past the chunk carry r = 0 and add nothing; their dx stores are dropped.
+      const double r64 = (double)st.rs[rr];
       const float coef = (float)(r64 * r64 * r64 * (dot[rr] * inv_hidden));
 #pragma unroll
       for (int v = 0; v < VB; ++v) {
-        float fg[8], fx[8], fr[8], d[8];
-        unpack8(gv[rr][v], fg);
-        unpack8(xv[rr][v], fx);
-        unpack8(rv[rr][v], fr);
+        float fg[8], fx[8], d[8];
+        unpack8(st.g[rr][v], fg);
+        unpack8(st.x[rr][v], fx);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          d[k] = fmaf(-fx[k], coef, (fg[k] * we[v][k]) * rs[rr]) + fr[k];
+        for (int k = 0; k < 8; ++k) d[k] = fmaf(-fx[k], coef, (fg[k] * we[v][k]) * st.rs[rr]);
+        if constexpr (GRES) {
+          float fr[8];
+          unpack8(st.r[rr][v], fr);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) d[k] += fr[k];
+        }
         bstore16(rdx[rr], odx[rr] + (uint32_t)(v * TPR * 16), pack8(d));
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[v][k] = fma((double)(fg[k] * fx[k]), r64, acc[v][k]);
       }
+    }
+  };
+
+  if constexpr (kDB) {
+    // Two steps in flight: the next step's loads are issued before the current step's
+    // reduction and barrier, so the memory pipe stays busy through them.
+    BwdStep<VB, RB> s0, s1;
+    int64_t base = rb;
+    if (base < re) load(s0, base);
+    while (base < re) {
+      int64_t nb = base + Geom::PER_ITER;
+      if (nb < re) load(s1, nb);
+      process(s0, base);
+      base = nb;
+      if (base >= re) break;
+      nb = base + Geom::PER_ITER;
+      if (nb < re) load(s0, nb);
+      process(s1, base);
+      base = nb;
+    }
+  } else {
+    BwdStep<VB, RB> s0;
+    for (int64_t base = rb; base < re; base += Geom::PER_ITER) {
+      load(s0, base);
+      process(s0, base);
     }
   }
 
@@ -235,14 +287,17 @@ __global__ void __launch_bounds__(NT) bwd_reduce_kernel(float* dw, const double*
   }
 }
 
-// (threads per row, vectors per thread, rows per group per iteration, threads per block)
+// (threads per row, vectors per thread, rows per group per step, threads per block).
+// The host takes the first tier, in this order, whose TPR*VB covers hidden/8; the tiers
+// after the tenth are alternatives for tuning builds.  From 512 threads up a row spans the
+// whole block, so a block owns all columns of its chunk.
 #define DN_BWD_TIERS(X)                                                         \
   X(0, 8, 1, 4, 256)     X(1, 16, 1, 4, 256)    X(2, 32, 1, 4, 256)            \
   X(3, 64, 1, 4, 256)    X(4, 128, 1, 4, 256)   X(5, 256, 1, 4, 256)           \
-  X(6, 512, 1, 4, 512)   X(7, 1024, 1, 4, 1024) X(8, 1024, 2, 2, 1024)         \
-  X(9, 1024, 4, 1, 1024) X(10, 512, 2, 2, 512)   X(11, 512, 2, 4, 512)          \
-  X(12, 1024, 1, 2, 1024) X(13, 1024, 1, 1, 1024) X(14, 512, 2, 1, 512)
+  X(6, 512, 1, 4, 512)   X(7, 512, 2, 2, 512)   X(8, 512, 4, 1, 512)           \
+  X(9, 1024, 4, 1, 1024) X(10, 1024, 1, 4, 1024) X(11, 512, 2, 4, 512)         \
+  X(12, 1024, 1, 2, 1024) X(13, 512, 1, 2, 512)
 
-constexpr int kBwdTierCount = 15;
+constexpr int kBwdTierCount = 14;
 
 }  // namespace dn

@@ -108,6 +108,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ v4u bload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy));
 }
+// Temporal load: for data every row reads again (a broadcast style row).
+__device__ __forceinline__ v4u bload16_keep(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const v4u& v) {
   __builtin_amdgcn_raw_buffer_store_b128(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off,

@@ -71,10 +71,38 @@ __host__ __device__ inline size_t fwd_lds_bytes(int nvec, int w_in_lds, int g, i
   return (w_in_lds ? (size_t)32 * nvec : 0) + (size_t)2 * g * wpr * r * sizeof(double);
 }
 
+// The data one step of the forward loads: R row slots of VMAX vectors per tensor.
+template <int R, int VMAX>
+struct FwdStep {
+  int64_t row[R];
+  bool rok[R];
+  v4u a[R][VMAX];                               // x, then h
+  v4u b[R][VMAX];                               // residual
+  v4u c[R][VMAX];                               // gate
+  v4u ssc[R][VMAX], ssh[R][VMAX], sgt[R][VMAX]; // Ada style chunks
+};
+
+// Prefetching the next step (two steps in flight) is built in but off by default for the
+// forward: on MI355X it measured slower for the forward rows (train forward at H=8192:
+// 5.86 TB/s without, 5.67 TB/s with) -- HBM streams better with fewer bytes in flight per
+// wave.  A tuning build enables it with DN_FWD_PREFETCH; it is used only when both steps
+// fit in the VGPRs a wave may use at this block size.
+constexpr bool fwd_double_buffer(int in, int epi, int vmax, int r, int nt) {
+#ifndef DN_FWD_PREFETCH
+  return false;
+#endif
+  const int tensors = 1 + (in != IN_PLAIN) + (in == IN_GATED) +
+                      3 * (epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8);
+  const int step = tensors * 4 * vmax * r;
+  const int budget = nt >= 1024 ? 128 : 256;
+  return 2 * step + 96 <= budget;
+}
+
 template <int IN, int EPI, int TPR, int VMAX, int R, int NT>
 __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   extern __shared__ __align__(16) unsigned char dn_lds[];
   using Geom = RowGeom<TPR, R, NT>;
+  using Step = FwdStep<R, VMAX>;
   constexpr int G = Geom::G;
   constexpr int WPR = Geom::WPR;
   constexpr int RPW = Geom::RPW;
@@ -82,6 +110,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   constexpr bool kAda = (EPI == EPI_ADA_BF16 || EPI == EPI_ADA_FP8);
   constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8);
   constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8);
+  constexpr bool kDB = fwd_double_buffer(IN, EPI, VMAX, R, NT);
 
   const Geom geo;
   const int tid = threadIdx.x;
@@ -121,63 +150,62 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   const double eps = (double)p.eps;
   int parity = 0;
 
-  for (int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER; base < p.rows;
-       base += (int64_t)gridDim.x * Geom::PER_ITER) {
+  // 1) Issue every load of the step starting at row `base`.
+  auto load = [&](Step& st, int64_t base) {
     const int64_t first = geo.first(base);
-    int64_t row[R];
-    bool rok[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      row[rr] = geo.row(first, rr);
-      rok[rr] = row[rr] < p.rows;
+      st.row[rr] = geo.row(first, rr);
+      st.rok[rr] = st.row[rr] < p.rows;
     }
-
-    // 1) Issue every load of the step before any use.
-    v4u a[R][VMAX];                               // x, then h
-    v4u b[R][VMAX];                               // residual
-    v4u c[R][VMAX];                               // gate
-    v4u ssc[R][VMAX], ssh[R][VMAX], sgt[R][VMAX]; // Ada style chunks
-    {
-      rsrc_t rx[R], rres[R], rg[R], rst[R];
-      uint32_t ox[R], ores[R], og[R], ost[R];
-      tensor_span<TPR, R, RPW>(p.x, p.sx, 2, 16, row_bf16, first, p.rows, lane, geo.j, lane_ok,
-                               rx, ox);
-      if constexpr (IN != IN_PLAIN)
-        tensor_span<TPR, R, RPW>(p.r, p.sr, 2, 16, row_bf16, first, p.rows, lane, geo.j,
-                                 lane_ok, rres, ores);
-      if constexpr (IN == IN_GATED)
-        tensor_span<TPR, R, RPW>(p.gate, p.sg, 2, 16, row_bf16, first, p.rows, lane, geo.j,
-                                 lane_ok, rg, og);
-      if constexpr (kAda) {
-        if (p.style_bcast) {
-          // Every row reads the single style row.
+    rsrc_t rx[R], rres[R], rg[R], rst[R];
+    uint32_t ox[R], ores[R], og[R], ost[R];
+    tensor_span<TPR, R, RPW>(p.x, p.sx, 2, 16, row_bf16, first, p.rows, lane, geo.j, lane_ok,
+                             rx, ox);
+    if constexpr (IN != IN_PLAIN)
+      tensor_span<TPR, R, RPW>(p.r, p.sr, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                               lane_ok, rres, ores);
+    if constexpr (IN == IN_GATED)
+      tensor_span<TPR, R, RPW>(p.gate, p.sg, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                               lane_ok, rg, og);
+    if constexpr (kAda) {
+      if (p.style_bcast) {
+        // Every row reads the single style row.
 #pragma unroll
-          for (int rr = 0; rr < R; ++rr) {
-            rst[rr] = make_rsrc(p.style, 3u * row_bf16);
-            ost[rr] = lane_ok ? (uint32_t)(lane * 16) : kOutOfRange;
-          }
-        } else {
-          tensor_span<TPR, R, RPW>(p.style, p.sst, 2, 16, 3u * row_bf16, first, p.rows, lane,
-                                   geo.j, lane_ok, rst, ost);
+        for (int rr = 0; rr < R; ++rr) {
+          rst[rr] = make_rsrc(p.style, 3u * row_bf16);
+          ost[rr] = lane_ok ? (uint32_t)(lane * 16) : kOutOfRange;
         }
+      } else {
+        tensor_span<TPR, R, RPW>(p.style, p.sst, 2, 16, 3u * row_bf16, first, p.rows, lane,
+                                 geo.j, lane_ok, rst, ost);
       }
+    }
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
+    for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
-        for (int v = 0; v < VMAX; ++v) {
-          const uint32_t dv = (uint32_t)(v * TPR * 16);
-          a[rr][v] = bload16(rx[rr], ox[rr] + dv);
-          if constexpr (IN != IN_PLAIN) b[rr][v] = bload16(rres[rr], ores[rr] + dv);
-          if constexpr (IN == IN_GATED) c[rr][v] = bload16(rg[rr], og[rr] + dv);
-          if constexpr (kAda) {
-            ssc[rr][v] = bload16(rst[rr], ost[rr] + dv);
-            ssh[rr][v] = bload16(rst[rr], ost[rr] + dv + row_bf16);
-            sgt[rr][v] = bload16(rst[rr], ost[rr] + dv + 2u * row_bf16);
+      for (int v = 0; v < VMAX; ++v) {
+        const uint32_t dv = (uint32_t)(v * TPR * 16);
+        st.a[rr][v] = bload16(rx[rr], ox[rr] + dv);
+        if constexpr (IN != IN_PLAIN) st.b[rr][v] = bload16(rres[rr], ores[rr] + dv);
+        if constexpr (IN == IN_GATED) st.c[rr][v] = bload16(rg[rr], og[rr] + dv);
+        if constexpr (kAda) {
+          if (p.style_bcast) {     // one style row serves every token: keep it cached
+            st.ssc[rr][v] = bload16_keep(rst[rr], ost[rr] + dv);
+            st.ssh[rr][v] = bload16_keep(rst[rr], ost[rr] + dv + row_bf16);
+            st.sgt[rr][v] = bload16_keep(rst[rr], ost[rr] + dv + 2u * row_bf16);
+          } else {
+            st.ssc[rr][v] = bload16(rst[rr], ost[rr] + dv);
+            st.ssh[rr][v] = bload16(rst[rr], ost[rr] + dv + row_bf16);
+            st.sgt[rr][v] = bload16(rst[rr], ost[rr] + dv + 2u * row_bf16);
           }
         }
       }
     }
+  };
 
+  auto process = [&](Step& st, int64_t base) {
+    const int64_t first = geo.first(base);
     // 2) h (rounded to BF16, stored early) and per-lane sums of squares of that BF16 h.
     double ss[R];
     {
@@ -192,23 +220,23 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int v = 0; v < VMAX; ++v) {
           float fh[8];
-          unpack8(a[rr][v], fh);
+          unpack8(st.a[rr][v], fh);
           if constexpr (IN == IN_ADD) {
             float fr[8];
-            unpack8(b[rr][v], fr);
+            unpack8(st.b[rr][v], fr);
 #pragma unroll
             for (int k = 0; k < 8; ++k) fh[k] = fh[k] + fr[k];
           } else if constexpr (IN == IN_GATED) {
             float fr[8], fg[8];
-            unpack8(b[rr][v], fr);
-            unpack8(c[rr][v], fg);
+            unpack8(st.b[rr][v], fr);
+            unpack8(st.c[rr][v], fg);
 #pragma unroll
             for (int k = 0; k < 8; ++k) fh[k] = fmaf(fh[k], fg[k], fr[k]);
           }
           if constexpr (IN != IN_PLAIN) {
-            a[rr][v] = pack8(fh);
-            unpack8(a[rr][v], fh);       // the norm sees the BF16 h_new
-            bstore16(rh[rr], oh[rr] + (uint32_t)(v * TPR * 16), a[rr][v]);
+            st.a[rr][v] = pack8(fh);
+            unpack8(st.a[rr][v], fh);       // the norm sees the BF16 h_new
+            bstore16(rh[rr], oh[rr] + (uint32_t)(v * TPR * 16), st.a[rr][v]);
           }
           // Lanes past the row end loaded zeros: they add nothing.
           ss[rr] += (double)sumsq8(fh);
@@ -220,7 +248,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
-      for (int v = 0; v < VMAX; ++v) keep_packed(a[rr][v]);
+      for (int v = 0; v < VMAX; ++v) keep_packed(st.a[rr][v]);
       ss[rr] = group_sum<RW>(ss[rr]);
     }
     if constexpr (WPR > 1) {
@@ -247,7 +275,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     for (int rr = 0; rr < R; ++rr) {
       const double r64 = 1.0 / sqrt(ss[rr] * inv_hidden + eps);
       rs[rr] = (float)r64;
-      if (p.rstd && lane == 0 && rok[rr]) p.rstd[row[rr]] = rs[rr];
+      if (p.rstd && lane == 0 && st.rok[rr]) p.rstd[st.row[rr]] = rs[rr];
     }
 
     // 5) Epilogue: y = (h * r) * w_eff in FP32, then the output format.
@@ -273,7 +301,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
-        unpack8(a[rr][v], fh);
+        unpack8(st.a[rr][v], fh);
         if (p.w_in_lds) {
           const float4 lo = wl[widx], hi = wl[nvec + widx];
           we[0] = lo.x; we[1] = lo.y; we[2] = lo.z; we[3] = lo.w;
@@ -305,12 +333,12 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) fn[k] *= rcp;
           bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(fn));
-          if ((lane & 15) == 0 && rok[rr] && idx < nvec)
-            p.bscale[(int64_t)(idx >> 4) * p.bld + row[rr]] = s;
+          if ((lane & 15) == 0 && st.rok[rr] && idx < nvec)
+            p.bscale[(int64_t)(idx >> 4) * p.bld + st.row[rr]] = s;
         } else {  // AdaRMSNorm epilogue
           float fsc[8], fsh[8], o[8];
-          unpack8(ssc[rr][v], fsc);
-          unpack8(ssh[rr][v], fsh);
+          unpack8(st.ssc[rr][v], fsc);
+          unpack8(st.ssh[rr][v], fsh);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = fmaf(yv[k], 1.0f + fsc[k], fsh[k]);
           if constexpr (EPI == EPI_ADA_BF16) {
@@ -320,9 +348,35 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
             for (int k = 0; k < 8; ++k) o[k] *= inv_scale;
             bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(o));
           }
-          bstore16(rgo[rr], ogo[rr] + d16, sgt[rr][v]);
+          bstore16(rgo[rr], ogo[rr] + d16, st.sgt[rr][v]);
         }
       }
+    }
+  };
+
+  const int64_t stride = (int64_t)gridDim.x * Geom::PER_ITER;
+  if constexpr (kDB) {
+    // Two steps in flight: the next step's loads are issued before the current step's
+    // arithmetic, reduction and stores.
+    Step s0, s1;
+    int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER;
+    if (base < p.rows) load(s0, base);
+    while (base < p.rows) {
+      int64_t nb = base + stride;
+      if (nb < p.rows) load(s1, nb);
+      process(s0, base);
+      base = nb;
+      if (base >= p.rows) break;
+      nb = base + stride;
+      if (nb < p.rows) load(s0, nb);
+      process(s1, base);
+      base = nb;
+    }
+  } else {
+    Step s0;
+    for (int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER; base < p.rows; base += stride) {
+      load(s0, base);
+      process(s0, base);
     }
   }
 }
