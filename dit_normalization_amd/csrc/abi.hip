@@ -4,6 +4,7 @@
 // Every check runs before the first HIP call, so a rejected call touches no device state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -468,6 +469,15 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
   p.chunks = chunk_count(rows);
   const int tier = pick_bwd_tier(p.nvec);
   if (tier < 0) return fail(DN_ERR_SHAPE, "hidden %lld is too wide", (long long)hidden);
+  // A chunk's rows are every C-th row: rows that share a wave span (narrow rows) sit
+  // C row strides apart, and the span's byte range must stay below 2^30.
+  if (bwd_tier_shape(tier).tpr < 64) {
+    const int64_t widest = std::max(std::max(dx_stride, g_stride),
+                                    std::max(x_stride, g_residual ? g_residual_stride : 0));
+    if ((int64_t)32 * p.chunks * widest * 2 >= ((int64_t)1 << 30))
+      return fail(DN_ERR_SHAPE, "row strides up to %lld elements are supported at hidden %lld",
+                  (long long)(((int64_t)1 << 30) / (64 * p.chunks) - 1), (long long)hidden);
+  }
   const TierShape s = bwd_tier_shape(tier);
   const int gcount = s.nt / s.tpr;
   const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;

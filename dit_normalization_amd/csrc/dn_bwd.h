@@ -1,8 +1,10 @@
 // Training backward of RMSNorm for gfx950: dx plus a bitwise-deterministic FP32 dw.
 //
-// Stage 1 (bwd_partials_kernel): one block per fixed chunk of rows.  Every thread owns a
-// fixed set of 16-byte column vectors for the whole chunk, so its slice of dw stays in
-// FP64 registers while the block streams the chunk's rows:
+// Stage 1 (bwd_partials_kernel): one block per fixed chunk of rows; chunk c of C holds rows
+// c, c + C, c + 2C, ... (C = min(rows, 256)), so at any moment the blocks stream
+// neighbouring rows (HBM serves interleaved streams better than C separate contiguous
+// ranges).  Every thread owns a fixed set of 16-byte column vectors for the whole chunk, so
+// its slice of dw stays in FP64 registers while the block streams the chunk's rows:
 //     per row t:  c_t  = (1/H) sum_j g*w_eff*x         (lane partials in FP32, then FP64)
 //                 dx   = BF16(r*g*w_eff - x*(r^3*c_t) [+ g_residual])
 //     per column: P[chunk][j] += (g*x) * r              (exact products, FP64 sums)
@@ -97,8 +99,16 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
   const bool lane_ok = TPR >= 64 || lane < nvec;
   const uint32_t row_bf16 = 2u * (uint32_t)p.hidden;
   const int chunk = blockIdx.x;
-  const int64_t rb = (int64_t)chunk * p.rows / p.chunks;
-  const int64_t re = (int64_t)(chunk + 1) * p.rows / p.chunks;
+  // The chunk's rows as a strided matrix: logical row j is row chunk + j*C of the inputs.
+  const int64_t C = p.chunks;
+  const int64_t re = (p.rows - chunk + C - 1) / C;     // rows in this chunk
+  const int64_t rb = 0;
+  const uint16_t* g_c = p.g + chunk * p.sg;
+  const uint16_t* x_c = p.x + chunk * p.sx;
+  const uint16_t* gr_c = p.gres ? p.gres + chunk * p.sgr : nullptr;
+  uint16_t* dx_c = p.dx + chunk * p.sdx;
+  const float* rstd_c = p.rstd + chunk;
+  const int64_t sg_c = C * p.sg, sx_c = C * p.sx, sgr_c = C * p.sgr, sdx_c = C * p.sdx;
   const double inv_hidden = 1.0 / (double)p.hidden;
 
   // This thread's columns are fixed for the whole chunk: weights and FP64 column sums
@@ -118,18 +128,18 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
     const int64_t first = geo.first(base);
     rsrc_t rg[RB], rx[RB], rr_[RB];
     uint32_t og[RB], ox[RB], or_[RB];
-    tensor_span<TPR, RB, RPW>(p.g, p.sg, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rg,
+    tensor_span<TPR, RB, RPW>(g_c, sg_c, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rg,
                               og);
-    tensor_span<TPR, RB, RPW>(p.x, p.sx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rx,
+    tensor_span<TPR, RB, RPW>(x_c, sx_c, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok, rx,
                               ox);
     if constexpr (GRES)
-      tensor_span<TPR, RB, RPW>(p.gres, p.sgr, 2, 16, row_bf16, first, re, lane, geo.j,
+      tensor_span<TPR, RB, RPW>(gr_c, sgr_c, 2, 16, row_bf16, first, re, lane, geo.j,
                                 lane_ok, rr_, or_);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       st.row[rr] = geo.row(first, rr);
       st.rok[rr] = st.row[rr] < re;
-      st.rs[rr] = st.rok[rr] ? p.rstd[st.row[rr]] : 0.0f;
+      st.rs[rr] = st.rok[rr] ? rstd_c[st.row[rr] * C] : 0.0f;
 #pragma unroll
       for (int v = 0; v < VB; ++v) {
         const uint32_t dv = (uint32_t)(v * TPR * 16);
@@ -179,7 +189,7 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
     }
     rsrc_t rdx[RB];
     uint32_t odx[RB];
-    tensor_span<TPR, RB, RPW>(p.dx, p.sdx, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok,
+    tensor_span<TPR, RB, RPW>(dx_c, sdx_c, 2, 16, row_bf16, first, re, lane, geo.j, lane_ok,
                               rdx, odx);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
