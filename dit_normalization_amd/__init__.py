@@ -10,11 +10,15 @@ __all__ = [
     "dn_fused_add_rmsnorm_fp8_block_quant", "dn_ada_rms_norm", "dn_gate_residual_ada_norm_fp8",
     "dn_train_forward", "dn_train_backward", "dn_train_backward_partials",
     "dn_train_backward_reduce", "dn_train_backward_workspace_bytes", "train_backward_workspace",
-    "dn_force_threads_per_row", "dn_max_hidden", "DnormError",
+    "dn_force_threads_per_row", "dn_max_hidden", "DnormError", "rmsnorm_train",
+    "RMSNormTrainFunction",
 ]
 
 
 def __getattr__(name):
+    if name in ("rmsnorm_train", "RMSNormTrainFunction"):
+        from . import autograd
+        return getattr(autograd, name)
     if name in __all__:
         from . import dnorm
         return getattr(dnorm, name)

@@ -140,6 +140,12 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int* out) {
         per_cu <= 0)
       per_cu = 1;
     if (DN_BLOCKS_PER_CU > 0 && per_cu > DN_BLOCKS_PER_CU) per_cu = DN_BLOCKS_PER_CU;
+#ifdef DN_WAVES_PER_CU
+    {
+      const int cap = DN_WAVES_PER_CU * 64 / nt;
+      per_cu = std::min(per_cu, cap > 0 ? cap : 1);
+    }
+#endif
     ot = c.occ.emplace(key, per_cu).first;
   }
   *out = it->second * ot->second;

@@ -236,7 +236,9 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           if constexpr (IN != IN_PLAIN) {
             st.a[rr][v] = pack8(fh);
             unpack8(st.a[rr][v], fh);       // the norm sees the BF16 h_new
+#ifndef DN_LATE_H_STORE
             bstore16(rh[rr], oh[rr] + (uint32_t)(v * TPR * 16), st.a[rr][v]);
+#endif
           }
           // Lanes past the row end loaded zeros: they add nothing.
           ss[rr] += (double)sumsq8(fh);
@@ -301,6 +303,15 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
+#ifdef DN_LATE_H_STORE
+        if constexpr (IN != IN_PLAIN) {
+          rsrc_t rh[R];
+          uint32_t oh[R];
+          tensor_span<TPR, R, RPW>(p.h, p.sh, 2, 16, p.h ? row_bf16 : 0u, first,
+                                   p.h ? p.rows : first, lane, geo.j, lane_ok, rh, oh);
+          bstore16(rh[rr], oh[rr] + d16, st.a[rr][v]);
+        }
+#endif
         unpack8(st.a[rr][v], fh);
         if (p.w_in_lds) {
           const float4 lo = wl[widx], hi = wl[nvec + widx];

@@ -1,0 +1,89 @@
+"""GPU parity of the autograd wrapper (forward outputs and gradients vs the FP64 oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import rmsnorm as O
+from tests.conftest import values
+from tests.parity import assert_bf16, assert_bits_equal, assert_dx
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ag():
+    from dit_normalization_amd import autograd
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return autograd
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def assert_dw_composite(gpu, ref: O.TrainBackward, g, x, rstd, what):
+    """dw from the kernel's own rstd: beyond the 1e-5 relative gate, allow what a 2e-7
+    relative difference of each row's rstd (the rstd gate) can move the column sum."""
+    err = np.abs(gpu.detach().float().cpu().double().numpy() - ref.dw_exact)
+    spread = np.sum(np.abs(g * x * np.asarray(rstd)[:, None]), axis=0)
+    bad = err > 1e-5 * np.abs(ref.dw_exact) + 4e-7 * spread
+    assert not bad.any(), f"{what}: {bad.sum()} columns off"
+
+
+def test_autograd_plain_fp32_weight(ag):
+    wl = W.train(rows=300, hidden=4096)
+    t = wl.tensors
+    x = dev(t["h"]).requires_grad_(True)
+    w = dev(t["w"]).requires_grad_(True)
+    y = ag.rmsnorm_train(x, w, 1e-6, w_bias=1.0)
+    y.backward(dev(t["g"]))
+    fwd = O.train_forward(values(t["h"]), values(t["w"]), 1.0, 1e-6)
+    assert_bf16(y.detach(), fwd.y_exact, "y")
+    ref = O.train_backward(values(t["g"]), values(t["h"]), values(t["w"]), fwd.rstd, 1.0)
+    assert_dx(x.grad, ref.dx_exact, "x.grad")
+    assert w.grad.dtype == torch.float32
+    assert_dw_composite(w.grad, ref, values(t["g"]), values(t["h"]), fwd.rstd, "w.grad")
+
+
+def test_autograd_residual_route(ag):
+    wl = W.train(rows=257, hidden=2048)
+    t = wl.tensors
+    wb = W.normal((2048,), 40, 0, mean=1.0, std=0.1)
+    gh = W.normal((257, 2048), 40, 1)
+    h = dev(t["h"]).requires_grad_(True)
+    u = dev(t["residual"]).requires_grad_(True)
+    w = dev(wb).requires_grad_(True)
+    y, h_new = ag.rmsnorm_train(h, w, 1e-6, residual=u)
+    torch.autograd.backward([y, h_new], [dev(t["g"]), dev(gh)])
+    fwd = O.train_forward(values(t["h"]), values(wb), 0.0, 1e-6, residual=values(t["residual"]))
+    assert_bits_equal(h_new.detach(), fwd.h_new, "h_new")
+    assert_bf16(y.detach(), fwd.y_exact, "y")
+    ref = O.train_backward(values(t["g"]), fwd.h_new, values(wb), fwd.rstd, 0.0, values(gh))
+    assert torch.equal(h.grad.view(torch.int16), u.grad.view(torch.int16)), \
+        "both residual inputs get the same gradient"
+    assert_dx(h.grad, ref.dx_exact, "h.grad")
+    assert w.grad.dtype == torch.bfloat16
+    # BF16 dw: one rounding of the FP32 result on top of the gate
+    got = values(w.grad.detach())
+    spread = np.sum(np.abs(values(t["g"]) * fwd.h_new * fwd.rstd[:, None]), axis=0)
+    assert np.all(np.abs(got - ref.dw_exact) <= 2.0 ** -8 * np.abs(ref.dw_exact) + 4e-7 * spread)
+
+
+def test_autograd_3d_input(ag):
+    x0 = W.normal((4, 33, 1024), 41, 0)
+    w0 = W.normal((1024,), 41, 1, mean=1.0, std=0.1)
+    g0 = W.normal((4, 33, 1024), 41, 2)
+    x = dev(x0).requires_grad_(True)
+    w = dev(w0).requires_grad_(True)
+    y = ag.rmsnorm_train(x, w, 1e-6)
+    assert y.shape == (4, 33, 1024)
+    y.backward(dev(g0))
+    x2, g2 = values(x0).reshape(-1, 1024), values(g0).reshape(-1, 1024)
+    fwd = O.train_forward(x2, values(w0), 0.0, 1e-6)
+    assert_bf16(y.detach().reshape(-1, 1024), fwd.y_exact, "y 3d")
+    ref = O.train_backward(g2, x2, values(w0), fwd.rstd, 0.0)
+    assert_dx(x.grad.reshape(-1, 1024), ref.dx_exact, "x.grad 3d")
