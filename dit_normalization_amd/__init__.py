@@ -1,4 +1,5 @@
-"""MI355X-native (gfx950) row-wise RMSNorm family behind a C ABI (include/dnorm.h).
+"""MI355X-native (gfx950) row-wise RMSNorm and LayerNorm families behind a C ABI
+(include/dnorm.h).
 
 ``dit_normalization_amd.dnorm`` is the thin binding of ``libdnorm.so``; its ``dn_*``
 functions are re-exported here on first use.  Importing any of them without the built
@@ -10,6 +11,9 @@ __all__ = [
     "dn_fused_add_rmsnorm_fp8_block_quant", "dn_ada_rms_norm", "dn_gate_residual_ada_norm_fp8",
     "dn_train_forward", "dn_train_backward", "dn_train_backward_partials",
     "dn_train_backward_reduce", "dn_train_backward_workspace_bytes", "train_backward_workspace",
+    "dn_layernorm", "dn_layernorm_quant", "dn_fused_dit_gate_residual_layernorm_gamma_beta",
+    "dn_fused_dit_gate_residual_layernorm_scale_shift",
+    "dn_fused_dit_residual_layernorm_scale_shift",
     "dn_force_threads_per_row", "dn_max_hidden", "DnormError", "rmsnorm_train",
     "RMSNormTrainFunction",
 ]

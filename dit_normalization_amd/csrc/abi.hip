@@ -1,4 +1,4 @@
-// C ABI of the RMSNorm family (include/dnorm.h): host-side argument checks, row-tier
+// C ABI of the RMSNorm and LayerNorm families (include/dnorm.h): host-side argument checks, row-tier
 // selection by hidden size, persistent-grid sizing, and the kernel launches.
 //
 // Every check runs before the first HIP call, so a rejected call touches no device state.
@@ -24,8 +24,9 @@ constexpr int kMaxHidden = 32768;
 // Row strides are bounded so that the rows one wave touches in a step (at most 32) span
 // less than 2^30 bytes: buffer descriptors carry 32-bit record counts.
 constexpr int64_t kMaxStride = (int64_t)1 << 24;
-// The effective weight is staged in LDS up to this many 16-byte column vectors (32 KiB
-// of FP32 per block); wider rows read it from global memory (L2-resident) instead.
+// Per-column parameters are staged in LDS up to this many 16-byte column vectors (32 KiB
+// of FP32 per block for the RMSNorm weight, 64 KiB for LayerNorm gamma and beta); wider
+// rows read them from global memory (L2-resident) instead.
 constexpr int kMaxLdsWeightVectors = 1024;
 
 // Persistent forward grids hold at most DN_BLOCKS_PER_CU blocks per compute unit: on
@@ -173,8 +174,9 @@ dn_status launch_fwd(FwdParams p, hipStream_t stream) {
   const TierShape s = fwd_tier_shape(tier);
   const int g = s.nt / s.tpr;
   const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;
-  p.w_in_lds = p.nvec <= kMaxLdsWeightVectors;
-  const size_t lds = fwd_lds_bytes(p.nvec, p.w_in_lds, g, wpr, s.r);
+  constexpr int planes = fwd_weight_planes(EPI);
+  p.w_in_lds = planes > 0 && p.nvec <= kMaxLdsWeightVectors;
+  const size_t lds = fwd_lds_bytes(p.nvec, p.w_in_lds ? planes : 0, g, wpr, s.r, fwd_stats(EPI));
 
   const void* kernel = nullptr;
   if (fwd_launch<IN, EPI>(p, tier, 0, 0, nullptr, &kernel) != hipSuccess || !kernel)
@@ -227,6 +229,15 @@ dn_status check_workspace(const void* ws, size_t bytes, int64_t hidden) {
 }
 
 int chunk_count(int64_t rows) { return (int)(rows < kMaxChunks ? rows : kMaxChunks); }
+
+// LayerNorm gamma and beta: FP32 [hidden], 16-byte aligned.
+dn_status check_affine(const float* gamma, const float* beta) {
+  if (!gamma) return fail(DN_ERR_NULL, "gamma must not be NULL");
+  if (!beta) return fail(DN_ERR_NULL, "beta must not be NULL");
+  if (!aligned(gamma, 16)) return fail(DN_ERR_ALIGN, "gamma must be 16-byte aligned");
+  if (!aligned(beta, 16)) return fail(DN_ERR_ALIGN, "beta must be 16-byte aligned");
+  return DN_OK;
+}
 
 }  // namespace
 
@@ -516,6 +527,126 @@ dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw, const void* 
                                       w_bias, rstd, g_residual, g_residual_stride, workspace,
                                       workspace_bytes_, rows, hidden, stream));
   return dn_train_backward_reduce(dw, workspace, workspace_bytes_, rows, hidden, stream);
+}
+
+// ------------------------------------------------------------------ LayerNorm family
+
+dn_status dn_layernorm(void* y, int64_t y_stride, const void* x, int64_t x_stride,
+                       const float* gamma, const float* beta, int64_t rows, int64_t hidden,
+                       float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(y, y_stride, hidden, 2, "y"));
+  DN_CHECK(check_affine(gamma, beta));
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.y = static_cast<uint16_t*>(y); p.sy = y_stride;
+  p.w = gamma; p.w_f32 = 1; p.beta = beta;
+  return launch_fwd<IN_PLAIN, EPI_LN_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_layernorm_quant(uint8_t* out, int64_t out_stride, const void* x, int64_t x_stride,
+                             const float* gamma, const float* beta, const float* scale,
+                             int64_t rows, int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(out, out_stride, hidden, 1, "out"));
+  DN_CHECK(check_affine(gamma, beta));
+  DN_CHECK(check_f32(scale, "scale", true));
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.q = out; p.sq = out_stride;
+  p.w = gamma; p.w_f32 = 1; p.beta = beta;
+  p.scale = scale;
+  return launch_fwd<IN_PLAIN, EPI_LN_FP8>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_dit_gate_residual_layernorm_gamma_beta(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* gate, int64_t gate_stride, float gate_bias, const float* gamma,
+    const float* beta, int64_t rows, int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_matrix(gate, gate_stride, hidden, 2, "gate"));
+  DN_CHECK(check_matrix(norm_out, norm_out_stride, hidden, 2, "norm_out"));
+  if (residual_out)
+    DN_CHECK(check_matrix(residual_out, residual_out_stride, hidden, 2, "residual_out"));
+  DN_CHECK(check_affine(gamma, beta));
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.gate = static_cast<const uint16_t*>(gate); p.sg = gate_stride;
+  p.gate_bias = gate_bias;
+  p.h = static_cast<uint16_t*>(residual_out); p.sh = residual_out_stride;
+  p.y = static_cast<uint16_t*>(norm_out); p.sy = norm_out_stride;
+  p.w = gamma; p.w_f32 = 1; p.beta = beta;
+  return launch_fwd<IN_GATED_BIAS, EPI_LN_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_dit_gate_residual_layernorm_scale_shift(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* gate, int64_t gate_stride, float gate_bias, const void* scale,
+    int64_t scale_stride, float scale_bias, const void* shift, int64_t shift_stride,
+    float shift_bias, int64_t rows, int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_matrix(gate, gate_stride, hidden, 2, "gate"));
+  DN_CHECK(check_matrix(scale, scale_stride, hidden, 2, "scale"));
+  DN_CHECK(check_matrix(shift, shift_stride, hidden, 2, "shift"));
+  DN_CHECK(check_matrix(norm_out, norm_out_stride, hidden, 2, "norm_out"));
+  if (residual_out)
+    DN_CHECK(check_matrix(residual_out, residual_out_stride, hidden, 2, "residual_out"));
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.gate = static_cast<const uint16_t*>(gate); p.sg = gate_stride;
+  p.gate_bias = gate_bias;
+  p.msc = static_cast<const uint16_t*>(scale); p.smsc = scale_stride;
+  p.msh = static_cast<const uint16_t*>(shift); p.smsh = shift_stride;
+  p.scale_bias = scale_bias; p.shift_bias = shift_bias;
+  p.h = static_cast<uint16_t*>(residual_out); p.sh = residual_out_stride;
+  p.y = static_cast<uint16_t*>(norm_out); p.sy = norm_out_stride;
+  return launch_fwd<IN_GATED_BIAS, EPI_LN_MOD_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_fused_dit_residual_layernorm_scale_shift(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* scale, int64_t scale_stride, float scale_bias, const void* shift,
+    int64_t shift_stride, float shift_bias, int64_t rows, int64_t hidden, float eps,
+    dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(scale, scale_stride, hidden, 2, "scale"));
+  DN_CHECK(check_matrix(shift, shift_stride, hidden, 2, "shift"));
+  DN_CHECK(check_matrix(norm_out, norm_out_stride, hidden, 2, "norm_out"));
+  if (residual) {
+    DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+    if (residual_out)
+      DN_CHECK(check_matrix(residual_out, residual_out_stride, hidden, 2, "residual_out"));
+  } else if (residual_out) {
+    return fail(DN_ERR_UNSUPPORTED, "residual_out needs a residual (pass NULL for both)");
+  }
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.msc = static_cast<const uint16_t*>(scale); p.smsc = scale_stride;
+  p.msh = static_cast<const uint16_t*>(shift); p.smsh = shift_stride;
+  p.scale_bias = scale_bias; p.shift_bias = shift_bias;
+  p.y = static_cast<uint16_t*>(norm_out); p.sy = norm_out_stride;
+  if (!residual)
+    return launch_fwd<IN_PLAIN, EPI_LN_MOD_BF16>(p, static_cast<hipStream_t>(stream));
+  p.r = static_cast<const uint16_t*>(residual); p.sr = residual_stride;
+  p.h = static_cast<uint16_t*>(residual_out); p.sh = residual_out_stride;
+  return launch_fwd<IN_ADD, EPI_LN_MOD_BF16>(p, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

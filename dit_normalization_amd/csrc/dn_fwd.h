@@ -1,10 +1,15 @@
-// Forward row engine of the RMSNorm family for gfx950.
+// Forward row engine of the RMSNorm and LayerNorm families for gfx950.
 //
 // One template covers every forward variant; two compile-time kinds select what a row
 // reads and what its epilogue writes:
-//   input  : x | x + residual (fused add) | FMA(x, gate, residual) (gated residual)
-//   output : BF16 y | FP8 at a static scale | FP8 with 1x128 block scales |
+//   input  : x | x + residual (fused add) | FMA(x, gate, residual) (gated residual) |
+//            FMA(x, gate + gate_bias, residual) (DiT gated residual)
+//   output : RMSNorm: BF16 y | FP8 at a static scale | FP8 with 1x128 block scales |
 //            AdaRMSNorm (style scale/shift, gate copy) in BF16 or FP8
+//            LayerNorm: BF16 or static FP8 of n*gamma + beta | BF16 of the DiT modulation
+//            n*(1 + scale + scale_bias) + (shift + shift_bias)
+// The LayerNorm epilogues also switch the row statistics from the sum of squares to the
+// FP64 pair (sum, sum of squares), from which mean and variance follow in one pass.
 //
 // Row mapping (chosen on the host by hidden size): a row is owned by a group of TPR
 // threads.  Thread `lane` of the group owns the 16-byte column vectors lane, lane+TPR,
@@ -19,25 +24,43 @@
 // range check zero-fills ragged tails and drops their stores.
 //
 // Blocks are persistent: the grid is sized to the resident capacity of the chip and each
-// block walks row groups with a grid stride.  The effective weight FP32(w + bias) is staged
-// once per block into LDS (two planes of float4, so lanes read consecutive 16-byte words:
-// conflict-free ds_read_b128) and read from there for every row.
+// block walks row groups with a grid stride.  Per-column parameters (the effective RMSNorm
+// weight FP32(w + bias), or LayerNorm's gamma and beta) are staged once per block into
+// LDS as planes of float4, so lanes read consecutive 16-byte words (conflict-free
+// ds_read_b128), and read from there for every row.
 #pragma once
 
 #include "dn_device.h"
 
 namespace dn {
 
-enum InKind { IN_PLAIN = 0, IN_ADD = 1, IN_GATED = 2 };
-enum EpiKind { EPI_BF16 = 0, EPI_FP8 = 1, EPI_FP8_BLOCK = 2, EPI_ADA_BF16 = 3, EPI_ADA_FP8 = 4 };
+enum InKind { IN_PLAIN = 0, IN_ADD = 1, IN_GATED = 2, IN_GATED_BIAS = 3 };
+enum EpiKind {
+  EPI_BF16 = 0, EPI_FP8 = 1, EPI_FP8_BLOCK = 2, EPI_ADA_BF16 = 3, EPI_ADA_FP8 = 4,
+  EPI_LN_BF16 = 5, EPI_LN_FP8 = 6, EPI_LN_MOD_BF16 = 7
+};
+
+constexpr bool epi_is_ln(int epi) { return epi >= EPI_LN_BF16; }
+constexpr bool in_is_gated(int in) { return in == IN_GATED || in == IN_GATED_BIAS; }
+// FP32 planes (16 bytes per column vector each) of per-column parameters staged in LDS:
+// the RMSNorm effective weight (2), LayerNorm gamma and beta (4), none for the modulation.
+constexpr int fwd_weight_planes(int epi) {
+  return epi == EPI_LN_MOD_BF16 ? 0 : (epi_is_ln(epi) ? 4 : 2);
+}
+// FP64 statistics a row reduces: sum of squares, plus the sum for LayerNorm.
+constexpr int fwd_stats(int epi) { return epi_is_ln(epi) ? 2 : 1; }
 
 struct FwdParams {
   const uint16_t* x;     int64_t sx;
-  const uint16_t* r;     int64_t sr;     // residual (IN_ADD, IN_GATED)
-  const uint16_t* gate;  int64_t sg;     // IN_GATED
+  const uint16_t* r;     int64_t sr;     // residual (IN_ADD, gated inputs)
+  const uint16_t* gate;  int64_t sg;     // gated inputs
   const uint16_t* style; int64_t sst;    // Ada: [style_rows, 3*hidden]
   int style_bcast;                       // Ada: one style row for every token
-  const void* w;         int w_f32;      float w_bias;
+  const void* w;         int w_f32;      float w_bias;   // LayerNorm: w = gamma (FP32)
+  const float* beta;                     // LayerNorm beta (FP32 [hidden])
+  const uint16_t* msc;   int64_t smsc;   // DiT modulation scale rows (BF16)
+  const uint16_t* msh;   int64_t smsh;   // DiT modulation shift rows (BF16)
+  float gate_bias, scale_bias, shift_bias;
   const float* scale;                    // FP8 static: device FP32 [1]
   uint16_t* y;           int64_t sy;     // BF16 output (y, normed_out, Ada out); nullable
   uint16_t* h;           int64_t sh;     // h_new output; nullable
@@ -49,7 +72,7 @@ struct FwdParams {
   int hidden;
   int nvec;                              // hidden / 8
   float eps;
-  int w_in_lds;                          // effective weight staged in LDS
+  int w_in_lds;                          // per-column parameters staged in LDS
 };
 
 // Effective weight FP32(w + bias) of one 16-byte column vector, read from global memory.
@@ -66,9 +89,24 @@ __device__ __forceinline__ void load_weff8(const FwdParams& p, int vec, float e[
   for (int k = 0; k < 8; ++k) e[k] += p.w_bias;
 }
 
-// Bytes of dynamic LDS a forward launch needs.
-__host__ __device__ inline size_t fwd_lds_bytes(int nvec, int w_in_lds, int g, int wpr, int r) {
-  return (w_in_lds ? (size_t)32 * nvec : 0) + (size_t)2 * g * wpr * r * sizeof(double);
+// LayerNorm gamma and beta of one 16-byte column vector, read from global memory.
+__device__ __forceinline__ void load_affine8(const FwdParams& p, int vec, float ga[8],
+                                             float be[8]) {
+  const float4* g = reinterpret_cast<const float4*>(p.w) + 2 * vec;
+  const float4* b = reinterpret_cast<const float4*>(p.beta) + 2 * vec;
+  const float4 g0 = g[0], g1 = g[1], b0 = b[0], b1 = b[1];
+  ga[0] = g0.x; ga[1] = g0.y; ga[2] = g0.z; ga[3] = g0.w;
+  ga[4] = g1.x; ga[5] = g1.y; ga[6] = g1.z; ga[7] = g1.w;
+  be[0] = b0.x; be[1] = b0.y; be[2] = b0.z; be[3] = b0.w;
+  be[4] = b1.x; be[5] = b1.y; be[6] = b1.z; be[7] = b1.w;
+}
+
+// Bytes of dynamic LDS a forward launch needs: `planes` FP32 planes of per-column
+// parameters (0 when they are read from global memory) and double-buffered reduction
+// slots of `stats` doubles per wave and row slot.
+__host__ __device__ inline size_t fwd_lds_bytes(int nvec, int planes, int g, int wpr, int r,
+                                                int stats) {
+  return (size_t)16 * planes * nvec + (size_t)2 * g * wpr * r * stats * sizeof(double);
 }
 
 // The data one step of the forward loads: R row slots of VMAX vectors per tensor.
@@ -91,8 +129,9 @@ constexpr bool fwd_double_buffer(int in, int epi, int vmax, int r, int nt) {
 #ifndef DN_FWD_PREFETCH
   return false;
 #endif
-  const int tensors = 1 + (in != IN_PLAIN) + (in == IN_GATED) +
-                      3 * (epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8);
+  const int tensors = 1 + (in != IN_PLAIN) + in_is_gated(in) +
+                      3 * (epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8) +
+                      2 * (epi == EPI_LN_MOD_BF16);
   const int step = tensors * 4 * vmax * r;
   const int budget = nt >= 1024 ? 128 : 256;
   return 2 * step + 96 <= budget;
@@ -108,8 +147,14 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   constexpr int RPW = Geom::RPW;
   constexpr int RW = TPR < 64 ? TPR : 64;        // lanes of a row inside one wave
   constexpr bool kAda = (EPI == EPI_ADA_BF16 || EPI == EPI_ADA_FP8);
-  constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8);
-  constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8);
+  constexpr bool kLN = epi_is_ln(EPI);
+  constexpr bool kMod = (EPI == EPI_LN_MOD_BF16);
+  constexpr bool kGatedIn = in_is_gated(IN);
+  constexpr int kPlanes = fwd_weight_planes(EPI);
+  constexpr int kStats = fwd_stats(EPI);
+  constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8 || EPI == EPI_LN_FP8);
+  constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8 ||
+                            EPI == EPI_LN_FP8);
   constexpr bool kDB = fwd_double_buffer(IN, EPI, VMAX, R, NT);
 
   const Geom geo;
@@ -121,14 +166,23 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   // Sub-wave rows: lanes past the row's last vector take an out-of-range offset.
   const bool lane_ok = TPR >= 64 || lane < nvec;
   float4* wl = reinterpret_cast<float4*>(dn_lds);
-  double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)32 * nvec : 0));
+  double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)16 * kPlanes * nvec : 0));
 
-  if (p.w_in_lds) {
+  if (kPlanes > 0 && p.w_in_lds) {
     for (int i = tid; i < nvec; i += NT) {
-      float e[8];
-      load_weff8(p, i, e);
-      wl[i] = make_float4(e[0], e[1], e[2], e[3]);
-      wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
+      if constexpr (kLN) {
+        float ga[8], be[8];
+        load_affine8(p, i, ga, be);
+        wl[i] = make_float4(ga[0], ga[1], ga[2], ga[3]);
+        wl[nvec + i] = make_float4(ga[4], ga[5], ga[6], ga[7]);
+        wl[2 * nvec + i] = make_float4(be[0], be[1], be[2], be[3]);
+        wl[3 * nvec + i] = make_float4(be[4], be[5], be[6], be[7]);
+      } else {
+        float e[8];
+        load_weff8(p, i, e);
+        wl[i] = make_float4(e[0], e[1], e[2], e[3]);
+        wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
+      }
     }
     __syncthreads();
   }
@@ -158,16 +212,22 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
       st.row[rr] = geo.row(first, rr);
       st.rok[rr] = st.row[rr] < p.rows;
     }
-    rsrc_t rx[R], rres[R], rg[R], rst[R];
-    uint32_t ox[R], ores[R], og[R], ost[R];
+    rsrc_t rx[R], rres[R], rg[R], rst[R], rsc[R], rsh[R];
+    uint32_t ox[R], ores[R], og[R], ost[R], osc[R], osh[R];
     tensor_span<TPR, R, RPW>(p.x, p.sx, 2, 16, row_bf16, first, p.rows, lane, geo.j, lane_ok,
                              rx, ox);
     if constexpr (IN != IN_PLAIN)
       tensor_span<TPR, R, RPW>(p.r, p.sr, 2, 16, row_bf16, first, p.rows, lane, geo.j,
                                lane_ok, rres, ores);
-    if constexpr (IN == IN_GATED)
+    if constexpr (kGatedIn)
       tensor_span<TPR, R, RPW>(p.gate, p.sg, 2, 16, row_bf16, first, p.rows, lane, geo.j,
                                lane_ok, rg, og);
+    if constexpr (kMod) {
+      tensor_span<TPR, R, RPW>(p.msc, p.smsc, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                               lane_ok, rsc, osc);
+      tensor_span<TPR, R, RPW>(p.msh, p.smsh, 2, 16, row_bf16, first, p.rows, lane, geo.j,
+                               lane_ok, rsh, osh);
+    }
     if constexpr (kAda) {
       if (p.style_bcast) {
         // Every row reads the single style row.
@@ -188,7 +248,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const uint32_t dv = (uint32_t)(v * TPR * 16);
         st.a[rr][v] = bload16(rx[rr], ox[rr] + dv);
         if constexpr (IN != IN_PLAIN) st.b[rr][v] = bload16(rres[rr], ores[rr] + dv);
-        if constexpr (IN == IN_GATED) st.c[rr][v] = bload16(rg[rr], og[rr] + dv);
+        if constexpr (kGatedIn) st.c[rr][v] = bload16(rg[rr], og[rr] + dv);
+        if constexpr (kMod) {
+          st.ssc[rr][v] = bload16(rsc[rr], osc[rr] + dv);
+          st.ssh[rr][v] = bload16(rsh[rr], osh[rr] + dv);
+        }
         if constexpr (kAda) {
           if (p.style_bcast) {     // one style row serves every token: keep it cached
             st.ssc[rr][v] = bload16_keep(rst[rr], ost[rr] + dv);
@@ -207,7 +271,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   auto process = [&](Step& st, int64_t base) {
     const int64_t first = geo.first(base);
     // 2) h (rounded to BF16, stored early) and per-lane sums of squares of that BF16 h.
-    double ss[R];
+    double ss[R], s1[R];
     {
       rsrc_t rh[R];
       uint32_t oh[R];
@@ -217,6 +281,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         ss[rr] = 0.0;
+        s1[rr] = 0.0;
 #pragma unroll
         for (int v = 0; v < VMAX; ++v) {
           float fh[8];
@@ -232,6 +297,12 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
             unpack8(st.c[rr][v], fg);
 #pragma unroll
             for (int k = 0; k < 8; ++k) fh[k] = fmaf(fh[k], fg[k], fr[k]);
+          } else if constexpr (IN == IN_GATED_BIAS) {
+            float fr[8], fg[8];
+            unpack8(st.b[rr][v], fr);
+            unpack8(st.c[rr][v], fg);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) fh[k] = fmaf(fh[k], fg[k] + p.gate_bias, fr[k]);
           }
           if constexpr (IN != IN_PLAIN) {
             st.a[rr][v] = pack8(fh);
@@ -241,7 +312,18 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #endif
           }
           // Lanes past the row end loaded zeros: they add nothing.
-          ss[rr] += (double)sumsq8(fh);
+          if constexpr (kLN) {
+            // Exact FP64 terms: the sum and the sum of squares of a BF16 row carry no
+            // rounding worth the name, so the one-pass variance stays accurate.
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const double d = (double)fh[k];
+              s1[rr] += d;
+              ss[rr] = fma(d, d, ss[rr]);
+            }
+          } else {
+            ss[rr] += (double)sumsq8(fh);
+          }
         }
       }
     }
@@ -252,30 +334,50 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int v = 0; v < VMAX; ++v) keep_packed(st.a[rr][v]);
       ss[rr] = group_sum<RW>(ss[rr]);
+      if constexpr (kLN) s1[rr] = group_sum<RW>(s1[rr]);
     }
     if constexpr (WPR > 1) {
       const int wave_in_row = lane >> 6;
-      double* slot = red + (size_t)parity * G * WPR * R + (size_t)geo.grp * WPR * R;
+      double* slot = red + ((size_t)parity * G * WPR * R + (size_t)geo.grp * WPR * R) * kStats;
       if ((lane & 63) == 0) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) slot[wave_in_row * R + rr] = ss[rr];
+        for (int rr = 0; rr < R; ++rr) {
+          slot[(wave_in_row * R + rr) * kStats] = ss[rr];
+          if constexpr (kLN) slot[(wave_in_row * R + rr) * kStats + 1] = s1[rr];
+        }
       }
       __syncthreads();
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        double s = 0.0;
+        double s = 0.0, t = 0.0;
 #pragma unroll
-        for (int w8 = 0; w8 < WPR; ++w8) s += slot[w8 * R + rr];
+        for (int w8 = 0; w8 < WPR; ++w8) {
+          s += slot[(w8 * R + rr) * kStats];
+          if constexpr (kLN) t += slot[(w8 * R + rr) * kStats + 1];
+        }
         ss[rr] = s;
+        s1[rr] = t;
       }
       parity ^= 1;
     }
 
-    // 4) rstd = 1/sqrt(mean + eps): IEEE FP64 divide and square root, one FP32 rounding.
-    float rs[R];
+    // 4) RMSNorm: rstd = 1/sqrt(mean square + eps).  LayerNorm: mean = sum/H, variance =
+    //    (sum of squares)/H - mean^2 (population variance), rstd = 1/sqrt(var + eps).
+    //    IEEE FP64 divide and square root, one FP32 rounding of each result.
+    float rs[R], mu[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      const double r64 = 1.0 / sqrt(ss[rr] * inv_hidden + eps);
+      double r64;
+      if constexpr (kLN) {
+        const double mean = s1[rr] / (double)p.hidden;
+        double var = ss[rr] / (double)p.hidden - mean * mean;
+        var = var > 0.0 ? var : 0.0;
+        r64 = 1.0 / sqrt(var + eps);
+        mu[rr] = (float)mean;
+      } else {
+        r64 = 1.0 / sqrt(ss[rr] * inv_hidden + eps);
+        mu[rr] = 0.0f;
+      }
       rs[rr] = (float)r64;
       if (p.rstd && lane == 0 && st.rok[rr]) p.rstd[st.row[rr]] = rs[rr];
     }
@@ -283,7 +385,8 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     // 5) Epilogue: y = (h * r) * w_eff in FP32, then the output format.
     rsrc_t ry[R], rq[R], rgo[R];
     uint32_t oy[R], oq[R], ogo[R];
-    if constexpr (EPI == EPI_BF16 || EPI == EPI_ADA_BF16 || EPI == EPI_FP8_BLOCK)
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_ADA_BF16 || EPI == EPI_FP8_BLOCK ||
+                  EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16)
       tensor_span<TPR, R, RPW>(p.y, p.sy, 2, 16, p.y ? row_bf16 : 0u, first,
                                p.y ? p.rows : first, lane, geo.j, lane_ok, ry, oy);
     if constexpr (kFp8Out)
@@ -299,7 +402,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         // Keep the scheduler from hoisting every vector's weight reads to the top.
         __builtin_amdgcn_sched_barrier(0);
         const int idx = v * TPR + lane;
-        const int widx = idx < nvec ? idx : nvec - 1;   // ragged lanes read a valid weight
+        int widx = idx < nvec ? idx : nvec - 1;   // ragged lanes read a valid weight
+        // The per-column parameters are the same for every row, so the compiler would keep
+        // them in VGPRs across the row loop.  LayerNorm's gamma and beta take 8 VGPRs per
+        // vector: 1024-thread blocks (128 VGPRs a lane) re-read them from LDS instead.
+        if constexpr (kLN && NT >= 1024) asm volatile("" : "+v"(widx));
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
@@ -313,19 +420,49 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         }
 #endif
         unpack8(st.a[rr][v], fh);
-        if (p.w_in_lds) {
-          const float4 lo = wl[widx], hi = wl[nvec + widx];
-          we[0] = lo.x; we[1] = lo.y; we[2] = lo.z; we[3] = lo.w;
-          we[4] = hi.x; we[5] = hi.y; we[6] = hi.z; we[7] = hi.w;
-        } else {
-          load_weff8(p, widx, we);
-        }
+        if constexpr (kLN) {
+          // n = (h - mean) * rstd in FP32, then one FMA with gamma and beta (or with the
+          // modulation's 1 + scale + scale_bias and shift + shift_bias).
+          float nv[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
+          for (int k = 0; k < 8; ++k) nv[k] = (fh[k] - mu[rr]) * rs[rr];
+          if constexpr (kMod) {
+            float fsc[8], fsh[8];
+            unpack8(st.ssc[rr][v], fsc);
+            unpack8(st.ssh[rr][v], fsh);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              yv[k] = fmaf(nv[k], (1.0f + fsc[k]) + p.scale_bias, fsh[k] + p.shift_bias);
+          } else {
+            float be[8];
+            if (p.w_in_lds) {
+              const float4 g0 = wl[widx], g1 = wl[nvec + widx];
+              const float4 b0 = wl[2 * nvec + widx], b1 = wl[3 * nvec + widx];
+              we[0] = g0.x; we[1] = g0.y; we[2] = g0.z; we[3] = g0.w;
+              we[4] = g1.x; we[5] = g1.y; we[6] = g1.z; we[7] = g1.w;
+              be[0] = b0.x; be[1] = b0.y; be[2] = b0.z; be[3] = b0.w;
+              be[4] = b1.x; be[5] = b1.y; be[6] = b1.z; be[7] = b1.w;
+            } else {
+              load_affine8(p, widx, we, be);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) yv[k] = fmaf(nv[k], we[k], be[k]);
+          }
+        } else {
+          if (p.w_in_lds) {
+            const float4 lo = wl[widx], hi = wl[nvec + widx];
+            we[0] = lo.x; we[1] = lo.y; we[2] = lo.z; we[3] = lo.w;
+            we[4] = hi.x; we[5] = hi.y; we[6] = hi.z; we[7] = hi.w;
+          } else {
+            load_weff8(p, widx, we);
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
+        }
 
-        if constexpr (EPI == EPI_BF16) {
+        if constexpr (EPI == EPI_BF16 || EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16) {
           bstore16(ry[rr], oy[rr] + d16, pack8(yv));
-        } else if constexpr (EPI == EPI_FP8) {
+        } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
           bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(yv));
@@ -412,10 +549,12 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 constexpr int kFwdTierCount = 18;
 constexpr int kFwdAutoTiers = 11;   // tiers the automatic choice considers
 
-// Largest VMAX an input/epilogue combination is built with: the Ada and gated routes
-// keep up to six 16-byte vectors per column in flight, so they stop at 6.
+// Largest VMAX an input/epilogue combination is built with: the Ada, gated and
+// modulation routes keep five or six 16-byte vectors per column in flight, so they stop
+// at 6.
 constexpr int fwd_vmax_limit(int in, int epi) {
-  return (in == IN_GATED || epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8) ? 6 : 16;
+  return (in_is_gated(in) || epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8 ||
+          epi == EPI_LN_MOD_BF16) ? 6 : 16;
 }
 
 }  // namespace dn

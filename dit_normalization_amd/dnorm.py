@@ -54,6 +54,17 @@ SIGNATURES = {
         [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
         _I32),
     "dn_train_backward_reduce": ([_P, _P, _SZ, _I64, _I64, _P], _I32),
+    "dn_layernorm": ([_P, _I64, _P, _I64, _P, _P, _I64, _I64, _F32, _P], _I32),
+    "dn_layernorm_quant": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _F32, _P], _I32),
+    "dn_fused_dit_gate_residual_layernorm_gamma_beta": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P, _P, _I64, _I64, _F32, _P],
+        _I32),
+    "dn_fused_dit_gate_residual_layernorm_scale_shift": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P, _I64, _F32, _P, _I64, _F32,
+         _I64, _I64, _F32, _P], _I32),
+    "dn_fused_dit_residual_layernorm_scale_shift": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P, _I64, _F32, _I64, _I64, _F32,
+         _P], _I32),
 }
 
 
@@ -376,6 +387,123 @@ def dn_train_backward_reduce(workspace, rows: int, hidden: int, *, dw=None):
                                         workspace.numel() * workspace.element_size(), rows, hidden,
                                         _stream(workspace)), "dn_train_backward_reduce")
     return dw
+
+
+def _affine(t: torch.Tensor, name: str):
+    """LayerNorm gamma / beta: FP32 [hidden], contiguous and 16-byte aligned."""
+    if t.dtype != torch.float32:
+        raise DnormError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_contiguous() or t.data_ptr() % 16 != 0:
+        t = t.contiguous().clone()
+    return t
+
+
+def dn_layernorm(x, gamma, beta, eps: float = 1e-6, *, out=None):
+    """y = BF16(LayerNorm(x) * gamma + beta) per row (population variance)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
+    y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
+    yr, _, sy = _rows(y, "out")
+    _check(lib.dn_layernorm(yr.data_ptr(), sy, xr.data_ptr(), sx, g.data_ptr(), b.data_ptr(), rows,
+                            H, eps, _stream(x)), "dn_layernorm")
+    _writeback(y, yr)
+    return y
+
+
+def dn_layernorm_quant(x, gamma, beta, scale, eps: float = 1e-6, *, out=None):
+    """out = e4m3fn((LayerNorm(x) * gamma + beta) / scale)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
+    q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    s = _scale_tensor(scale, x.device)
+    _check(lib.dn_layernorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, g.data_ptr(), b.data_ptr(),
+                                  s.data_ptr(), rows, H, eps, _stream(x)), "dn_layernorm_quant")
+    _writeback(q, qr)
+    return q
+
+
+def _dit_outputs(x, residual_out, norm_out, want_residual_out: bool):
+    n = norm_out if norm_out is not None else _out_like(x, x.shape, torch.bfloat16)
+    nr, _, sn = _rows(n, "norm_out")
+    ro, ror, sro = None, None, 0
+    if want_residual_out:
+        ro = residual_out if residual_out is not None else _out_like(x, x.shape, torch.bfloat16)
+        ror, _, sro = _rows(ro, "residual_out")
+    return n, nr, sn, ro, ror, sro
+
+
+def dn_fused_dit_gate_residual_layernorm_gamma_beta(x, residual, gate, gamma, beta,
+                                                    eps: float = 1e-6, *, gate_bias: float = 0.0,
+                                                    residual_out=None, norm_out=None):
+    """residual_out = BF16(residual + x*(gate + gate_bias)); norm_out = BF16(LayerNorm(
+    residual_out) * gamma + beta).  Returns (residual_out, norm_out); gate may be a strided
+    per-token chunk view (row stride 6*hidden)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    rr, _, sr = _rows(residual, "residual")
+    gt, _, sg = _rows(gate, "gate")
+    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True)
+    _check(lib.dn_fused_dit_gate_residual_layernorm_gamma_beta(
+        ror.data_ptr(), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, rr.data_ptr(), sr,
+        gt.data_ptr(), sg, gate_bias, g.data_ptr(), b.data_ptr(), rows, H, eps, _stream(x)),
+        "dn_fused_dit_gate_residual_layernorm_gamma_beta")
+    _writeback(ro, ror)
+    _writeback(n, nr)
+    return ro, n
+
+
+def dn_fused_dit_gate_residual_layernorm_scale_shift(x, residual, gate, scale, shift,
+                                                     eps: float = 1e-6, *, gate_bias: float = 0.0,
+                                                     scale_bias: float = 0.0,
+                                                     shift_bias: float = 0.0, residual_out=None,
+                                                     norm_out=None):
+    """residual_out = BF16(residual + x*(gate + gate_bias)); norm_out = BF16(LayerNorm(
+    residual_out) * (1 + scale + scale_bias) + (shift + shift_bias)).  Returns
+    (residual_out, norm_out)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    rr, _, sr = _rows(residual, "residual")
+    gt, _, sg = _rows(gate, "gate")
+    sc, _, ssc = _rows(scale, "scale")
+    sh, _, ssh = _rows(shift, "shift")
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True)
+    _check(lib.dn_fused_dit_gate_residual_layernorm_scale_shift(
+        ror.data_ptr(), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, rr.data_ptr(), sr,
+        gt.data_ptr(), sg, gate_bias, sc.data_ptr(), ssc, scale_bias, sh.data_ptr(), ssh,
+        shift_bias, rows, H, eps, _stream(x)),
+        "dn_fused_dit_gate_residual_layernorm_scale_shift")
+    _writeback(ro, ror)
+    _writeback(n, nr)
+    return ro, n
+
+
+def dn_fused_dit_residual_layernorm_scale_shift(x, scale, shift, residual=None,
+                                                eps: float = 1e-6, *, scale_bias: float = 0.0,
+                                                shift_bias: float = 0.0, residual_out=None,
+                                                norm_out=None):
+    """h = BF16(x + residual) (x alone without a residual); norm_out = BF16(LayerNorm(h) *
+    (1 + scale + scale_bias) + (shift + shift_bias)).  Returns (residual_out, norm_out),
+    residual_out None without a residual."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    sc, _, ssc = _rows(scale, "scale")
+    sh, _, ssh = _rows(shift, "shift")
+    rr, sr = None, 0
+    if residual is not None:
+        rr, _, sr = _rows(residual, "residual")
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, residual is not None)
+    _check(lib.dn_fused_dit_residual_layernorm_scale_shift(
+        _ptr(ror), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, _ptr(rr), sr, sc.data_ptr(), ssc,
+        scale_bias, sh.data_ptr(), ssh, shift_bias, rows, H, eps, _stream(x)),
+        "dn_fused_dit_residual_layernorm_scale_shift")
+    if ro is not None:
+        _writeback(ro, ror)
+    _writeback(n, nr)
+    return ro, n
 
 
 def dn_force_threads_per_row(threads: int):

@@ -1,10 +1,16 @@
 /*
- * dnorm.h -- C ABI of the row-wise RMSNorm family on AMD Instinct MI355X (gfx950).
+ * dnorm.h -- C ABI of the row-wise RMSNorm and LayerNorm families on AMD Instinct MI355X
+ * (gfx950).
  *
- * Every operation normalises rows of a [rows, hidden] matrix independently:
+ * Every operation normalises rows of a [rows, hidden] matrix independently.  RMSNorm:
  *
  *     r_t  = 1 / sqrt(mean_j h_tj^2 + eps)        (FP32 statistics, eps an FP32 number)
  *     y_tj = BF16((h_tj * r_t) * w_eff_j),  w_eff_j = FP32(w_j + w_bias)
+ *
+ * LayerNorm (population variance over the row):
+ *
+ *     m_t  = mean_j h_tj,  r_t = 1 / sqrt(mean_j (h_tj - m_t)^2 + eps)
+ *     n_tj = (h_tj - m_t) * r_t,  y_tj = n_tj * gamma_j + beta_j
  *
  * Pages cited (by title and section):
  *   [norm docs]   "flashinfer.norm" API reference: the API table and the section
@@ -234,6 +240,72 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride,
 
 dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes,
                                    int64_t rows, int64_t hidden, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * LayerNorm family   ([norm docs] API table: layernorm, layernorm_quant and the three
+ *                     fused_dit_* calls; [norm guide] §4, §5.3)
+ *
+ * Statistics: the row's sum and sum of squares are accumulated in FP64 from the BF16
+ * values (exactly converted), mean = sum/hidden and variance = sum of squares/hidden -
+ * mean^2 in FP64 (clamped at 0), r = 1/sqrt(variance + eps) in FP64; mean and r are then
+ * rounded once to FP32 and n = (h - mean) * r is evaluated in FP32.
+ *
+ * layernorm:        y = BF16(FMA(n, gamma, beta)).
+ * layernorm_quant:  out = e4m3fn(FMA(n, gamma, beta) / scale); scale: device FP32 [1]
+ *                   (applied as a multiplication by its FP32 reciprocal).
+ *   x: BF16 [rows, hidden]; gamma, beta: FP32 [hidden], 16-byte aligned, required.
+ */
+dn_status dn_layernorm(void* y, int64_t y_stride, const void* x, int64_t x_stride,
+                       const float* gamma, const float* beta,
+                       int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+dn_status dn_layernorm_quant(uint8_t* out, int64_t out_stride,
+                             const void* x, int64_t x_stride,
+                             const float* gamma, const float* beta, const float* scale,
+                             int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* DiT gate/residual + LayerNorm, the three modes of [norm guide] §5.3 (BF16 outputs):
+ *
+ *   gate_residual + gamma/beta:
+ *     residual_out = BF16(FP32-FMA(x, FP32(gate + gate_bias), residual))
+ *     norm_out     = BF16(FMA(n(residual_out), gamma, beta))
+ *   gate_residual + scale/shift:
+ *     residual_out as above;
+ *     norm_out = BF16(FMA(n(residual_out), FP32(FP32(1 + scale) + scale_bias),
+ *                         FP32(shift + shift_bias)))
+ *   residual + scale/shift:
+ *     h = BF16(x + residual) (written to residual_out when given), or h = x when
+ *     residual is NULL (residual_out must then be NULL too); norm_out as in the
+ *     scale/shift mode with n(h).
+ *
+ *   x, residual: BF16 [rows, hidden].  gate, scale, shift: BF16 [rows, hidden] with their
+ *   own row strides, so the per-token chunks of one modulation tensor (row stride
+ *   6*hidden, [norm guide] §5.3) are passed without a copy.  gate_bias, scale_bias and
+ *   shift_bias are FP32 scalars.  residual_out is optional (NULL: not written) and may be
+ *   residual itself (in place); norm_out is required.  Any hidden that is a multiple of 8
+ *   is accepted (the pages' DiT model uses 3072).
+ */
+dn_status dn_fused_dit_gate_residual_layernorm_gamma_beta(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* gate, int64_t gate_stride, float gate_bias,
+    const float* gamma, const float* beta,
+    int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+dn_status dn_fused_dit_gate_residual_layernorm_scale_shift(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* gate, int64_t gate_stride, float gate_bias,
+    const void* scale, int64_t scale_stride, float scale_bias,
+    const void* shift, int64_t shift_stride, float shift_bias,
+    int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+dn_status dn_fused_dit_residual_layernorm_scale_shift(
+    void* residual_out, int64_t residual_out_stride, void* norm_out, int64_t norm_out_stride,
+    const void* x, int64_t x_stride, const void* residual, int64_t residual_stride,
+    const void* scale, int64_t scale_stride, float scale_bias,
+    const void* shift, int64_t shift_stride, float shift_bias,
+    int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Test and tuning hook: force the threads that share one row (8, 16, 32, 64, 128, 256,

@@ -44,7 +44,10 @@ def test_header_declares_the_expected_calls():
               "dn_fused_add_rmsnorm_fp8_block_quant", "dn_ada_rms_norm",
               "dn_gate_residual_ada_norm_fp8", "dn_train_forward", "dn_train_backward",
               "dn_train_backward_workspace_bytes", "dn_train_backward_partials",
-              "dn_train_backward_reduce", "dn_last_error"]:
+              "dn_train_backward_reduce", "dn_layernorm", "dn_layernorm_quant",
+              "dn_fused_dit_gate_residual_layernorm_gamma_beta",
+              "dn_fused_dit_gate_residual_layernorm_scale_shift",
+              "dn_fused_dit_residual_layernorm_scale_shift", "dn_last_error"]:
         assert n in names
 
 
@@ -161,6 +164,41 @@ def test_train_checks(lib):
     r = lib.dn_train_backward_reduce
     assert r(A, B, ws, 0, 8192, None) == OK
     assert r(A, B, ws // 2, 5, 8192, None) == E_WS
+
+
+def test_layernorm_checks(lib):
+    ln = lib.dn_layernorm
+    assert ln(A, 3072, B, 3072, C, D, 0, 3072, 1e-6, None) == OK
+    assert ln(A, 3072, B, 3072, 0, D, 4, 3072, 1e-6, None) == E_NULL          # gamma
+    assert b"gamma" in lib.dn_last_error()
+    assert ln(A, 3072, B, 3072, C, 0, 4, 3072, 1e-6, None) == E_NULL          # beta
+    assert ln(A, 3072, B, 3072, C + 4, D, 4, 3072, 1e-6, None) == E_ALIGN     # gamma alignment
+    assert ln(A, 3072, B, 3064, C, D, 4, 3072, 1e-6, None) == E_SHAPE         # stride < hidden
+    lq = lib.dn_layernorm_quant
+    assert lq(A, 3072, B, 3072, C, D, E, 0, 3072, 1e-6, None) == OK
+    assert lq(A, 3072, B, 3072, C, D, 0, 4, 3072, 1e-6, None) == E_NULL       # scale
+
+
+def test_dit_checks(lib):
+    gb = lib.dn_fused_dit_gate_residual_layernorm_gamma_beta
+    # gate as a chunk of a [rows, 6*hidden] modulation tensor: row stride 18432
+    assert gb(0, 0, A, 3072, B, 3072, C, 3072, D, 18432, 0.0, E, A, 0, 3072, 1e-6, None) == OK
+    assert gb(0, 0, A, 3072, B, 3072, C, 3072, 0, 18432, 0.0, E, A, 4, 3072, 1e-6, None) == E_NULL
+    assert gb(0, 0, 0, 3072, B, 3072, C, 3072, D, 18432, 0.0, E, A, 4, 3072, 1e-6, None) == E_NULL
+    assert gb(0, 0, A, 3072, B, 3072, C, 3072, D, 18436, 0.0, E, A, 4, 3072, 1e-6,
+              None) == E_ALIGN                                   # gate stride not 8-aligned
+    ss = lib.dn_fused_dit_gate_residual_layernorm_scale_shift
+    assert ss(A, 3072, B, 3072, C, 3072, D, 3072, E, 18432, 0.0, A, 18432, 0.0, B, 18432, 0.0,
+              0, 3072, 1e-6, None) == OK
+    assert ss(A, 3072, B, 3072, C, 3072, D, 3072, E, 18432, 0.0, 0, 18432, 0.0, B, 18432, 0.0,
+              4, 3072, 1e-6, None) == E_NULL                     # scale
+    rs = lib.dn_fused_dit_residual_layernorm_scale_shift
+    assert rs(0, 0, A, 3072, B, 3072, 0, 0, C, 18432, 0.0, D, 18432, 0.0, 0, 3072, 1e-6,
+              None) == OK
+    assert rs(E, 3072, A, 3072, B, 3072, 0, 0, C, 18432, 0.0, D, 18432, 0.0, 4, 3072, 1e-6,
+              None) == E_UNSUP                                   # residual_out without residual
+    assert rs(0, 0, A, 3072, B, 3072, 0, 0, C, 18432, 0.0, 0, 18432, 0.0, 4, 3072, 1e-6,
+              None) == E_NULL                                    # shift
 
 
 def test_force_threads_per_row(lib):

@@ -108,3 +108,37 @@ def ada(rows: int = 2520, dim: int = 3072, seed: int = 5, broadcast: bool = Fals
         "w": torch.ones((dim,), dtype=BF16),
         "style": normal((style_rows, 3 * dim), seed, 3 + (100 if broadcast else 0)),
     }, {"eps": 1e-6, "scale": 0.04, "rows": rows, "dim": dim, "broadcast": broadcast})
+
+
+# --- the LayerNorm family ---------------------------------------------------------------
+
+def layernorm(rows: int = 8192, hidden: int = 4096, seed: int = 6, mean: float = 0.5) -> Workload:
+    """LayerNorm (+ static FP8): x ~ N(mean, 1) (a non-zero mean exercises the centring);
+    FP32 gamma ~ N(1, 0.1) and beta ~ N(0, 0.1); scale 0.04."""
+    return Workload("layernorm", {
+        "x": normal((rows, hidden), seed, 0, mean=mean),
+        "gamma": normal((hidden,), seed, 1, mean=1.0, std=0.1, dtype=F32),
+        "beta": normal((hidden,), seed, 2, std=0.1, dtype=F32),
+    }, {"eps": 1e-6, "scale": 0.04, "rows": rows, "hidden": hidden})
+
+
+DIT_CHUNKS = ("shift", "scale", "gate", "shift_mlp", "scale_mlp", "gate_mlp")
+
+
+def dit(rows: int = 2520, hidden: int = 3072, seed: int = 7) -> Workload:
+    """DiT gate/residual + LayerNorm: x, residual ~ N(0,1); a per-token modulation tensor
+    temb [rows, 6*hidden] ~ N(0, 0.5) whose six chunks (shift, scale, gate, and the MLP's
+    three) are views with row stride 6*hidden; FP32 gamma ~ N(1, 0.1), beta ~ N(0, 0.1);
+    scalar biases gate 0.25, scale 0.125, shift -0.0625."""
+    temb = normal((rows, 6 * hidden), seed, 2, std=0.5)
+    t = {
+        "x": normal((rows, hidden), seed, 0),
+        "residual": normal((rows, hidden), seed, 1),
+        "temb": temb,
+        "gamma": normal((hidden,), seed, 3, mean=1.0, std=0.1, dtype=F32),
+        "beta": normal((hidden,), seed, 4, std=0.1, dtype=F32),
+    }
+    for k, name in enumerate(DIT_CHUNKS):
+        t[name] = temb[:, k * hidden:(k + 1) * hidden]
+    return Workload("dit", t, {"eps": 1e-6, "rows": rows, "hidden": hidden, "gate_bias": 0.25,
+                               "scale_bias": 0.125, "shift_bias": -0.0625})
