@@ -17,6 +17,11 @@ HIP events recorded on the stream the kernels run on.  `cpu_baseline` times the 
 oracle on a bounded sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+`--family layernorm` times the LayerNorm family instead (one line, per-kernel GB/s):
+layernorm and layernorm_quant on BF16 [8192, 4096], and the three DiT gate/residual +
+LayerNorm modes on BF16 [16384, 3072] with gate/scale/shift read as row-stride-6*hidden
+chunks of one per-token modulation tensor.
 """
 from __future__ import annotations
 
@@ -121,12 +126,121 @@ def cpu_baseline(seconds: float = 10.0):
                       f"({el:.1f} s, single-threaded numpy FP64)"}
 
 
+LN = (8192, 4096)
+DIT = (16384, 3072)
+
+
+def ln_alg_bytes():
+    """Algorithmic HBM bytes per launch of the LayerNorm family."""
+    tl, hl = LN
+    td, hd = DIT
+    el, ed = tl * hl, td * hd
+    return {
+        # read x; write y; FP32 gamma and beta
+        "layernorm": 4 * el + 8 * hl,
+        # read x; write FP8 out; gamma, beta, scale
+        "layernorm_quant": 3 * el + 8 * hl + 4,
+        # read x, residual, gate; write residual_out, norm_out; gamma, beta
+        "dit_gate_residual_layernorm_gamma_beta": 10 * ed + 8 * hd,
+        # read x, residual, gate, scale, shift; write residual_out, norm_out
+        "dit_gate_residual_layernorm_scale_shift": 14 * ed,
+        # read x, residual, scale, shift; write residual_out, norm_out
+        "dit_residual_layernorm_scale_shift": 12 * ed,
+    }
+
+
+def run_layernorm_family(a) -> int:
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating LayerNorm inputs", file=sys.stderr, flush=True)
+    lw = W.layernorm(*LN)
+    x, gam, bet = (lw.tensors[k].to(dev) for k in ("x", "gamma", "beta"))
+    y = torch.empty_like(x)
+    q = torch.empty(LN, dtype=torch.float8_e4m3fn, device=dev)
+    scale = torch.tensor([0.04], dtype=torch.float32, device=dev)
+    dw = W.dit(*DIT)
+    p = dw.params
+    td, hd = DIT
+    dx, dr = dw.tensors["x"].to(dev), dw.tensors["residual"].to(dev)
+    temb = dw.tensors["temb"].to(dev)
+    chunk = {n: temb[:, k * hd:(k + 1) * hd] for k, n in enumerate(W.DIT_CHUNKS)}
+    dg, db = dw.tensors["gamma"].to(dev), dw.tensors["beta"].to(dev)
+    ro, no = torch.empty_like(dx), torch.empty_like(dx)
+
+    calls = {
+        "layernorm": lambda: dn.dn_layernorm(x, gam, bet, 1e-6, out=y),
+        "dit_gate_residual_layernorm_gamma_beta": lambda: (
+            dn.dn_fused_dit_gate_residual_layernorm_gamma_beta(
+                dx, dr, chunk["gate"], dg, db, 1e-6, gate_bias=p["gate_bias"], residual_out=ro,
+                norm_out=no)),
+        "layernorm_quant": lambda: dn.dn_layernorm_quant(x, gam, bet, scale, 1e-6, out=q),
+        "dit_gate_residual_layernorm_scale_shift": lambda: (
+            dn.dn_fused_dit_gate_residual_layernorm_scale_shift(
+                dx, dr, chunk["gate"], chunk["scale"], chunk["shift"], 1e-6,
+                gate_bias=p["gate_bias"], scale_bias=p["scale_bias"],
+                shift_bias=p["shift_bias"], residual_out=ro, norm_out=no)),
+        "dit_residual_layernorm_scale_shift": lambda: (
+            dn.dn_fused_dit_residual_layernorm_scale_shift(
+                dx, chunk["scale"], chunk["shift"], dr, 1e-6, scale_bias=p["scale_bias"],
+                shift_bias=p["shift_bias"], residual_out=ro, norm_out=no)),
+    }
+    names = list(calls)
+    for _ in range(a.warmup):
+        for n in names:
+            calls[n]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps of the LayerNorm family", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        for j, n in enumerate(names):
+            e[j].record(stream)
+            calls[n]()
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ab = ln_alg_bytes()
+    kernels = {}
+    for j, n in enumerate(names):
+        avg = sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e-3 / len(evs)
+        gbs = ab[n] / avg / 1e9
+        kernels[n] = {"us": round(avg * 1e6, 2), "bytes": ab[n], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    step_bytes = sum(ab.values())
+    value = step_bytes / (wall / a.steps) / 1e9
+    line = {
+        "metric": "achieved HBM GB/s, LayerNorm family", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "layernorm + layernorm_quant BF16 [8192,4096]; DiT gate/residual "
+                               "+ LayerNorm (gamma/beta, scale/shift) and residual + LayerNorm "
+                               "scale/shift BF16 [16384,3072], modulation chunks of a "
+                               "[16384,18432] tensor",
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4), "step_bytes": step_bytes,
+                   "parallelism": "single GPU"},
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--family", choices=("rmsnorm", "layernorm"), default="rmsnorm",
+                    help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm family")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
@@ -144,6 +258,8 @@ def main(argv=None) -> int:
     from dit_normalization_amd import dnorm as dn
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.family == "layernorm":
+        return run_layernorm_family(a)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)

@@ -101,6 +101,24 @@ __device__ __forceinline__ void load_affine8(const FwdParams& p, int vec, float 
   be[4] = b1.x; be[5] = b1.y; be[6] = b1.z; be[7] = b1.w;
 }
 
+// The same through buffer descriptors: the row loop reads gamma and beta this way when
+// they are not staged in LDS.  (Plain pointers here would let the compiler merge the LDS
+// and global reads into generic flat loads, which wait on every outstanding row store.)
+__device__ __forceinline__ void load_affine8_buf(rsrc_t g, rsrc_t b, int vec, float ga[8],
+                                                 float be[8]) {
+  const uint32_t off = (uint32_t)vec * 32u;
+  const v4u g0 = bload16_keep(g, off), g1 = bload16_keep(g, off + 16);
+  const v4u b0 = bload16_keep(b, off), b1 = bload16_keep(b, off + 16);
+  ga[0] = __uint_as_float(g0.x); ga[1] = __uint_as_float(g0.y);
+  ga[2] = __uint_as_float(g0.z); ga[3] = __uint_as_float(g0.w);
+  ga[4] = __uint_as_float(g1.x); ga[5] = __uint_as_float(g1.y);
+  ga[6] = __uint_as_float(g1.z); ga[7] = __uint_as_float(g1.w);
+  be[0] = __uint_as_float(b0.x); be[1] = __uint_as_float(b0.y);
+  be[2] = __uint_as_float(b0.z); be[3] = __uint_as_float(b0.w);
+  be[4] = __uint_as_float(b1.x); be[5] = __uint_as_float(b1.y);
+  be[6] = __uint_as_float(b1.z); be[7] = __uint_as_float(b1.w);
+}
+
 // Bytes of dynamic LDS a forward launch needs: `planes` FP32 planes of per-column
 // parameters (0 when they are read from global memory) and double-buffered reduction
 // slots of `stats` doubles per wave and row slot.
@@ -406,7 +424,12 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         // The per-column parameters are the same for every row, so the compiler would keep
         // them in VGPRs across the row loop.  LayerNorm's gamma and beta take 8 VGPRs per
         // vector: 1024-thread blocks (128 VGPRs a lane) re-read them from LDS instead.
-        if constexpr (kLN && NT >= 1024) asm volatile("" : "+v"(widx));
+#ifdef DN_LN_NO_HOIST
+        constexpr bool kReread = kLN;
+#else
+        constexpr bool kReread = kLN && NT >= 1024;
+#endif
+        if constexpr (kReread) asm volatile("" : "+v"(widx));
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
@@ -443,7 +466,8 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
               be[0] = b0.x; be[1] = b0.y; be[2] = b0.z; be[3] = b0.w;
               be[4] = b1.x; be[5] = b1.y; be[6] = b1.z; be[7] = b1.w;
             } else {
-              load_affine8(p, widx, we, be);
+              load_affine8_buf(make_rsrc(p.w, 4u * (uint32_t)p.hidden),
+                               make_rsrc(p.beta, 4u * (uint32_t)p.hidden), widx, we, be);
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] = fmaf(nv[k], we[k], be[k]);
