@@ -174,6 +174,14 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8 ||
                             EPI == EPI_LN_FP8);
   constexpr bool kDB = fwd_double_buffer(IN, EPI, VMAX, R, NT);
+  // Rows are held packed (BF16 pairs) across the reduction and unpacked again for the
+  // epilogue, halving their register footprint, except where the unpacked row fits
+  // comfortably: a single input of at most four vectors per lane and row.
+#ifdef DN_ALWAYS_PACK
+  constexpr bool kPackAcross = true;
+#else
+  constexpr bool kPackAcross = !(IN == IN_PLAIN && !kAda && !kMod && VMAX * R <= 4);
+#endif
 
   const Geom geo;
   const int tid = threadIdx.x;
@@ -184,6 +192,16 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   // Sub-wave rows: lanes past the row's last vector take an out-of-range offset.
   const bool lane_ok = TPR >= 64 || lane < nvec;
   float4* wl = reinterpret_cast<float4*>(dn_lds);
+  float inv_scale = 1.0f;
+  if constexpr (kStaticFp8) inv_scale = 1.0f / *p.scale;
+  // Static FP8 without a modulation: the reciprocal scale is folded into the staged
+  // per-column parameters (w_eff / scale; gamma / scale and beta / scale), one multiply
+  // per element fewer in the epilogue.
+#ifdef DN_NO_FOLD_SCALE
+  constexpr bool kFold = false;
+#else
+  constexpr bool kFold = (EPI == EPI_FP8 || EPI == EPI_LN_FP8);
+#endif
   double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)16 * kPlanes * nvec : 0));
 
   if (kPlanes > 0 && p.w_in_lds) {
@@ -191,6 +209,13 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
       if constexpr (kLN) {
         float ga[8], be[8];
         load_affine8(p, i, ga, be);
+        if constexpr (kFold) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            ga[k] *= inv_scale;
+            be[k] *= inv_scale;
+          }
+        }
         wl[i] = make_float4(ga[0], ga[1], ga[2], ga[3]);
         wl[nvec + i] = make_float4(ga[4], ga[5], ga[6], ga[7]);
         wl[2 * nvec + i] = make_float4(be[0], be[1], be[2], be[3]);
@@ -198,6 +223,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
       } else {
         float e[8];
         load_weff8(p, i, e);
+        if constexpr (kFold) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) e[k] *= inv_scale;
+        }
         wl[i] = make_float4(e[0], e[1], e[2], e[3]);
         wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
       }
@@ -214,9 +243,6 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         p.bscale[(i / pad) * p.bld + p.rows + (i % pad)] = 0.0f;
     }
   }
-
-  float inv_scale = 1.0f;
-  if constexpr (kStaticFp8) inv_scale = 1.0f / *p.scale;
 
   const double inv_hidden = 1.0 / (double)p.hidden;
   const double eps = (double)p.eps;
@@ -350,7 +376,9 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
-      for (int v = 0; v < VMAX; ++v) keep_packed(st.a[rr][v]);
+      for (int v = 0; v < VMAX; ++v) {
+        if constexpr (kPackAcross) keep_packed(st.a[rr][v]);
+      }
       ss[rr] = group_sum<RW>(ss[rr]);
       if constexpr (kLN) s1[rr] = group_sum<RW>(s1[rr]);
     }
@@ -468,6 +496,13 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
             } else {
               load_affine8_buf(make_rsrc(p.w, 4u * (uint32_t)p.hidden),
                                make_rsrc(p.beta, 4u * (uint32_t)p.hidden), widx, we, be);
+              if constexpr (kFold) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                  we[k] *= inv_scale;
+                  be[k] *= inv_scale;
+                }
+              }
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] = fmaf(nv[k], we[k], be[k]);
@@ -479,6 +514,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
             we[4] = hi.x; we[5] = hi.y; we[6] = hi.z; we[7] = hi.w;
           } else {
             load_weff8(p, widx, we);
+            if constexpr (kFold) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) we[k] *= inv_scale;
+            }
           }
 #pragma unroll
           for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
@@ -487,8 +526,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         if constexpr (EPI == EPI_BF16 || EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16) {
           bstore16(ry[rr], oy[rr] + d16, pack8(yv));
         } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8) {
+          if constexpr (!kFold) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
+            for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
+          }
           bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(yv));
         } else if constexpr (EPI == EPI_FP8_BLOCK) {
           // The BF16 normalised value is both normed_out and the quantiser's input.
