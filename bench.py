@@ -12,11 +12,20 @@ the 256 MB Infinity Cache by the previous kernel's traffic.
 
 `value` = algorithmic bytes of a step / wall time of a step (K steps between device
 synchronisations).  Algorithmic bytes count each tensor the definition reads or writes
-once; the backward's FP64 workspace traffic is not counted.  Per-kernel durations come from
-HIP events recorded on the stream the kernels run on.  `cpu_baseline` times the FP64 numpy
-oracle on a bounded sample of the same workload on this host.
+once; the backward's FP64 workspace traffic is not counted.  Inside the timed region only
+the dominant kernel (the training forward, the roofline's kernel) is bracketed by HIP events
+on the kernels' stream; the per-kernel table comes from K more steps with an event between
+every two kernels (each event record costs the stream a few microseconds, so the table's
+durations include that).  `cpu_baseline` times the FP64 numpy oracle on a bounded sample
+of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+Profiler runs pass --step-only (no copy ceiling, no shard shape), so that every library
+dispatch belongs to the step.  Profiler summaries (host only, no GPU):
+    python bench.py --summarize-counters FETCH.csv WRITE.csv   # rocprofv3 --pmc outputs of a
+        bench run with --copy-calibration: writes profiles/hbm_traffic.json, prints a table
+    python bench.py --summarize-trace STATS.csv                # rocprofv3 --stats output
 
 `--family layernorm` times the LayerNorm family instead (one line, per-kernel GB/s):
 layernorm and layernorm_quant on BF16 [8192, 4096], and the three DiT gate/residual +
@@ -87,6 +96,92 @@ def measured_traffic(kernel: str):
     return None if k is None else k["traffic_bytes"]
 
 
+STEP_KERNELS = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
+                "train_backward_partials", "train_backward_reduce"]
+GIB_KIB = float(1 << 20)
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _step_symbols(rows):
+    """The library's kernel symbols in order of first dispatch: one bench step launches
+    them in STEP_KERNELS order."""
+    seen = []
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        n = r["Kernel_Name"]
+        if n.startswith("void dn::") and n not in seen:
+            seen.append(n)
+    if len(seen) != len(STEP_KERNELS):
+        raise SystemExit(f"expected {len(STEP_KERNELS)} library kernels, found {seen}")
+    return dict(zip(STEP_KERNELS, seen))
+
+
+def _counter(rows, name):
+    """Per-symbol mean of one counter (KiB per dispatch) and the copy calibration scale:
+    bytes per KiB reported, from the 1 GiB device copies (the largest copy dispatches)."""
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == name:
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs if v > GIB_KIB / 4]
+    if not copies:
+        raise SystemExit(f"no 1 GiB calibration copy in the {name} run (use --copy-calibration)")
+    scale = GIB_KIB / (sum(copies) / len(copies))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, scale, len(copies)
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> int:
+    fr, wr = _read_csv(fetch_csv), _read_csv(write_csv)
+    sym = _step_symbols(fr)
+    if _step_symbols(wr) != sym:
+        raise SystemExit("the two counter runs dispatched different kernels")
+    fetch, fscale, nf = _counter(fr, "FETCH_SIZE")
+    write, wscale, nw = _counter(wr, "WRITE_SIZE")
+    ab = alg_bytes()
+    out = {"source_sha256": kernel_source_sha256(), "fetch_scale": fscale, "write_scale": wscale,
+           "calibration": f"{nf} and {nw} device copies of 1 GiB", "kernels": {}}
+    print("| kernel | symbol | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic MiB | "
+          "algorithmic MiB | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    for k in STEP_KERNELS:
+        s_ = sym[k]
+        rb = fetch[s_] * 1024 * fscale
+        wb = write[s_] * 1024 * wscale
+        t = rb + wb
+        out["kernels"][k] = {"symbol": s_, "fetch_kib": round(fetch[s_], 1),
+                             "write_kib": round(write[s_], 1), "read_bytes": int(rb),
+                             "write_bytes": int(wb), "traffic_bytes": int(t),
+                             "algorithmic_bytes": ab[k],
+                             "traffic_over_algorithmic": round(t / ab[k], 4)}
+        short = s_.replace("void ", "").split("(")[0]
+        ratio = f"{t / ab[k]:.3f}" if ab[k] > 1 << 20 else "(workspace)"
+        print(f"| {k} | `{short}` | {fetch[s_]:,.1f} | {write[s_]:,.1f} | {t / 2**20:,.1f} | "
+              f"{ab[k] / 2**20:,.1f} | {ratio} |")
+    print(f"\nscales: FETCH_SIZE x{fscale:.4f}, WRITE_SIZE x{wscale:.4f}")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(f"wrote {path}")
+    return 0
+
+
+def summarize_trace(stats_csv: str) -> int:
+    rows = _read_csv(stats_csv)
+    print("| kernel | calls | average ns | min ns | max ns | share |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].replace("void ", "").split("(")[0]
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):,.0f} | "
+              f"{int(float(r['MinNs'])):,} | {int(float(r['MaxNs'])):,} | "
+              f"{float(r['Percentage']):.2f} % |")
+    return 0
+
+
 def cpu_baseline(seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same workload: row blocks of the
     fused-add + static-FP8 forward [*, 4096] and of the training forward and backward
@@ -147,6 +242,74 @@ def ln_alg_bytes():
         # read x, residual, scale, shift; write residual_out, norm_out
         "dit_residual_layernorm_scale_shift": 12 * ed,
     }
+
+
+def _stats(ts):
+    """Average, median, p10 and p90 of a list of durations in seconds, as microseconds."""
+    v = sorted(ts)
+    q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+    return {"us": round(sum(v) / len(v) * 1e6, 2), "median_us": round(q(0.5) * 1e6, 2),
+            "p10_us": round(q(0.1) * 1e6, 2), "p90_us": round(q(0.9) * 1e6, 2)}
+
+
+def device_copy_ceiling(torch, dev, reps: int = 5) -> float:
+    """Measured copy ceiling: a 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB),
+    median of `reps`, in GB/s of bytes moved."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return round(2 * (1 << 30) / sorted(ts)[len(ts) // 2] / 1e9, 1)
+
+
+SHARD = (2048, 8192)
+
+
+def shard_measurement(torch, dev, dn, W, reps: int = 10):
+    """The training forward + backward at one GPU's share of an 8-way data-parallel C4
+    batch ([2048, 8192]); a 1 GiB buffer is overwritten before every launch so that the
+    32 MiB tensors come from HBM, not from the Infinity Cache."""
+    T, H = SHARD
+    wl = W.train(rows=T, hidden=H)
+    h, u, w, g = (wl.tensors[k].to(dev) for k in ("h", "residual", "w", "g"))
+    y, hn, dx = torch.empty_like(h), torch.empty_like(h), torch.empty_like(h)
+    rs = torch.empty(T, dtype=torch.float32, device=dev)
+    dw = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = dn.train_backward_workspace(H, dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    e = T * H
+    calls = {
+        "train_forward": (8 * e + 4 * T + 4 * H, lambda: dn.dn_train_forward(
+            h, w, 1e-6, w_bias=1.0, residual=u, out=y, rstd=rs, residual_out=hn)),
+        "train_backward": (6 * e + 4 * T + 8 * H, lambda: dn.dn_train_backward(
+            g, hn, w, rs, w_bias=1.0, workspace=ws, dx=dx, dw=dw)),
+    }
+    out = {}
+    for name, (nbytes, fn) in calls.items():
+        fn()
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        st = _stats(ts)
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        out[name] = dict(st, bytes=nbytes, **{"GB/s": round(gbs, 1)},
+                         frac=round(gbs / HBM_PEAK_GBS, 4))
+    del flush
+    return {"shape": list(SHARD), "note": "one GPU's rows of C4 split 8 ways; median of "
+                                          f"{reps} cold launches", "kernels": out}
 
 
 def run_layernorm_family(a) -> int:
@@ -210,10 +373,10 @@ def run_layernorm_family(a) -> int:
     ab = ln_alg_bytes()
     kernels = {}
     for j, n in enumerate(names):
-        avg = sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e-3 / len(evs)
-        gbs = ab[n] / avg / 1e9
-        kernels[n] = {"us": round(avg * 1e6, 2), "bytes": ab[n], "GB/s": round(gbs, 1),
-                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        st = _stats([e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs])
+        gbs = ab[n] / (st["us"] * 1e-6) / 1e9
+        kernels[n] = dict(st, bytes=ab[n], **{"GB/s": round(gbs, 1)},
+                          frac=round(gbs / HBM_PEAK_GBS, 4))
     step_bytes = sum(ab.values())
     value = step_bytes / (wall / a.steps) / 1e9
     line = {
@@ -239,6 +402,11 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="skip the copy ceiling and the shard shape (profiler runs: every "
+                         "library dispatch is then a bench-step kernel)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV")
     ap.add_argument("--family", choices=("rmsnorm", "layernorm"), default="rmsnorm",
                     help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm family")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -246,6 +414,10 @@ def main(argv=None) -> int:
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
                          "times, to scale profiler byte counters")
     a = ap.parse_args(argv)
+    if a.summarize_counters:
+        return summarize_counters(*a.summarize_counters)
+    if a.summarize_trace:
+        return summarize_trace(a.summarize_trace)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
               f"MI355X (rows shard across GPUs with no communication except dw); --gpus {a.gpus} "
@@ -281,9 +453,9 @@ def main(argv=None) -> int:
     names = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
              "train_backward_partials", "train_backward_reduce"]
 
-    def step(events=None):
+    def step(events=None, only=None):
         def mark(i):
-            if events is not None:
+            if events is not None and (only is None or i in only):
                 events[i].record()
         mark(0)
         dn.dn_fused_add_rmsnorm(x2, r2, w2, 1e-6)
@@ -310,16 +482,26 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps between synchronisations (wall clock), with per-kernel events.
+    # Timed region: K steps between synchronisations (wall clock).  Only the dominant kernel
+    # (the training forward) is bracketed by events here: every event record in the stream
+    # costs ~3 us of device time (measured: 409 us per step without events, 428 us with six).
+    dom = "train_forward"
+    di = names.index(dom)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(evs[i])
+        step(evs[i], only=(di, di + 1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    dom_live = [e[di].elapsed_time(e[di + 1]) * 1e-3 for e in evs]
 
+    # Per-kernel breakdown: K more steps with an event between every two kernels.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     per = {n: [] for n in names}
     for e in evs:
         for j, n in enumerate(names):
@@ -331,10 +513,10 @@ def main(argv=None) -> int:
 
     kernels = {}
     for n in names:
-        avg = sum(per[n]) / len(per[n])
-        gbs = ab[n] / avg / 1e9
-        kernels[n] = {"us": round(avg * 1e6, 2), "bytes": ab[n], "GB/s": round(gbs, 1),
-                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        st = _stats(per[n])
+        gbs = ab[n] / (st["us"] * 1e-6) / 1e9
+        kernels[n] = dict(st, bytes=ab[n], **{"GB/s": round(gbs, 1)},
+                          frac=round(gbs / HBM_PEAK_GBS, 4))
     bwd_s = (sum(per["train_backward_partials"]) + sum(per["train_backward_reduce"])) / a.steps
     bwd_b = ab["train_backward_partials"] + ab["train_backward_reduce"]
     fa_s = sum(per["fused_add_rmsnorm"]) / a.steps
@@ -344,12 +526,18 @@ def main(argv=None) -> int:
         "fused_add_fwd_plus_train_bwd_GB/s": round((ab["fused_add_rmsnorm"] + bwd_b) /
                                                   (fa_s + bwd_s) / 1e9, 1),
     }
-    dom = max(names, key=lambda n: sum(per[n]))
-    dom_avg = sum(per[dom]) / len(per[dom])
+    dom_avg = sum(dom_live) / len(dom_live)
     achieved = ab[dom] / dom_avg / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom]}
+
+    ceiling = shard = None
+    if not a.step_only:
+        print("[bench] copy ceiling and one GPU's shard of the training shape", file=sys.stderr,
+              flush=True)
+        ceiling = {"device_copy_1GiB_GB/s": device_copy_ceiling(torch, dev)}
+        shard = shard_measurement(torch, dev, dn, W)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -369,6 +557,7 @@ def main(argv=None) -> int:
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "step_bytes": step_bytes, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "headline": headline,
+        "ceilings": ceiling, "shard_2048x8192": shard,
     }
     print(json.dumps(line), flush=True)
     return 0
