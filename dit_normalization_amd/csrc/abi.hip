@@ -658,4 +658,104 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
   return launch_fwd<IN_ADD, EPI_LN_MOD_BF16>(p, static_cast<hipStream_t>(stream));
 }
 
+// ------------------------------------------------------------------ fused QK norm + RoPE
+
+dn_status dn_fused_qk_rmsnorm_rope(
+    void* q_out, int64_t q_out_stride, void* k_out, int64_t k_out_stride, void* v_out,
+    int64_t v_out_stride, int output_fp8, const float* output_quant_scale,
+    const float* v_quant_scale, const void* qkv, int64_t qkv_stride, const void* q_weight,
+    const void* k_weight, int w_dtype, int is_qk_norm, int64_t tokens, int num_heads_q,
+    int num_heads_k, int num_heads_v, int head_dim, int ppf, int pph, int ppw,
+    int num_frame_channels, int num_height_channels, int num_width_channels, double base,
+    int interleave, double yarn_factor, double yarn_low, double yarn_high,
+    float attention_factor, float eps, dn_stream_t stream) {
+  if (tokens < 0) return fail(DN_ERR_SHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(DN_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (num_heads_q < 1 || num_heads_k < 1 || num_heads_v < 1 || num_heads_q > 32 ||
+      num_heads_k > 32 || num_heads_v > 32)
+    return fail(DN_ERR_SHAPE, "head counts must be in [1, 32] (got %d, %d, %d)", num_heads_q,
+                num_heads_k, num_heads_v);
+  const int cf = num_frame_channels, ch = num_height_channels, cw = num_width_channels;
+  if (cf < 0 || ch < 0 || cw < 0 || cf % 2 || ch % 2 || cw % 2 || cf + ch + cw != head_dim)
+    return fail(DN_ERR_SHAPE,
+                "frame/height/width channels must be even, >= 0 and sum to head_dim %d "
+                "(got %d, %d, %d)", head_dim, cf, ch, cw);
+  if (ppf < 1 || pph < 1 || ppw < 1)
+    return fail(DN_ERR_SHAPE, "ppf, pph and ppw must be >= 1");
+  const int64_t seq = (int64_t)ppf * pph * ppw;
+  if (tokens % seq != 0)
+    return fail(DN_ERR_SHAPE, "tokens %lld is not a multiple of ppf*pph*ppw = %lld",
+                (long long)tokens, (long long)seq);
+  if (!(base > 0.0)) return fail(DN_ERR_SHAPE, "base must be > 0");
+  if (!(yarn_factor > 0.0)) return fail(DN_ERR_SHAPE, "yarn factor must be > 0");
+  if (yarn_factor == 1.0 && attention_factor != 1.0f)
+    return fail(DN_ERR_SHAPE, "attention_factor must be 1.0 when the yarn factor is 1.0");
+  if (output_fp8 != 0 && output_fp8 != 1)
+    return fail(DN_ERR_DTYPE, "output_fp8 must be 0 or 1");
+  if (tokens == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  const int width = (num_heads_q + num_heads_k + num_heads_v) * head_dim;
+  DN_CHECK(check_matrix(qkv, qkv_stride, width, 2, "qkv"));
+  const int oe = output_fp8 ? 1 : 2;
+  DN_CHECK(check_matrix(q_out, q_out_stride, (int64_t)num_heads_q * head_dim, oe, "q_out"));
+  DN_CHECK(check_matrix(k_out, k_out_stride, (int64_t)num_heads_k * head_dim, oe, "k_out"));
+  DN_CHECK(check_matrix(v_out, v_out_stride, (int64_t)num_heads_v * head_dim, oe, "v_out"));
+  if (is_qk_norm) {
+    DN_CHECK(check_weight(q_weight, w_dtype));
+    if (!k_weight) return fail(DN_ERR_NULL, "k_weight must not be NULL");
+    if (!aligned(k_weight, 16)) return fail(DN_ERR_ALIGN, "k_weight must be 16-byte aligned");
+  }
+  if (output_fp8) {
+    DN_CHECK(check_f32(output_quant_scale, "output_quant_scale", true));
+    DN_CHECK(check_f32(v_quant_scale, "v_quant_scale", true));
+  }
+  RopeParams p{};
+  p.qkv = static_cast<const uint16_t*>(qkv); p.sqkv = qkv_stride;
+  p.wq = q_weight; p.wk = k_weight; p.w_f32 = w_dtype == DN_WEIGHT_F32;
+  p.qo = q_out; p.sqo = q_out_stride;
+  p.ko = k_out; p.sko = k_out_stride;
+  p.vo = v_out; p.svo = v_out_stride;
+  p.qk_scale = output_quant_scale; p.v_scale = v_quant_scale;
+  p.rows = tokens;
+  p.nq = num_heads_q; p.nk = num_heads_k; p.nv = num_heads_v; p.hd = head_dim;
+  p.cf = cf; p.ch = ch; p.cw = cw;
+  p.ppf = ppf; p.pph = pph; p.ppw = ppw;
+  p.eps = eps; p.af = attention_factor;
+  p.base = base; p.factor = yarn_factor; p.low = yarn_low; p.high = yarn_high;
+  p.qk_norm = is_qk_norm != 0;
+  p.nvec = width / 8;
+  p.nwvec = (num_heads_q + num_heads_k) * head_dim / 8;
+  p.w_in_lds = p.qk_norm && p.nwvec <= kMaxLdsWeightVectors;
+
+  const bool neox = interleave == 0;
+  const int units = neox ? p.nvec / 2 : p.nvec;
+  int tier = -1;
+  for (int t = 0; t < kRopeTierCount && tier < 0; ++t) {
+    const TierShape ts = rope_tier_shape(t);
+    if (ts.tpr * (neox ? ts.vmax / 2 : ts.vmax) >= units) tier = t;
+  }
+  if (tier < 0) return fail(DN_ERR_SHAPE, "the qkv row is too wide");
+  const TierShape ts = rope_tier_shape(tier);
+  const int g = ts.nt / ts.tpr;
+  const int wpr = ts.tpr > 64 ? ts.tpr / 64 : 1;
+  const size_t lds = rope_lds_bytes(p.w_in_lds, p.nwvec, head_dim, g, wpr);
+  auto launch = [&](int grid, hipStream_t st, const void** k) -> hipError_t {
+    if (neox)
+      return output_fp8 ? rope_launch<true, true>(p, tier, grid, lds, st, k)
+                        : rope_launch<true, false>(p, tier, grid, lds, st, k);
+    return output_fp8 ? rope_launch<false, true>(p, tier, grid, lds, st, k)
+                      : rope_launch<false, false>(p, tier, grid, lds, st, k);
+  };
+  const void* kernel = nullptr;
+  if (launch(0, nullptr, &kernel) != hipSuccess || !kernel)
+    return fail(DN_ERR_HIP, "no kernel instance for rope tier %d", tier);
+  int capacity = 0;
+  DN_CHECK(resident_blocks(kernel, ts.nt, lds, DN_BLOCKS_PER_CU_SINGLE, &capacity));
+  const int64_t needed = (tokens + g - 1) / g;
+  const int grid = (int)(needed < capacity ? needed : capacity);
+  const hipError_t e = launch(grid > 0 ? grid : 1, static_cast<hipStream_t>(stream), nullptr);
+  if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return DN_OK;
+}
+
 }  // extern "C"

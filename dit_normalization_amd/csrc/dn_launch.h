@@ -6,6 +6,7 @@
 
 #include "dn_bwd.h"
 #include "dn_fwd.h"
+#include "dn_rope.h"
 
 namespace dn {
 
@@ -40,6 +41,21 @@ inline TierShape bwd_tier_shape(int tier) {
 template <int IN, int EPI>
 hipError_t fwd_launch(const FwdParams& p, int tier, int grid, size_t lds, hipStream_t s,
                       const void** kernel_out);
+
+inline TierShape rope_tier_shape(int tier) {
+  switch (tier) {
+#define DN_X(i, tpr, v, nt) \
+  case i: return TierShape{tpr, v, 1, nt};
+    DN_ROPE_TIERS(DN_X)
+#undef DN_X
+  }
+  return TierShape{0, 0, 0, 0};
+}
+
+// Launch one fused QK RMSNorm + RoPE kernel instance (or return its address).
+template <bool NEOX, bool FP8>
+hipError_t rope_launch(const RopeParams& p, int tier, int grid, size_t lds, hipStream_t s,
+                       const void** kernel_out);
 
 hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStream_t s,
                                const void** kernel_out);

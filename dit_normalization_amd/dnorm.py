@@ -23,6 +23,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int
 _F32 = ctypes.c_float
+_F64 = ctypes.c_double
 _SZ = ctypes.c_size_t
 
 # C signatures (argument types in order), mirroring include/dnorm.h.
@@ -65,6 +66,10 @@ SIGNATURES = {
     "dn_fused_dit_residual_layernorm_scale_shift": (
         [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P, _I64, _F32, _I64, _I64, _F32,
          _P], _I32),
+    "dn_fused_qk_rmsnorm_rope": (
+        [_P, _I64, _P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32,
+         _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F64, _I32, _F64, _F64, _F64,
+         _F32, _F32, _P], _I32),
 }
 
 
@@ -504,6 +509,54 @@ def dn_fused_dit_residual_layernorm_scale_shift(x, scale, shift, residual=None,
         _writeback(ro, ror)
     _writeback(n, nr)
     return ro, n
+
+
+def dn_fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, num_heads_q: int, num_heads_k: int,
+                             num_heads_v: int, head_dim: int, ppf: int, pph: int, ppw: int,
+                             channels, eps: float = 1e-6, *, base: float = 10000.0,
+                             interleave: bool = True, yarn_factor: float = 1.0,
+                             yarn_low: float = 0.0, yarn_high: float = 0.0,
+                             attention_factor: float = 1.0, is_qk_norm: bool = True,
+                             output_fp8: bool = False, output_quant_scale=None,
+                             v_quant_scale=None, q_out=None, k_out=None, v_out=None):
+    """Cross-head RMSNorm of Q and K, 3-D RoPE (frame/height/width channel groups
+    `channels`), V copy.  qkv: BF16 [tokens, (nq+nk+nv)*head_dim] or [batch, seq, ...].
+    Returns (q_out, k_out, v_out), BF16 or (output_fp8) e4m3fn."""
+    xr, rows, sx = _rows(qkv, "qkv")
+    lead = qkv.shape[:-1]
+    nq, nk, nv, hd = int(num_heads_q), int(num_heads_k), int(num_heads_v), int(head_dim)
+    odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
+
+    def out(t, heads, name):
+        if t is None:
+            t = torch.empty((*lead, heads * hd), dtype=odt, device=qkv.device)
+        tr, _, st = _rows(t, name, odt)
+        if tr.data_ptr() != t.data_ptr():
+            raise DnormError(f"{name} needs a row-addressable layout")
+        return t, tr, st
+
+    q_out, qr, sq = out(q_out, nq, "q_out")
+    k_out, kr, sk = out(k_out, nk, "k_out")
+    v_out, vr, sv = out(v_out, nv, "v_out")
+    wq = wk = None
+    wcode = DN_WEIGHT_BF16
+    if is_qk_norm:
+        wq, wcode = _weight(q_weight)
+        wk, wcode_k = _weight(k_weight)
+        if wcode_k != wcode:
+            raise DnormError("q_weight and k_weight must have the same dtype")
+    qs = vs = None
+    if output_fp8:
+        qs = _scale_tensor(1.0 if output_quant_scale is None else output_quant_scale, qkv.device)
+        vs = _scale_tensor(1.0 if v_quant_scale is None else v_quant_scale, qkv.device)
+    cf, ch, cw = (int(c) for c in channels)
+    _check(lib.dn_fused_qk_rmsnorm_rope(
+        qr.data_ptr(), sq, kr.data_ptr(), sk, vr.data_ptr(), sv, int(bool(output_fp8)), _ptr(qs),
+        _ptr(vs), xr.data_ptr(), sx, _ptr(wq), _ptr(wk), wcode, int(bool(is_qk_norm)), rows, nq,
+        nk, nv, hd, int(ppf), int(pph), int(ppw), cf, ch, cw, float(base), int(bool(interleave)),
+        float(yarn_factor), float(yarn_low), float(yarn_high), float(attention_factor),
+        float(eps), _stream(qkv)), "dn_fused_qk_rmsnorm_rope")
+    return q_out, k_out, v_out
 
 
 def dn_force_threads_per_row(threads: int):

@@ -308,6 +308,45 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
     int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * fused_qk_rmsnorm_rope   ([norm docs] API table: fused_qk_rmsnorm_rope; [norm guide] §5.2)
+ *
+ * qkv: BF16 [tokens, (nq + nk + nv) * head_dim] (row stride qkv_stride), heads in the
+ * order Q, K, V.  Per token:
+ *   Q and K (is_qk_norm != 0): n = (x * r) * w, r = 1/sqrt(mean(x^2) + eps) taken across
+ *     all heads of Q (resp. K); q_weight [nq*head_dim], k_weight [nk*head_dim], BF16 or
+ *     FP32 (w_dtype).  is_qk_norm == 0: n = x, weights unused (may be NULL).
+ *   3-D rotary embedding of every head: the token's index t in its sequence (t mod
+ *     ppf*pph*ppw) gives frame t / (pph*ppw), height (t / ppw) % pph, width t % ppw.
+ *     Pair j < head_dim/2 is channels (2j, 2j+1) when interleave != 0, (j, j + head_dim/2)
+ *     otherwise (NeoX); the first num_frame_channels/2 pairs turn with the frame, the next
+ *     num_height_channels/2 with the height, the rest with the width, at angle
+ *     position * inv_freq, inv_freq = base^(-2i/count) for pair i of a group of count
+ *     channels.  yarn_factor != 1 blends inv_freq / factor and inv_freq with
+ *     ramp = clamp((i - yarn_low) / (yarn_high - yarn_low), 0, 1) (yarn_high == yarn_low
+ *     takes yarn_high + 0.001).  (a, b) -> (a cos - b sin, a sin + b cos), with cos and
+ *     sin times attention_factor; angles and sincos in FP64, then FP32.
+ *   V: copied bit for bit.
+ * Outputs q_out [tokens, nq*head_dim], k_out, v_out (each with its row stride): BF16
+ * (output_fp8 == 0; one rounding of the FP32 result), or e4m3fn (output_fp8 == 1): Q and K
+ * divided by *output_quant_scale, V by *v_quant_scale (device FP32 [1] each).
+ *
+ * Limits (the pages'): head_dim in {64, 128, 256}; 1..32 heads of each kind; channel
+ * counts even (0 allowed) summing to head_dim; tokens a multiple of ppf*pph*ppw;
+ * attention_factor must be 1 when yarn_factor is 1.
+ */
+dn_status dn_fused_qk_rmsnorm_rope(
+    void* q_out, int64_t q_out_stride, void* k_out, int64_t k_out_stride,
+    void* v_out, int64_t v_out_stride, int output_fp8,
+    const float* output_quant_scale, const float* v_quant_scale,
+    const void* qkv, int64_t qkv_stride,
+    const void* q_weight, const void* k_weight, int w_dtype, int is_qk_norm,
+    int64_t tokens, int num_heads_q, int num_heads_k, int num_heads_v, int head_dim,
+    int ppf, int pph, int ppw,
+    int num_frame_channels, int num_height_channels, int num_width_channels,
+    double base, int interleave, double yarn_factor, double yarn_low, double yarn_high,
+    float attention_factor, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Test and tuning hook: force the threads that share one row (8, 16, 32, 64, 128, 256,
  * 512 or 1024) in every forward launch of this process; 0 restores the automatic choice
  * by hidden size.  Returns DN_ERR_SHAPE for other values or when the forced count cannot

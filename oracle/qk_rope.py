@@ -40,10 +40,12 @@ from .formats import bf16_round
 from .rmsnorm import Quant, quantize_static
 
 
-def token_positions(tokens: int, ppf: int, pph: int, ppw: int):
-    """(frame, height, width) patch coordinates of every token (row-major patches)."""
+def token_positions(tokens, ppf: int, pph: int, ppw: int):
+    """(frame, height, width) patch coordinates of every token (row-major patches).
+    `tokens` is a token count (tokens 0 .. tokens-1) or an array of token indices."""
     seq = ppf * pph * ppw
-    t = np.arange(tokens, dtype=np.int64) % seq
+    ids = np.arange(tokens) if np.ndim(tokens) == 0 else np.asarray(tokens)
+    t = ids.astype(np.int64) % seq
     return t // (pph * ppw), (t // ppw) % pph, t % ppw
 
 
@@ -72,9 +74,10 @@ def pair_tables(head_dim: int, channels, base=10000.0, factor=1.0, low=0.0, high
     return group.astype(np.int64), freq
 
 
-def rope_angles(tokens: int, head_dim: int, channels, ppf: int, pph: int, ppw: int,
+def rope_angles(tokens, head_dim: int, channels, ppf: int, pph: int, ppw: int,
                 base=10000.0, factor=1.0, low=0.0, high=0.0) -> np.ndarray:
-    """theta[t, j] = position of token t in pair j's group * inv_freq[j], FP64."""
+    """theta[t, j] = position of token t in pair j's group * inv_freq[j], FP64 (`tokens` as
+    in token_positions)."""
     pos = np.stack(token_positions(tokens, ppf, pph, ppw), axis=1).astype(np.float64)
     group, freq = pair_tables(head_dim, channels, base, factor, low, high)
     return pos[:, group] * freq[None, :]
@@ -131,14 +134,17 @@ def qk_rmsnorm_rope(qkv, q_weight, k_weight, nq: int, nk: int, nv: int, head_dim
                     channels, ppf: int, pph: int, ppw: int, eps: float = 1e-6,
                     base: float = 10000.0, interleave: bool = True, factor: float = 1.0,
                     low: float = 0.0, high: float = 0.0, attention_factor: float = 1.0,
-                    is_qk_norm: bool = True) -> QKRope:
+                    is_qk_norm: bool = True, token_ids=None) -> QKRope:
     """Q and K: cross-head RMSNorm (unless is_qk_norm is False), then the 3-D rotary
-    embedding; V: copied (norm guide §5.2)."""
+    embedding; V: copied (norm guide §5.2).  `token_ids` gives the token index of each row
+    of qkv when the rows are a sample of a longer call (default: rows 0, 1, ...)."""
     qkv = np.asarray(qkv, dtype=np.float64)
     tokens = qkv.shape[0]
     hd = head_dim
     assert qkv.shape[1] == (nq + nk + nv) * hd
-    assert tokens % (ppf * pph * ppw) == 0
+    if token_ids is None:
+        assert tokens % (ppf * pph * ppw) == 0
+        token_ids = tokens
     q = qkv[:, :nq * hd]
     k = qkv[:, nq * hd:(nq + nk) * hd]
     v = qkv[:, (nq + nk) * hd:]
@@ -146,7 +152,7 @@ def qk_rmsnorm_rope(qkv, q_weight, k_weight, nq: int, nk: int, nv: int, head_dim
     if is_qk_norm:
         q, rq = cross_head_rmsnorm(q, q_weight, eps)
         k, rk = cross_head_rmsnorm(k, k_weight, eps)
-    theta = rope_angles(tokens, hd, channels, ppf, pph, ppw, base, factor, low, high)
+    theta = rope_angles(token_ids, hd, channels, ppf, pph, ppw, base, factor, low, high)
     qo, qm = rotate(q.reshape(tokens, nq, hd), theta, interleave, attention_factor)
     ko, km = rotate(k.reshape(tokens, nk, hd), theta, interleave, attention_factor)
     qo, qm = qo.reshape(tokens, -1), qm.reshape(tokens, -1)

@@ -47,7 +47,8 @@ def test_header_declares_the_expected_calls():
               "dn_train_backward_reduce", "dn_layernorm", "dn_layernorm_quant",
               "dn_fused_dit_gate_residual_layernorm_gamma_beta",
               "dn_fused_dit_gate_residual_layernorm_scale_shift",
-              "dn_fused_dit_residual_layernorm_scale_shift", "dn_last_error"]:
+              "dn_fused_dit_residual_layernorm_scale_shift", "dn_fused_qk_rmsnorm_rope",
+              "dn_last_error"]:
         assert n in names
 
 
@@ -199,6 +200,32 @@ def test_dit_checks(lib):
               None) == E_UNSUP                                   # residual_out without residual
     assert rs(0, 0, A, 3072, B, 3072, 0, 0, C, 18432, 0.0, 0, 18432, 0.0, 4, 3072, 1e-6,
               None) == E_NULL                                    # shift
+
+
+def rope(lib, tokens=12, nq=24, nk=24, nv=24, hd=128, ppf=1, pph=3, ppw=4, ch=(44, 42, 42),
+         fp8=0, qs=A, vs=B, qkv=C, qkv_s=None, wq=D, wk=E, norm=1, factor=1.0, af=1.0):
+    w = (nq + nk + nv) * hd
+    return lib.dn_fused_qk_rmsnorm_rope(
+        A, nq * hd, B, nk * hd, C, nv * hd, fp8, qs, vs, qkv, w if qkv_s is None else qkv_s,
+        wq, wk, 0, norm, tokens, nq, nk, nv, hd, ppf, pph, ppw, ch[0], ch[1], ch[2], 10000.0, 1,
+        factor, 0.0, 0.0, af, 1e-6, None)
+
+
+def test_qk_rope_checks(lib):
+    assert rope(lib, tokens=0) == OK
+    assert rope(lib, tokens=0, qkv=0, wq=0, wk=0) == OK          # empty: NULL pointers
+    assert rope(lib, tokens=0, hd=96, ch=(32, 32, 32)) == E_UNSUP   # head_dim not 64/128/256
+    assert rope(lib, tokens=0, nq=33) == E_SHAPE                  # more than 32 heads
+    assert rope(lib, tokens=0, ch=(44, 41, 43)) == E_SHAPE        # odd channel counts
+    assert rope(lib, tokens=0, ch=(44, 42, 40)) == E_SHAPE        # do not sum to head_dim
+    assert rope(lib, tokens=13) == E_SHAPE                        # not a multiple of 12
+    assert b"multiple" in lib.dn_last_error()
+    assert rope(lib, tokens=0, af=1.5) == E_SHAPE                 # af != 1 needs yarn
+    assert rope(lib, tokens=0, factor=4.0, af=1.5) == OK
+    assert rope(lib, wq=0) == E_NULL
+    assert rope(lib, fp8=1, qs=0) == E_NULL                        # FP8 needs its scales
+    assert rope(lib, qkv_s=9208) == E_SHAPE                       # stride < width
+    assert rope(lib, ch=(128, 0, 0), tokens=0) == OK              # empty groups allowed
 
 
 def test_force_threads_per_row(lib):

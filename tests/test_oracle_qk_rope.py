@@ -193,3 +193,14 @@ def test_each_channel_group_follows_its_own_axis(axis):
     others = np.ones(20, dtype=bool)
     others[start:stop] = False
     assert (th[:, others] == 0).all()
+
+
+def test_token_ids_select_rows_of_the_full_call():
+    nq, nk, nv, hd = 1, 1, 1, 64
+    qkv = bf16_values((24, 3 * hd))
+    w = np.ones(hd)
+    full = Q.qk_rmsnorm_rope(qkv, w, w, nq, nk, nv, hd, (24, 20, 20), 2, 3, 4)
+    ids = np.array([0, 5, 17, 23])
+    part = Q.qk_rmsnorm_rope(qkv[ids], w, w, nq, nk, nv, hd, (24, 20, 20), 2, 3, 4,
+                             token_ids=ids)
+    assert (part.q_exact == full.q_exact[ids]).all() and (part.k == full.k[ids]).all()

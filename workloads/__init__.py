@@ -142,3 +142,20 @@ def dit(rows: int = 2520, hidden: int = 3072, seed: int = 7) -> Workload:
         t[name] = temb[:, k * hidden:(k + 1) * hidden]
     return Workload("dit", t, {"eps": 1e-6, "rows": rows, "hidden": hidden, "gate_bias": 0.25,
                                "scale_bias": 0.125, "shift_bias": -0.0625})
+
+
+def qk_rope(ppf: int = 16, pph: int = 24, ppw: int = 32, batch: int = 1, nq: int = 24,
+            nk: int = 24, nv: int = 24, head_dim: int = 128, channels=(44, 42, 42),
+            seed: int = 8) -> Workload:
+    """Fused QK RMSNorm + 3-D RoPE: qkv BF16 [batch*ppf*pph*ppw, (nq+nk+nv)*head_dim]
+    ~ N(0,1); q_weight, k_weight BF16 ~ N(1, 0.1).  The default head layout (24 heads of
+    128 channels; 44 frame, 42 height and 42 width channels) is that of a 3072-wide
+    video DiT; the patch grid 16 x 24 x 32 is a stand-in video latent."""
+    tokens = batch * ppf * pph * ppw
+    return Workload("qk_rope", {
+        "qkv": normal((tokens, (nq + nk + nv) * head_dim), seed, 0),
+        "q_weight": normal((nq * head_dim,), seed, 1, mean=1.0, std=0.1),
+        "k_weight": normal((nk * head_dim,), seed, 2, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "tokens": tokens, "nq": nq, "nk": nk, "nv": nv, "head_dim": head_dim,
+        "channels": tuple(channels), "ppf": ppf, "pph": pph, "ppw": ppw, "base": 10000.0,
+        "output_scale": 0.05, "v_scale": 0.02})
