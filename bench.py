@@ -30,7 +30,8 @@ dispatch belongs to the step.  Profiler summaries (host only, no GPU):
 `--family layernorm` times the LayerNorm family instead (one line, per-kernel GB/s):
 layernorm and layernorm_quant on BF16 [8192, 4096], and the three DiT gate/residual +
 LayerNorm modes on BF16 [16384, 3072] with gate/scale/shift read as row-stride-6*hidden
-chunks of one per-token modulation tensor.
+chunks of one per-token modulation tensor.  `--family qk_rope` times the fused QK
+RMSNorm + 3-D RoPE + V copy on qkv BF16 [12288, 9216] (both pairings, BF16 and e4m3fn).
 """
 from __future__ import annotations
 
@@ -352,6 +353,16 @@ def run_layernorm_family(a) -> int:
                 dx, chunk["scale"], chunk["shift"], dr, 1e-6, scale_bias=p["scale_bias"],
                 shift_bias=p["shift_bias"], residual_out=ro, norm_out=no)),
     }
+    return time_family(a, torch, dev, calls, ln_alg_bytes(), "achieved HBM GB/s, LayerNorm family",
+                       "layernorm + layernorm_quant BF16 [8192,4096]; DiT gate/residual "
+                       "+ LayerNorm (gamma/beta, scale/shift) and residual + LayerNorm "
+                       "scale/shift BF16 [16384,3072], modulation chunks of a "
+                       "[16384,18432] tensor")
+
+
+def time_family(a, torch, dev, calls, ab, metric, workload) -> int:
+    """Warm up, then time `a.steps` rounds of every call in `calls` (one event between every
+    two calls on the calls' stream) and print one JSON line with per-call GB/s."""
     names = list(calls)
     for _ in range(a.warmup):
         for n in names:
@@ -360,7 +371,7 @@ def run_layernorm_family(a) -> int:
     stream = torch.cuda.current_stream(dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(a.steps)]
-    print(f"[bench] timing {a.steps} steps of the LayerNorm family", file=sys.stderr, flush=True)
+    print(f"[bench] timing {a.steps} rounds", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -370,7 +381,6 @@ def run_layernorm_family(a) -> int:
         e[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ab = ln_alg_bytes()
     kernels = {}
     for j, n in enumerate(names):
         st = _stats([e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs])
@@ -380,20 +390,59 @@ def run_layernorm_family(a) -> int:
     step_bytes = sum(ab.values())
     value = step_bytes / (wall / a.steps) / 1e9
     line = {
-        "metric": "achieved HBM GB/s, LayerNorm family", "value": round(value, 1),
+        "metric": metric, "value": round(value, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(wall / a.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "layernorm + layernorm_quant BF16 [8192,4096]; DiT gate/residual "
-                               "+ LayerNorm (gamma/beta, scale/shift) and residual + LayerNorm "
-                               "scale/shift BF16 [16384,3072], modulation chunks of a "
-                               "[16384,18432] tensor",
+        "config": {"workload": workload,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4), "step_bytes": step_bytes,
                    "parallelism": "single GPU"},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def run_qk_rope_family(a) -> int:
+    """fused_qk_rmsnorm_rope on the stand-in video latent (12288 tokens, 24+24+24 heads of
+    128 channels, 44/42/42 frame/height/width channels): interleaved and NeoX pairing, BF16
+    and e4m3fn outputs."""
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating QK RoPE inputs", file=sys.stderr, flush=True)
+    wl = W.qk_rope()
+    t, p = wl.tensors, wl.params
+    qkv, wq, wk = (t[k].to(dev) for k in ("qkv", "q_weight", "k_weight"))
+    T, width = qkv.shape
+    qs = torch.tensor([p["output_scale"]], dtype=torch.float32, device=dev)
+    vs = torch.tensor([p["v_scale"]], dtype=torch.float32, device=dev)
+    outs = {}
+    for fp8 in (False, True):
+        dt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+        outs[fp8] = [torch.empty((T, n * p["head_dim"]), dtype=dt, device=dev)
+                     for n in (p["nq"], p["nk"], p["nv"])]
+
+    def call(interleave, fp8):
+        q, k, v = outs[fp8]
+        return lambda: dn.dn_fused_qk_rmsnorm_rope(
+            qkv, wq, wk, p["nq"], p["nk"], p["nv"], p["head_dim"], p["ppf"], p["pph"], p["ppw"],
+            p["channels"], p["eps"], interleave=interleave, output_fp8=fp8,
+            output_quant_scale=qs, v_quant_scale=vs, q_out=q, k_out=k, v_out=v)
+
+    calls = {"qk_rope_interleaved_bf16": call(True, False), "qk_rope_neox_bf16": call(False, False),
+             "qk_rope_interleaved_fp8": call(True, True), "qk_rope_neox_fp8": call(False, True)}
+    e = T * width
+    wbytes = 2 * (p["nq"] + p["nk"]) * p["head_dim"]
+    ab = {"qk_rope_interleaved_bf16": 4 * e + wbytes, "qk_rope_neox_bf16": 4 * e + wbytes,
+          "qk_rope_interleaved_fp8": 3 * e + wbytes + 8, "qk_rope_neox_fp8": 3 * e + wbytes + 8}
+    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused QK RMSNorm + 3-D RoPE",
+                       f"fused_qk_rmsnorm_rope qkv BF16 [{T},{width}] (24+24+24 heads x 128, "
+                       f"patches {p['ppf']}x{p['pph']}x{p['ppw']}), BF16 or e4m3fn q/k/v out")
 
 
 def main(argv=None) -> int:
@@ -407,8 +456,9 @@ def main(argv=None) -> int:
                          "library dispatch is then a bench-step kernel)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", metavar="STATS_CSV")
-    ap.add_argument("--family", choices=("rmsnorm", "layernorm"), default="rmsnorm",
-                    help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm family")
+    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope"), default="rmsnorm",
+                    help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm "
+                         "family; qk_rope: the fused QK RMSNorm + 3-D RoPE")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
@@ -432,6 +482,8 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.family == "layernorm":
         return run_layernorm_family(a)
+    if a.family == "qk_rope":
+        return run_qk_rope_family(a)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)

@@ -684,6 +684,8 @@ dn_status dn_fused_qk_rmsnorm_rope(
   if (ppf < 1 || pph < 1 || ppw < 1)
     return fail(DN_ERR_SHAPE, "ppf, pph and ppw must be >= 1");
   const int64_t seq = (int64_t)ppf * pph * ppw;
+  if (tokens >= ((int64_t)1 << 31) || seq >= ((int64_t)1 << 31))
+    return fail(DN_ERR_SHAPE, "tokens and ppf*pph*ppw must stay below 2^31");
   if (tokens % seq != 0)
     return fail(DN_ERR_SHAPE, "tokens %lld is not a multiple of ppf*pph*ppw = %lld",
                 (long long)tokens, (long long)seq);

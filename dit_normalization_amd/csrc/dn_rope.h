@@ -13,9 +13,12 @@
 // half-head runs (NeoX).
 //
 // The rotation angles depend only on the token and the pair index j < hd/2, not on the
-// head, so each step the row's lanes compute the token's hd/2 (cos, sin) pairs once, in
-// FP64 (the position times an FP64 inverse frequency, FP64 sincos), round them to FP32 and
-// share them through LDS.  The inverse-frequency table itself (base^(-2i/count) per
+// head, so each step the row's lanes compute the token's hd/2 (cos, sin) pairs once and
+// share them through LDS.  The angle is the position times an FP64 inverse frequency,
+// reduced modulo 2*pi in FP64 (pi split in two parts), and its sine and cosine are taken
+// in FP32 on the reduced argument (|r| <= pi, where the FP32 routine is accurate to a few
+// ulp): as good as an FP64 sincos rounded to FP32 for this purpose, at a fraction of the
+// cost.  The inverse-frequency table itself (base^(-2i/count) per
 // frame / height / width channel group, with the YaRN blend) is built once per block.
 #pragma once
 
@@ -69,6 +72,11 @@ __device__ __forceinline__ void rope_weight8(const RopeParams& p, int vec, float
     unpack8(ld16(reinterpret_cast<const uint16_t*>(w) + 8 * i), e);
   }
 }
+
+// 2*pi as the sum of two doubles, and 1/(2*pi), for the FP64 argument reduction.
+constexpr double k2PiHi = 6.283185307179586232;
+constexpr double k2PiLo = 2.4492935982947064e-16;
+constexpr double kInv2Pi = 0.15915494309189535;
 
 template <int TPR, int VMAX, int NT, bool NEOX, bool FP8>
 __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
@@ -137,7 +145,7 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
     inv_v = 1.0f / *p.v_scale;
   }
   // cos and sin carry the attention factor (and, for FP8 outputs, 1/scale).
-  const double cs_mul = (double)p.af * (double)inv_qk;
+  const float cs_mul = (float)((double)p.af * (double)inv_qk);
 
   // This lane's units: byte offset of the first vector in the qkv row, class (0 Q, 1 K,
   // 2 V, 3 none), and the unit's index inside its head.
@@ -156,8 +164,9 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
     uoff[m] = ok ? (uint32_t)vec * 16u : kOutOfRange;
   }
 
-  const int64_t seq = (int64_t)p.ppf * p.pph * p.ppw;
-  const int64_t hw = (int64_t)p.pph * p.ppw;
+  // Token counts and patch grids stay below 2^31 (checked on the host): 32-bit index math.
+  const uint32_t seq = (uint32_t)p.ppf * p.pph * p.ppw;
+  const uint32_t hw = (uint32_t)p.pph * p.ppw;
   const double eps = (double)p.eps;
   int parity = 0;
   const int64_t stride = (int64_t)gridDim.x * Geom::PER_ITER;
@@ -180,16 +189,19 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
 
     // 2) The token's (cos, sin) table, computed by the row's lanes.
     {
-      const int64_t t = row % seq;
+      const uint32_t t = (uint32_t)row % seq;
       const double pf = (double)(t / hw);
-      const double ph = (double)((t / p.ppw) % p.pph);
-      const double pw = (double)(t % p.ppw);
+      const double ph = (double)((t / (uint32_t)p.ppw) % (uint32_t)p.pph);
+      const double pw = (double)(t % (uint32_t)p.ppw);
       float2* tab = cs + ((size_t)parity * G + geo.grp) * half;
       for (int j = lane; j < half; j += TPR) {
         const double pos = j < p.cf / 2 ? pf : (j < (p.cf + p.ch) / 2 ? ph : pw);
-        double sn, cn;
-        sincos(pos * freq[j], &sn, &cn);
-        tab[j] = make_float2((float)(cn * cs_mul), (float)(sn * cs_mul));
+        const double th = pos * freq[j];
+        const double k = rint(th * kInv2Pi);
+        const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, th));
+        float sn, cn;
+        sincosf((float)r, &sn, &cn);
+        tab[j] = make_float2(cn * cs_mul, sn * cs_mul);
       }
     }
 
