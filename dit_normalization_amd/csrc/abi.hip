@@ -658,6 +658,32 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
   return launch_fwd<IN_ADD, EPI_LN_MOD_BF16>(p, static_cast<hipStream_t>(stream));
 }
 
+// ------------------------------------------------------------------ RMSNorm + SiLU
+
+dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
+                                const float* scale, const void* x, int64_t x_stride,
+                                const void* w, int w_dtype, float w_bias, int64_t rows,
+                                int64_t hidden, float eps, dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (output_fp8 != 0 && output_fp8 != 1)
+    return fail(DN_ERR_DTYPE, "output_fp8 must be 0 or 1");
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
+  DN_CHECK(check_matrix(out, out_stride, hidden, output_fp8 ? 1 : 2, "out"));
+  DN_CHECK(check_weight(w, w_dtype));
+  if (output_fp8) DN_CHECK(check_f32(scale, "scale", true));
+  FwdParams p = base_params(rows, hidden, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  if (output_fp8) {
+    p.q = static_cast<uint8_t*>(out); p.sq = out_stride;
+    p.scale = scale;
+    return launch_fwd<IN_PLAIN, EPI_SILU_FP8>(p, static_cast<hipStream_t>(stream));
+  }
+  p.y = static_cast<uint16_t*>(out); p.sy = out_stride;
+  return launch_fwd<IN_PLAIN, EPI_SILU_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
 // ------------------------------------------------------------------ fused QK norm + RoPE
 
 dn_status dn_fused_qk_rmsnorm_rope(

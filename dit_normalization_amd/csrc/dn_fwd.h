@@ -8,6 +8,7 @@
 //            AdaRMSNorm (style scale/shift, gate copy) in BF16 or FP8
 //            LayerNorm: BF16 or static FP8 of n*gamma + beta | BF16 of the DiT modulation
 //            n*(1 + scale + scale_bias) + (shift + shift_bias)
+//            RMSNorm + SiLU: BF16 or static FP8 of y / (1 + exp(-y))
 // The LayerNorm epilogues also switch the row statistics from the sum of squares to the
 // FP64 pair (sum, sum of squares), from which mean and variance follow in one pass.
 //
@@ -37,10 +38,13 @@ namespace dn {
 enum InKind { IN_PLAIN = 0, IN_ADD = 1, IN_GATED = 2, IN_GATED_BIAS = 3 };
 enum EpiKind {
   EPI_BF16 = 0, EPI_FP8 = 1, EPI_FP8_BLOCK = 2, EPI_ADA_BF16 = 3, EPI_ADA_FP8 = 4,
-  EPI_LN_BF16 = 5, EPI_LN_FP8 = 6, EPI_LN_MOD_BF16 = 7
+  EPI_LN_BF16 = 5, EPI_LN_FP8 = 6, EPI_LN_MOD_BF16 = 7, EPI_SILU_BF16 = 8, EPI_SILU_FP8 = 9
 };
 
-constexpr bool epi_is_ln(int epi) { return epi >= EPI_LN_BF16; }
+constexpr bool epi_is_ln(int epi) {
+  return epi == EPI_LN_BF16 || epi == EPI_LN_FP8 || epi == EPI_LN_MOD_BF16;
+}
+constexpr bool epi_is_silu(int epi) { return epi == EPI_SILU_BF16 || epi == EPI_SILU_FP8; }
 constexpr bool in_is_gated(int in) { return in == IN_GATED || in == IN_GATED_BIAS; }
 // FP32 planes (16 bytes per column vector each) of per-column parameters staged in LDS:
 // the RMSNorm effective weight (2), LayerNorm gamma and beta (4), none for the modulation.
@@ -170,9 +174,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   constexpr bool kGatedIn = in_is_gated(IN);
   constexpr int kPlanes = fwd_weight_planes(EPI);
   constexpr int kStats = fwd_stats(EPI);
-  constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8 || EPI == EPI_LN_FP8);
+  constexpr bool kSilu = epi_is_silu(EPI);
+  constexpr bool kStaticFp8 = (EPI == EPI_FP8 || EPI == EPI_ADA_FP8 || EPI == EPI_LN_FP8 ||
+                               EPI == EPI_SILU_FP8);
   constexpr bool kFp8Out = (EPI == EPI_FP8 || EPI == EPI_FP8_BLOCK || EPI == EPI_ADA_FP8 ||
-                            EPI == EPI_LN_FP8);
+                            EPI == EPI_LN_FP8 || EPI == EPI_SILU_FP8);
   constexpr bool kDB = fwd_double_buffer(IN, EPI, VMAX, R, NT);
   // Rows are held packed (BF16 pairs) across the reduction and unpacked again for the
   // epilogue, halving their register footprint, except where the unpacked row fits
@@ -432,7 +438,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     rsrc_t ry[R], rq[R], rgo[R];
     uint32_t oy[R], oq[R], ogo[R];
     if constexpr (EPI == EPI_BF16 || EPI == EPI_ADA_BF16 || EPI == EPI_FP8_BLOCK ||
-                  EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16)
+                  EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16 || EPI == EPI_SILU_BF16)
       tensor_span<TPR, R, RPW>(p.y, p.sy, 2, 16, p.y ? row_bf16 : 0u, first,
                                p.y ? p.rows : first, lane, geo.j, lane_ok, ry, oy);
     if constexpr (kFp8Out)
@@ -522,10 +528,21 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
         }
+        if constexpr (kSilu) {
+          // SiLU(y) = y / (1 + e^-y), evaluated as (y or y e^y) / (1 + e^-|y|) so that the
+          // exponential never overflows (IEEE divide, accurate expf).
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float e = expf(-fabsf(yv[k]));
+            const float num = yv[k] >= 0.0f ? yv[k] : yv[k] * e;
+            yv[k] = num / (1.0f + e);
+          }
+        }
 
-        if constexpr (EPI == EPI_BF16 || EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16) {
+        if constexpr (EPI == EPI_BF16 || EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16 ||
+                      EPI == EPI_SILU_BF16) {
           bstore16(ry[rr], oy[rr] + d16, pack8(yv));
-        } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8) {
+        } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8 || EPI == EPI_SILU_FP8) {
           if constexpr (!kFold) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;

@@ -66,6 +66,8 @@ SIGNATURES = {
     "dn_fused_dit_residual_layernorm_scale_shift": (
         [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F32, _P, _I64, _F32, _I64, _I64, _F32,
          _P], _I32),
+    "dn_fused_rmsnorm_silu": ([_P, _I64, _I32, _P, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P],
+                              _I32),
     "dn_fused_qk_rmsnorm_rope": (
         [_P, _I64, _P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32,
          _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F64, _I32, _F64, _F64, _F64,
@@ -509,6 +511,25 @@ def dn_fused_dit_residual_layernorm_scale_shift(x, scale, shift, residual=None,
         _writeback(ro, ror)
     _writeback(n, nr)
     return ro, n
+
+
+def dn_fused_rmsnorm_silu(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=None,
+                          output_fp8: bool = False, scale=1.0):
+    """SiLU(RMSNorm(x, w)); BF16 out, or e4m3fn(SiLU(...) / scale) when output_fp8 (or when
+    `out` is a float8_e4m3fn tensor)."""
+    xr, rows, sx = _rows(x, "x")
+    H = xr.size(-1)
+    w, wcode = _weight(w)
+    fp8 = bool(output_fp8) or (out is not None and out.dtype == torch.float8_e4m3fn)
+    odt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    o = out if out is not None else _out_like(x, x.shape, odt)
+    orr, _, so = _rows(o, "out", odt)
+    s = _scale_tensor(scale, x.device) if fp8 else None
+    _check(lib.dn_fused_rmsnorm_silu(orr.data_ptr(), so, int(fp8), _ptr(s), xr.data_ptr(), sx,
+                                     w.data_ptr(), wcode, w_bias, rows, H, eps, _stream(x)),
+           "dn_fused_rmsnorm_silu")
+    _writeback(o, orr)
+    return o
 
 
 def dn_fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, num_heads_q: int, num_heads_k: int,

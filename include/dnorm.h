@@ -308,6 +308,21 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
     int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * fused_rmsnorm_silu   ([norm docs] API table: fused_rmsnorm_silu; [norm guide] §5.1)
+ *   y = (x * r) * FP32(w + w_bias) as rmsnorm (unrounded), s = y / (1 + exp(-y)) in FP32
+ *   (IEEE divide; the exponential is taken of -|y| so it never overflows).
+ *   output_fp8 == 0: out BF16 [rows, hidden] = BF16(s).
+ *   output_fp8 == 1: out e4m3fn [rows, hidden] = e4m3fn(s / *scale), scale a device FP32
+ *   [1] (the pages leave the FP8 scale open; pass 1.0 for a plain conversion).
+ *   The pages' NVFP4 output and the engine workspace of their implementation have no
+ *   counterpart here (no workspace is needed).
+ */
+dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
+                                const float* scale, const void* x, int64_t x_stride,
+                                const void* w, int w_dtype, float w_bias,
+                                int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * fused_qk_rmsnorm_rope   ([norm docs] API table: fused_qk_rmsnorm_rope; [norm guide] §5.2)
  *
  * qkv: BF16 [tokens, (nq + nk + nv) * head_dim] (row stride qkv_stride), heads in the
@@ -324,7 +339,8 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
  *     channels.  yarn_factor != 1 blends inv_freq / factor and inv_freq with
  *     ramp = clamp((i - yarn_low) / (yarn_high - yarn_low), 0, 1) (yarn_high == yarn_low
  *     takes yarn_high + 0.001).  (a, b) -> (a cos - b sin, a sin + b cos), with cos and
- *     sin times attention_factor; angles and sincos in FP64, then FP32.
+ *     sin times attention_factor.  Angles are formed and reduced modulo 2*pi in FP64; their
+ *     sine and cosine are evaluated in FP32 on the reduced argument.
  *   V: copied bit for bit.
  * Outputs q_out [tokens, nq*head_dim], k_out, v_out (each with its row stride): BF16
  * (output_fp8 == 0; one rounding of the FP32 result), or e4m3fn (output_fp8 == 1): Q and K

@@ -48,7 +48,7 @@ def test_header_declares_the_expected_calls():
               "dn_fused_dit_gate_residual_layernorm_gamma_beta",
               "dn_fused_dit_gate_residual_layernorm_scale_shift",
               "dn_fused_dit_residual_layernorm_scale_shift", "dn_fused_qk_rmsnorm_rope",
-              "dn_last_error"]:
+              "dn_fused_rmsnorm_silu", "dn_last_error"]:
         assert n in names
 
 
@@ -226,6 +226,16 @@ def test_qk_rope_checks(lib):
     assert rope(lib, fp8=1, qs=0) == E_NULL                        # FP8 needs its scales
     assert rope(lib, qkv_s=9208) == E_SHAPE                       # stride < width
     assert rope(lib, ch=(128, 0, 0), tokens=0) == OK              # empty groups allowed
+
+
+def test_silu_checks(lib):
+    f = lib.dn_fused_rmsnorm_silu
+    assert f(A, 512, 0, 0, B, 512, C, 0, 0.0, 0, 512, 1e-6, None) == OK
+    assert f(A, 512, 2, 0, B, 512, C, 0, 0.0, 4, 512, 1e-6, None) == E_DTYPE      # fp8 flag
+    assert f(A, 512, 1, 0, B, 512, C, 0, 0.0, 4, 512, 1e-6, None) == E_NULL       # FP8 scale
+    assert f(A, 512, 0, 0, B, 512, 0, 0, 0.0, 4, 512, 1e-6, None) == E_NULL       # weight
+    assert f(A, 512, 0, 0, B, 512, C, 0, 0.0, 4, 164, 1e-6, None) == E_UNSUP      # 164 % 8
+    assert f(A + 4, 160, 1, D, B, 160, C, 0, 0.0, 4, 160, 1e-6, None) == E_ALIGN  # fp8 base
 
 
 def test_force_threads_per_row(lib):

@@ -159,3 +159,17 @@ def qk_rope(ppf: int = 16, pph: int = 24, ppw: int = 32, batch: int = 1, nq: int
     }, {"eps": 1e-6, "tokens": tokens, "nq": nq, "nk": nk, "nv": nv, "head_dim": head_dim,
         "channels": tuple(channels), "ppf": ppf, "pph": pph, "ppw": ppw, "base": 10000.0,
         "output_scale": 0.05, "v_scale": 0.02})
+
+
+def rmsnorm_silu(tokens: int = 99840, hidden: int = 512, seed: int = 9) -> Workload:
+    """Fused RMSNorm + SiLU: x BF16 [tokens, hidden] ~ N(0,1), w BF16 ~ N(1, 0.1); FP8 scale
+    0.02.  The pages tune this op for a video VAE decoder over hidden sizes 64 ... 1024 and
+    1560 ... 399360 tokens."""
+    return Workload("rmsnorm_silu", {
+        "x": normal((tokens, hidden), seed, 0),
+        "w": normal((hidden,), seed, 1, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "tokens": tokens, "hidden": hidden, "scale": 0.02})
+
+
+SILU_HIDDEN = (64, 128, 160, 256, 320, 512, 640, 1024)
+SILU_TOKENS = (1560, 6240, 24960, 99840, 399360)
