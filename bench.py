@@ -31,7 +31,8 @@ dispatch belongs to the step.  Profiler summaries (host only, no GPU):
 layernorm and layernorm_quant on BF16 [8192, 4096], and the three DiT gate/residual +
 LayerNorm modes on BF16 [16384, 3072] with gate/scale/shift read as row-stride-6*hidden
 chunks of one per-token modulation tensor.  `--family qk_rope` times the fused QK
-RMSNorm + 3-D RoPE + V copy on qkv BF16 [12288, 9216] (both pairings, BF16 and e4m3fn).
+RMSNorm + 3-D RoPE + V copy on qkv BF16 [12288, 9216] (both pairings, BF16 and e4m3fn);
+`--family silu` the fused RMSNorm + SiLU at three video-VAE shapes.
 """
 from __future__ import annotations
 
@@ -445,6 +446,34 @@ def run_qk_rope_family(a) -> int:
                        f"patches {p['ppf']}x{p['pph']}x{p['ppw']}), BF16 or e4m3fn q/k/v out")
 
 
+def run_silu_family(a) -> int:
+    """fused_rmsnorm_silu at three of the pages' video-VAE shapes, BF16 and e4m3fn out."""
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating RMSNorm + SiLU inputs", file=sys.stderr, flush=True)
+    calls, ab = {}, {}
+    scale = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    for T, H in ((399360, 128), (99840, 512), (24960, 1024)):
+        wl = W.rmsnorm_silu(T, H)
+        x, w = wl.tensors["x"].to(dev), wl.tensors["w"].to(dev)
+        ob = torch.empty_like(x)
+        o8 = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev)
+        calls[f"silu_bf16_{T}x{H}"] = (lambda x=x, w=w, ob=ob: dn.dn_fused_rmsnorm_silu(
+            x, w, 1e-6, out=ob))
+        calls[f"silu_fp8_{T}x{H}"] = (lambda x=x, w=w, o8=o8: dn.dn_fused_rmsnorm_silu(
+            x, w, 1e-6, out=o8, scale=scale))
+        ab[f"silu_bf16_{T}x{H}"] = 4 * T * H + 2 * H
+        ab[f"silu_fp8_{T}x{H}"] = 3 * T * H + 2 * H + 4
+    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused RMSNorm + SiLU",
+                       "fused_rmsnorm_silu BF16 [399360,128], [99840,512], [24960,1024]; "
+                       "BF16 or e4m3fn out")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,9 +485,11 @@ def main(argv=None) -> int:
                          "library dispatch is then a bench-step kernel)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", metavar="STATS_CSV")
-    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope"), default="rmsnorm",
+    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope", "silu"),
+                    default="rmsnorm",
                     help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm "
-                         "family; qk_rope: the fused QK RMSNorm + 3-D RoPE")
+                         "family; qk_rope: the fused QK RMSNorm + 3-D RoPE; silu: the fused "
+                         "RMSNorm + SiLU")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
@@ -484,6 +515,8 @@ def main(argv=None) -> int:
         return run_layernorm_family(a)
     if a.family == "qk_rope":
         return run_qk_rope_family(a)
+    if a.family == "silu":
+        return run_silu_family(a)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)

@@ -54,6 +54,8 @@ constexpr int fwd_weight_planes(int epi) {
 // FP64 statistics a row reduces: sum of squares, plus the sum for LayerNorm.
 constexpr int fwd_stats(int epi) { return epi_is_ln(epi) ? 2 : 1; }
 
+constexpr float kLog2E = 1.44269504088896341f;   // log2(e), rounded to FP32
+
 struct FwdParams {
   const uint16_t* x;     int64_t sx;
   const uint16_t* r;     int64_t sr;     // residual (IN_ADD, gated inputs)
@@ -529,13 +531,28 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
         }
         if constexpr (kSilu) {
-          // SiLU(y) = y / (1 + e^-y), evaluated as (y or y e^y) / (1 + e^-|y|) so that the
-          // exponential never overflows (IEEE divide, accurate expf).
+          // SiLU(y) = y / (1 + e^-y), evaluated as (y or y e^y) * 1/(1 + e^-|y|) so that the
+          // exponential never overflows.  e^-|y| = 2^(-|y| log2 e) on the hardware exp2
+          // (v_exp_f32, < 0.75 ulp on normal results, measured) and the reciprocal on
+          // v_rcp_f32 (< 0.9 ulp): together within (|y| + 5) FP32 ulps of SiLU(y).  v_exp_f32
+          // flushes results below 2^-126 to zero, so rows with |y| > 80 take the accurate
+          // library exponential instead.
+          float e[8];
+          float amax = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const float e = expf(-fabsf(yv[k]));
-            const float num = yv[k] >= 0.0f ? yv[k] : yv[k] * e;
-            yv[k] = num / (1.0f + e);
+            const float ay = fabsf(yv[k]);
+            amax = fmaxf(amax, ay);
+            e[k] = __builtin_amdgcn_exp2f(-ay * kLog2E);
+          }
+          if (amax > 80.0f) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = expf(-fabsf(yv[k]));
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float num = yv[k] >= 0.0f ? yv[k] : yv[k] * e[k];
+            yv[k] = num * __builtin_amdgcn_rcpf(1.0f + e[k]);
           }
         }
 

@@ -309,8 +309,9 @@ dn_status dn_fused_dit_residual_layernorm_scale_shift(
 
 /* ---------------------------------------------------------------------------------------
  * fused_rmsnorm_silu   ([norm docs] API table: fused_rmsnorm_silu; [norm guide] §5.1)
- *   y = (x * r) * FP32(w + w_bias) as rmsnorm (unrounded), s = y / (1 + exp(-y)) in FP32
- *   (IEEE divide; the exponential is taken of -|y| so it never overflows).
+ *   y = (x * r) * FP32(w + w_bias) as rmsnorm (unrounded), s = y / (1 + exp(-y)) in FP32:
+ *   (y or y*e) * (1/(1 + e)) with e = exp(-|y|) (no overflow) on the hardware exp2 and
+ *   reciprocal, within (|y| + 5) FP32 ulps of the exact SiLU of y.
  *   output_fp8 == 0: out BF16 [rows, hidden] = BF16(s).
  *   output_fp8 == 1: out e4m3fn [rows, hidden] = e4m3fn(s / *scale), scale a device FP32
  *   [1] (the pages leave the FP8 scale open; pass 1.0 for a plain conversion).
