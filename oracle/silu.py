@@ -52,3 +52,35 @@ def fused_rmsnorm_silu_fp8(x, w, scale: float, eps: float = 1e-6, bias: float = 
 
 
 __all__ = ["silu", "fused_rmsnorm_silu", "fused_rmsnorm_silu_fp8", "RMSNormSilu", "Quant"]
+
+
+def sigmoid(g) -> np.ndarray:
+    """1 / (1 + exp(-g)) in FP64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
+
+
+@dataclass
+class SigmoidGate:
+    o_exact: np.ndarray      # RMSNorm(x) * w * sigmoid(gate)
+    o: np.ndarray            # BF16, written over x
+    mag: np.ndarray          # |o| * (2 + |gate|): the gate's exponential carries |g| ulps
+    rstd: np.ndarray
+
+
+def rmsnorm_sigmoid_gate(x, gate, w=None, eps: float = 1e-6, bias: float = 0.0) -> SigmoidGate:
+    """Per-head RMSNorm and sigmoid gate (norm docs, Fixed-Width Fused Norms:
+    rmsnorm_sigmoid_gate).  Reading: rows are heads ([tokens*heads, head_dim]); the head
+    is normalised as rmsnorm (weight [head_dim], ones when absent) and multiplied element by
+    element by sigmoid(gate) of the same shape; the result replaces x."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    ww = np.ones(hd) if w is None else np.asarray(w, dtype=np.float64)
+    n = rmsnorm(x.reshape(-1, hd), ww, bias, eps)
+    g = np.asarray(gate, dtype=np.float64).reshape(-1, hd)
+    o = n.y_exact * sigmoid(g)
+    return SigmoidGate(o, bf16_round(o), np.abs(o) * (2.0 + np.abs(g)), n.rstd)
+
+
+__all__ += ["sigmoid", "rmsnorm_sigmoid_gate", "SigmoidGate"]

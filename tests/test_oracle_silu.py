@@ -41,3 +41,23 @@ def test_fp8_matches_torch_cast():
     ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     ok = np.abs(v) < 448
     assert (F.codes_equal_e4m3(q.q, ref) | q.tie | ~ok).all()
+
+
+def test_sigmoid_gate_matches_torch_and_identities():
+    x = F.bf16_round(RNG.normal(0, 1, (40, 64)))
+    g = F.bf16_round(RNG.normal(0, 3, (40, 64)))
+    w = F.bf16_round(RNG.normal(1, 0.1, 64))
+    r = S.rmsnorm_sigmoid_gate(x, g, w, 1e-6)
+    n = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), weight=torch.from_numpy(w),
+                                     eps=float(np.float32(1e-6)))
+    ref = (n * torch.sigmoid(torch.from_numpy(g))).numpy()
+    np.testing.assert_allclose(r.o_exact, ref, rtol=1e-12, atol=1e-14)
+    # gate 0 halves the norm exactly; gates g and -g add up to the norm
+    half = S.rmsnorm_sigmoid_gate(x, np.zeros_like(g), w, 1e-6)
+    np.testing.assert_array_equal(half.o_exact, n.numpy() * 0.5)
+    neg = S.rmsnorm_sigmoid_gate(x, -g, w, 1e-6)
+    np.testing.assert_allclose(r.o_exact + neg.o_exact, n.numpy(), rtol=1e-13, atol=1e-13)
+    # no weight = ones
+    none = S.rmsnorm_sigmoid_gate(x, g, None, 1e-6)
+    ones = S.rmsnorm_sigmoid_gate(x, g, np.ones(64), 1e-6)
+    assert (none.o_exact == ones.o_exact).all()
