@@ -189,7 +189,8 @@ dn_status launch_fwd(FwdParams p, hipStream_t stream) {
     return fail(DN_ERR_HIP, "no kernel instance for tier %d", tier);
   int capacity = 0;
   constexpr bool single_stream = IN == IN_PLAIN && EPI != EPI_ADA_BF16 &&
-                                 EPI != EPI_ADA_FP8 && EPI != EPI_LN_MOD_BF16;
+                                 EPI != EPI_ADA_FP8 && EPI != EPI_LN_MOD_BF16 &&
+                                 EPI != EPI_SIGMOID_GATE;
   DN_CHECK(resident_blocks(kernel, s.nt, lds,
                            single_stream ? DN_BLOCKS_PER_CU_SINGLE : DN_BLOCKS_PER_CU, &capacity));
   const int64_t per_iter = (int64_t)g * s.r;
@@ -682,6 +683,25 @@ dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
   }
   p.y = static_cast<uint16_t*>(out); p.sy = out_stride;
   return launch_fwd<IN_PLAIN, EPI_SILU_BF16>(p, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ RMSNorm * sigmoid(gate)
+
+dn_status dn_rmsnorm_sigmoid_gate(void* x, int64_t x_stride, const void* gate,
+                                  int64_t gate_stride, const void* w, int w_dtype, float w_bias,
+                                  int64_t rows, int64_t head_dim, float eps,
+                                  dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, head_dim, 8, "head_dim"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(x, x_stride, head_dim, 2, "x"));
+  DN_CHECK(check_matrix(gate, gate_stride, head_dim, 2, "gate"));
+  if (w) DN_CHECK(check_weight(w, w_dtype));
+  FwdParams p = base_params(rows, head_dim, eps);
+  p.x = static_cast<const uint16_t*>(x); p.sx = x_stride;
+  p.y = static_cast<uint16_t*>(x); p.sy = x_stride;
+  p.gate = static_cast<const uint16_t*>(gate); p.sg = gate_stride;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  return launch_fwd<IN_PLAIN, EPI_SIGMOID_GATE>(p, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ fused QK norm + RoPE

@@ -9,6 +9,7 @@
 //            LayerNorm: BF16 or static FP8 of n*gamma + beta | BF16 of the DiT modulation
 //            n*(1 + scale + scale_bias) + (shift + shift_bias)
 //            RMSNorm + SiLU: BF16 or static FP8 of y / (1 + exp(-y))
+//            RMSNorm * sigmoid(gate): BF16 of y / (1 + exp(-gate)), gate an extra row tensor
 // The LayerNorm epilogues also switch the row statistics from the sum of squares to the
 // FP64 pair (sum, sum of squares), from which mean and variance follow in one pass.
 //
@@ -38,7 +39,8 @@ namespace dn {
 enum InKind { IN_PLAIN = 0, IN_ADD = 1, IN_GATED = 2, IN_GATED_BIAS = 3 };
 enum EpiKind {
   EPI_BF16 = 0, EPI_FP8 = 1, EPI_FP8_BLOCK = 2, EPI_ADA_BF16 = 3, EPI_ADA_FP8 = 4,
-  EPI_LN_BF16 = 5, EPI_LN_FP8 = 6, EPI_LN_MOD_BF16 = 7, EPI_SILU_BF16 = 8, EPI_SILU_FP8 = 9
+  EPI_LN_BF16 = 5, EPI_LN_FP8 = 6, EPI_LN_MOD_BF16 = 7, EPI_SILU_BF16 = 8, EPI_SILU_FP8 = 9,
+  EPI_SIGMOID_GATE = 10
 };
 
 constexpr bool epi_is_ln(int epi) {
@@ -83,6 +85,11 @@ struct FwdParams {
 
 // Effective weight FP32(w + bias) of one 16-byte column vector, read from global memory.
 __device__ __forceinline__ void load_weff8(const FwdParams& p, int vec, float e[8]) {
+  if (!p.w) {   // no weight: ones
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = 1.0f + p.w_bias;
+    return;
+  }
   if (p.w_f32) {
     const float4* w = reinterpret_cast<const float4*>(p.w) + 2 * vec;
     const float4 a = w[0], b = w[1];
@@ -155,7 +162,7 @@ constexpr bool fwd_double_buffer(int in, int epi, int vmax, int r, int nt) {
 #endif
   const int tensors = 1 + (in != IN_PLAIN) + in_is_gated(in) +
                       3 * (epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8) +
-                      2 * (epi == EPI_LN_MOD_BF16);
+                      2 * (epi == EPI_LN_MOD_BF16) + (epi == EPI_SIGMOID_GATE);
   const int step = tensors * 4 * vmax * r;
   const int budget = nt >= 1024 ? 128 : 256;
   return 2 * step + 96 <= budget;
@@ -174,6 +181,8 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   constexpr bool kLN = epi_is_ln(EPI);
   constexpr bool kMod = (EPI == EPI_LN_MOD_BF16);
   constexpr bool kGatedIn = in_is_gated(IN);
+  constexpr bool kSigGate = (EPI == EPI_SIGMOID_GATE);
+  constexpr bool kLoadGate = kGatedIn || kSigGate;
   constexpr int kPlanes = fwd_weight_planes(EPI);
   constexpr int kStats = fwd_stats(EPI);
   constexpr bool kSilu = epi_is_silu(EPI);
@@ -271,7 +280,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     if constexpr (IN != IN_PLAIN)
       tensor_span<TPR, R, RPW>(p.r, p.sr, 2, 16, row_bf16, first, p.rows, lane, geo.j,
                                lane_ok, rres, ores);
-    if constexpr (kGatedIn)
+    if constexpr (kLoadGate)
       tensor_span<TPR, R, RPW>(p.gate, p.sg, 2, 16, row_bf16, first, p.rows, lane, geo.j,
                                lane_ok, rg, og);
     if constexpr (kMod) {
@@ -300,7 +309,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const uint32_t dv = (uint32_t)(v * TPR * 16);
         st.a[rr][v] = bload16(rx[rr], ox[rr] + dv);
         if constexpr (IN != IN_PLAIN) st.b[rr][v] = bload16(rres[rr], ores[rr] + dv);
-        if constexpr (kGatedIn) st.c[rr][v] = bload16(rg[rr], og[rr] + dv);
+        if constexpr (kLoadGate) st.c[rr][v] = bload16(rg[rr], og[rr] + dv);
         if constexpr (kMod) {
           st.ssc[rr][v] = bload16(rsc[rr], osc[rr] + dv);
           st.ssh[rr][v] = bload16(rsh[rr], osh[rr] + dv);
@@ -440,7 +449,8 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     rsrc_t ry[R], rq[R], rgo[R];
     uint32_t oy[R], oq[R], ogo[R];
     if constexpr (EPI == EPI_BF16 || EPI == EPI_ADA_BF16 || EPI == EPI_FP8_BLOCK ||
-                  EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16 || EPI == EPI_SILU_BF16)
+                  EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16 || EPI == EPI_SILU_BF16 ||
+                  EPI == EPI_SIGMOID_GATE)
       tensor_span<TPR, R, RPW>(p.y, p.sy, 2, 16, p.y ? row_bf16 : 0u, first,
                                p.y ? p.rows : first, lane, geo.j, lane_ok, ry, oy);
     if constexpr (kFp8Out)
@@ -556,8 +566,31 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           }
         }
 
+        if constexpr (kSigGate) {
+          // y * sigmoid(g), sigmoid(g) = (1 or e) / (1 + e) with e = exp(-|g|), on the
+          // hardware exp2 and reciprocal as in the SiLU epilogue (library exp for |g| > 80).
+          float fg[8], e[8];
+          unpack8(st.c[rr][v], fg);
+          float amax = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float ag = fabsf(fg[k]);
+            amax = fmaxf(amax, ag);
+            e[k] = __builtin_amdgcn_exp2f(-ag * kLog2E);
+          }
+          if (amax > 80.0f) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = expf(-fabsf(fg[k]));
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float sg = (fg[k] >= 0.0f ? 1.0f : e[k]) * __builtin_amdgcn_rcpf(1.0f + e[k]);
+            yv[k] *= sg;
+          }
+        }
+
         if constexpr (EPI == EPI_BF16 || EPI == EPI_LN_BF16 || EPI == EPI_LN_MOD_BF16 ||
-                      EPI == EPI_SILU_BF16) {
+                      EPI == EPI_SILU_BF16 || EPI == EPI_SIGMOID_GATE) {
           bstore16(ry[rr], oy[rr] + d16, pack8(yv));
         } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8 || EPI == EPI_SILU_FP8) {
           if constexpr (!kFold) {
@@ -653,7 +686,7 @@ constexpr int kFwdAutoTiers = 11;   // tiers the automatic choice considers
 // at 6.
 constexpr int fwd_vmax_limit(int in, int epi) {
   return (in_is_gated(in) || epi == EPI_ADA_BF16 || epi == EPI_ADA_FP8 ||
-          epi == EPI_LN_MOD_BF16) ? 6 : 16;
+          epi == EPI_LN_MOD_BF16 || epi == EPI_SIGMOID_GATE) ? 6 : 16;
 }
 
 }  // namespace dn

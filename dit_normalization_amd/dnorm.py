@@ -68,6 +68,7 @@ SIGNATURES = {
          _P], _I32),
     "dn_fused_rmsnorm_silu": ([_P, _I64, _I32, _P, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P],
                               _I32),
+    "dn_rmsnorm_sigmoid_gate": ([_P, _I64, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
     "dn_fused_qk_rmsnorm_rope": (
         [_P, _I64, _P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32,
          _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F64, _I32, _F64, _F64, _F64,
@@ -530,6 +531,22 @@ def dn_fused_rmsnorm_silu(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=N
            "dn_fused_rmsnorm_silu")
     _writeback(o, orr)
     return o
+
+
+def dn_rmsnorm_sigmoid_gate(x, gate, eps: float = 1e-6, *, weight=None, w_bias: float = 0.0):
+    """In place: x <- BF16(RMSNorm(x) * w * sigmoid(gate)) per head row (x [..., head_dim],
+    gate of x's shape).  Returns x."""
+    xr, rows, sx = _rows(x, "x")
+    if xr.data_ptr() != x.data_ptr():
+        raise DnormError("rmsnorm_sigmoid_gate works in place: x needs a row-addressable layout")
+    hd = xr.size(-1)
+    gr, grows, sg = _rows(gate, "gate")
+    if grows != rows or gr.size(-1) != hd:
+        raise DnormError("gate must have x's shape")
+    w, wcode = (None, DN_WEIGHT_BF16) if weight is None else _weight(weight)
+    _check(lib.dn_rmsnorm_sigmoid_gate(xr.data_ptr(), sx, gr.data_ptr(), sg, _ptr(w), wcode, w_bias,
+                                       rows, hd, eps, _stream(x)), "dn_rmsnorm_sigmoid_gate")
+    return x
 
 
 def dn_fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, num_heads_q: int, num_heads_k: int,

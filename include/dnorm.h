@@ -324,6 +324,21 @@ dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
                                 int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * rmsnorm_sigmoid_gate   ([norm docs] Fixed-Width Fused Norms: rmsnorm_sigmoid_gate)
+ *   The pages name only "per-head RMSNorm and sigmoid gate, in place, for head dim 64";
+ *   the reading implemented: rows are heads (a [tokens, heads, head_dim] tensor passed as
+ *   rows = tokens*heads), y = (x * r) * FP32(w + w_bias) as rmsnorm, then
+ *   x <- BF16(y * sigmoid(gate)), gate BF16 of x's shape (own row stride).  w: BF16 or FP32
+ *   [head_dim], or NULL for ones.  sigmoid(g) = (1 or e) * 1/(1 + e), e = exp(-|g|), on the
+ *   hardware exp2 and reciprocal (within (|g| + 5) FP32 ulps).  Any head_dim that is a
+ *   multiple of 8 is accepted (the pages' kernel takes 64 only).
+ */
+dn_status dn_rmsnorm_sigmoid_gate(void* x, int64_t x_stride, const void* gate,
+                                  int64_t gate_stride, const void* w, int w_dtype,
+                                  float w_bias, int64_t rows, int64_t head_dim, float eps,
+                                  dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * fused_qk_rmsnorm_rope   ([norm docs] API table: fused_qk_rmsnorm_rope; [norm guide] §5.2)
  *
  * qkv: BF16 [tokens, (nq + nk + nv) * head_dim] (row stride qkv_stride), heads in the

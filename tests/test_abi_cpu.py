@@ -48,7 +48,7 @@ def test_header_declares_the_expected_calls():
               "dn_fused_dit_gate_residual_layernorm_gamma_beta",
               "dn_fused_dit_gate_residual_layernorm_scale_shift",
               "dn_fused_dit_residual_layernorm_scale_shift", "dn_fused_qk_rmsnorm_rope",
-              "dn_fused_rmsnorm_silu", "dn_last_error"]:
+              "dn_fused_rmsnorm_silu", "dn_rmsnorm_sigmoid_gate", "dn_last_error"]:
         assert n in names
 
 
@@ -236,6 +236,15 @@ def test_silu_checks(lib):
     assert f(A, 512, 0, 0, B, 512, 0, 0, 0.0, 4, 512, 1e-6, None) == E_NULL       # weight
     assert f(A, 512, 0, 0, B, 512, C, 0, 0.0, 4, 164, 1e-6, None) == E_UNSUP      # 164 % 8
     assert f(A + 4, 160, 1, D, B, 160, C, 0, 0.0, 4, 160, 1e-6, None) == E_ALIGN  # fp8 base
+
+
+def test_sigmoid_gate_checks(lib):
+    f = lib.dn_rmsnorm_sigmoid_gate
+    assert f(A, 64, B, 64, 0, 0, 0.0, 0, 64, 1e-6, None) == OK
+    assert f(A, 64, 0, 64, 0, 0, 0.0, 4, 64, 1e-6, None) == E_NULL          # gate
+    assert f(A, 64, B, 64, C, 5, 0.0, 4, 64, 1e-6, None) == E_DTYPE         # weight dtype
+    assert f(A, 64, B, 60, 0, 0, 0.0, 4, 64, 1e-6, None) == E_SHAPE         # gate stride
+    assert f(A, 64, B, 64, C + 2, 0, 0.0, 4, 64, 1e-6, None) == E_ALIGN     # weight base
 
 
 def test_force_threads_per_row(lib):

@@ -173,3 +173,15 @@ def rmsnorm_silu(tokens: int = 99840, hidden: int = 512, seed: int = 9) -> Workl
 
 SILU_HIDDEN = (64, 128, 160, 256, 320, 512, 640, 1024)
 SILU_TOKENS = (1560, 6240, 24960, 99840, 399360)
+
+
+def sigmoid_gate(tokens: int = 16384, heads: int = 64, head_dim: int = 64,
+                 seed: int = 10) -> Workload:
+    """Per-head RMSNorm + sigmoid gate: x, gate BF16 [tokens, heads*head_dim] ~ N(0,1) and
+    N(0, 2); w BF16 [head_dim] ~ N(1, 0.1).  Head dim 64 is the pages' width; 64 heads of
+    64 make a 4096-wide attention output."""
+    return Workload("sigmoid_gate", {
+        "x": normal((tokens, heads * head_dim), seed, 0),
+        "gate": normal((tokens, heads * head_dim), seed, 1, std=2.0),
+        "w": normal((head_dim,), seed, 2, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "tokens": tokens, "heads": heads, "head_dim": head_dim})
