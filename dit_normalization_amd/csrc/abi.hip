@@ -685,6 +685,88 @@ dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
   return launch_fwd<IN_PLAIN, EPI_SILU_BF16>(p, static_cast<hipStream_t>(stream));
 }
 
+// ------------------------------------------------------------------ gated-residual RMSNorm
+
+namespace {
+
+dn_status gres_common(void* next_out, int64_t next_out_stride, void* residual,
+                      int64_t residual_stride, const void* branch, int64_t branch_stride,
+                      const void* gate, int64_t gate_stride, int64_t gate_rows, const void* w,
+                      int w_dtype, float w_bias, const void* w_next, int w_next_dtype,
+                      float w_next_bias, int64_t rows, int64_t hidden, float eps, bool next,
+                      hipStream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_matrix(residual, residual_stride, hidden, 2, "residual"));
+  DN_CHECK(check_matrix(branch, branch_stride, hidden, 2, "branch"));
+  if (gate_rows != 1 && gate_rows != rows)
+    return fail(DN_ERR_SHAPE, "gate_rows must be 1 or rows (%lld), got %lld", (long long)rows,
+                (long long)gate_rows);
+  DN_CHECK(check_matrix(gate, gate_stride, hidden, 2, "gate"));
+  DN_CHECK(check_weight(w, w_dtype));
+  if (next) {
+    DN_CHECK(check_matrix(next_out, next_out_stride, hidden, 2, "out"));
+    DN_CHECK(check_weight(w_next, w_next_dtype));
+  }
+  GresParams p{};
+  p.b = static_cast<const uint16_t*>(branch); p.sb = branch_stride;
+  p.r = static_cast<uint16_t*>(residual); p.sr = residual_stride;
+  p.g = static_cast<const uint16_t*>(gate); p.sg = gate_stride; p.g_bcast = gate_rows == 1;
+  p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
+  p.w2 = w_next; p.w2_f32 = w_next_dtype == DN_WEIGHT_F32; p.w2_bias = w_next_bias;
+  p.y = static_cast<uint16_t*>(next_out); p.sy = next_out_stride;
+  p.rows = rows;
+  p.hidden = (int)hidden;
+  p.nvec = (int)(hidden / 8);
+  p.eps = eps;
+  p.w_in_lds = p.nvec <= kMaxLdsWeightVectors;
+  const int tier = pick_fwd_tier(p.nvec, 6, g_force_tpr.load());
+  if (tier < 0) return fail(DN_ERR_SHAPE, "hidden %lld is too wide", (long long)hidden);
+  const TierShape s = fwd_tier_shape(tier);
+  const int g = s.nt / s.tpr;
+  const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;
+  const size_t lds = gres_lds_bytes(p.nvec, p.w_in_lds, next, g, wpr, s.r);
+  auto launch = [&](int grid, hipStream_t st, const void** k) -> hipError_t {
+    return next ? gres_launch<true>(p, tier, grid, lds, st, k)
+                : gres_launch<false>(p, tier, grid, lds, st, k);
+  };
+  const void* kernel = nullptr;
+  if (launch(0, nullptr, &kernel) != hipSuccess || !kernel)
+    return fail(DN_ERR_HIP, "no kernel instance for tier %d", tier);
+  int capacity = 0;
+  DN_CHECK(resident_blocks(kernel, s.nt, lds, DN_BLOCKS_PER_CU, &capacity));
+  const int64_t per_iter = (int64_t)g * s.r;
+  const int64_t needed = (rows + per_iter - 1) / per_iter;
+  const int grid = (int)(needed < capacity ? needed : capacity);
+  const hipError_t e = launch(grid > 0 ? grid : 1, stream, nullptr);
+  if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return DN_OK;
+}
+
+}  // namespace
+
+dn_status dn_gated_residual_rmsnorm(void* residual, int64_t residual_stride,
+                                    const void* branch, int64_t branch_stride,
+                                    const void* gate, int64_t gate_stride, int64_t gate_rows,
+                                    const void* w, int w_dtype, float w_bias, int64_t rows,
+                                    int64_t hidden, float eps, dn_stream_t stream) {
+  return gres_common(nullptr, 0, residual, residual_stride, branch, branch_stride, gate,
+                     gate_stride, gate_rows, w, w_dtype, w_bias, nullptr, 0, 0.0f, rows, hidden,
+                     eps, false, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_gated_residual_next_rmsnorm(void* out, int64_t out_stride, void* residual,
+                                         int64_t residual_stride, const void* branch,
+                                         int64_t branch_stride, const void* gate,
+                                         int64_t gate_stride, int64_t gate_rows, const void* w,
+                                         int w_dtype, float w_bias, const void* w_next,
+                                         int w_next_dtype, float w_next_bias, int64_t rows,
+                                         int64_t hidden, float eps, dn_stream_t stream) {
+  return gres_common(out, out_stride, residual, residual_stride, branch, branch_stride, gate,
+                     gate_stride, gate_rows, w, w_dtype, w_bias, w_next, w_next_dtype,
+                     w_next_bias, rows, hidden, eps, true, static_cast<hipStream_t>(stream));
+}
+
 // ------------------------------------------------------------------ RMSNorm * sigmoid(gate)
 
 dn_status dn_rmsnorm_sigmoid_gate(void* x, int64_t x_stride, const void* gate,

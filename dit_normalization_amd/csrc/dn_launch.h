@@ -6,6 +6,7 @@
 
 #include "dn_bwd.h"
 #include "dn_fwd.h"
+#include "dn_gres.h"
 #include "dn_rope.h"
 
 namespace dn {
@@ -55,6 +56,11 @@ inline TierShape rope_tier_shape(int tier) {
 // Launch one fused QK RMSNorm + RoPE kernel instance (or return its address).
 template <bool NEOX, bool FP8>
 hipError_t rope_launch(const RopeParams& p, int tier, int grid, size_t lds, hipStream_t s,
+                       const void** kernel_out);
+
+// Launch one gated-residual RMSNorm kernel instance (forward tier table, VMAX <= 6).
+template <bool NEXT>
+hipError_t gres_launch(const GresParams& p, int tier, int grid, size_t lds, hipStream_t s,
                        const void** kernel_out);
 
 hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStream_t s,

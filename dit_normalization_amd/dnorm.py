@@ -68,6 +68,11 @@ SIGNATURES = {
          _P], _I32),
     "dn_fused_rmsnorm_silu": ([_P, _I64, _I32, _P, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P],
                               _I32),
+    "dn_gated_residual_rmsnorm": (
+        [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
+    "dn_gated_residual_next_rmsnorm": (
+        [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I32, _F32, _P, _I32, _F32, _I64, _I64,
+         _F32, _P], _I32),
     "dn_rmsnorm_sigmoid_gate": ([_P, _I64, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
     "dn_fused_qk_rmsnorm_rope": (
         [_P, _I64, _P, _I64, _P, _I64, _I32, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I32,
@@ -531,6 +536,47 @@ def dn_fused_rmsnorm_silu(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=N
            "dn_fused_rmsnorm_silu")
     _writeback(o, orr)
     return o
+
+
+def _gres_args(branch, residual, gate, w):
+    br, rows, sb = _rows(branch, "branch")
+    rr, rrows, sr = _rows(residual, "residual")
+    if rr.data_ptr() != residual.data_ptr():
+        raise DnormError("residual is updated in place: it needs a row-addressable layout")
+    if rrows != rows or rr.size(-1) != br.size(-1):
+        raise DnormError("branch and residual must have the same shape")
+    gr, grows, sg = _rows(gate, "gate")
+    if gr.size(-1) != br.size(-1) or grows not in (1, rows):
+        raise DnormError("gate must be [hidden], [1, hidden] or branch-shaped")
+    w, wcode = _weight(w)
+    return br, rows, sb, rr, sr, gr, grows, sg, w, wcode
+
+
+def dn_gated_residual_rmsnorm(branch, residual, gate, w, eps: float = 1e-6, *,
+                              w_bias: float = 0.0):
+    """residual <- BF16(residual + gate * RMSNorm(branch, w)) in place; returns residual.
+    gate: one row per token, or a single row ([hidden]) shared by every token."""
+    br, rows, sb, rr, sr, gr, grows, sg, w, wcode = _gres_args(branch, residual, gate, w)
+    _check(lib.dn_gated_residual_rmsnorm(rr.data_ptr(), sr, br.data_ptr(), sb, gr.data_ptr(), sg,
+                                         grows, w.data_ptr(), wcode, w_bias, rows, br.size(-1),
+                                         eps, _stream(branch)), "dn_gated_residual_rmsnorm")
+    return residual
+
+
+def dn_gated_residual_next_rmsnorm(branch, residual, gate, w, w_next, eps: float = 1e-6, *,
+                                   w_bias: float = 0.0, w_next_bias: float = 0.0, out=None):
+    """As dn_gated_residual_rmsnorm, then out = RMSNorm(residual, w_next) in the same launch;
+    returns (residual, out)."""
+    br, rows, sb, rr, sr, gr, grows, sg, w, wcode = _gres_args(branch, residual, gate, w)
+    w2, wcode2 = _weight(w_next)
+    o = out if out is not None else _out_like(branch, branch.shape, torch.bfloat16)
+    orr, _, so = _rows(o, "out")
+    _check(lib.dn_gated_residual_next_rmsnorm(
+        orr.data_ptr(), so, rr.data_ptr(), sr, br.data_ptr(), sb, gr.data_ptr(), sg, grows,
+        w.data_ptr(), wcode, w_bias, w2.data_ptr(), wcode2, w_next_bias, rows, br.size(-1), eps,
+        _stream(branch)), "dn_gated_residual_next_rmsnorm")
+    _writeback(o, orr)
+    return residual, o
 
 
 def dn_rmsnorm_sigmoid_gate(x, gate, eps: float = 1e-6, *, weight=None, w_bias: float = 0.0):

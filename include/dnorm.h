@@ -324,6 +324,36 @@ dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
                                 int64_t rows, int64_t hidden, float eps, dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * gated_residual_rmsnorm / gated_residual_next_rmsnorm
+ *   ([norm docs] Fixed-Width Fused Norms: "blend a normalized branch into the stream";
+ *    "plus the next RMSNorm in one launch")
+ *   The pages give no formula; the reading implemented:
+ *     n = (branch * r_b) * FP32(w + w_bias)            (rmsnorm of the branch, unrounded)
+ *     residual <- h = BF16(FMA(gate, n, residual))     (one FP32 rounding, then BF16)
+ *     next only: out = BF16((h * r_h) * FP32(w_next + w_next_bias)), r_h the rstd of the
+ *                BF16 row h (normalised in the same launch).
+ *   gate: BF16 [gate_rows, hidden], gate_rows = rows (one gate row per token) or 1 (one row
+ *   shared by every token, e.g. a per-channel gate).  Any hidden that is a multiple of 8
+ *   is accepted (the pages' kernels take 8192 only).
+ */
+dn_status dn_gated_residual_rmsnorm(void* residual, int64_t residual_stride,
+                                    const void* branch, int64_t branch_stride,
+                                    const void* gate, int64_t gate_stride, int64_t gate_rows,
+                                    const void* w, int w_dtype, float w_bias,
+                                    int64_t rows, int64_t hidden, float eps,
+                                    dn_stream_t stream);
+
+dn_status dn_gated_residual_next_rmsnorm(void* out, int64_t out_stride,
+                                         void* residual, int64_t residual_stride,
+                                         const void* branch, int64_t branch_stride,
+                                         const void* gate, int64_t gate_stride,
+                                         int64_t gate_rows,
+                                         const void* w, int w_dtype, float w_bias,
+                                         const void* w_next, int w_next_dtype,
+                                         float w_next_bias, int64_t rows, int64_t hidden,
+                                         float eps, dn_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * rmsnorm_sigmoid_gate   ([norm docs] Fixed-Width Fused Norms: rmsnorm_sigmoid_gate)
  *   The pages name only "per-head RMSNorm and sigmoid gate, in place, for head dim 64";
  *   the reading implemented: rows are heads (a [tokens, heads, head_dim] tensor passed as

@@ -44,13 +44,18 @@ def gated_residual_rmsnorm(branch, residual, gate, w, eps: float = 1e-6, bias: f
     h_exact = residual + gn
     h = bf16_round(h_exact)
     y_exact = y_mag = rn = None
+    h_mag = np.abs(residual) + np.abs(gn)
     if next_w is not None:
         nx = rmsnorm(h, next_w, next_bias, eps)
         y_exact, rn = nx.y_exact, nx.rstd
-        # the GPU's BF16 stream may differ from h by one ulp at rounding ties, which moves
-        # y by up to one ulp of its own
-        y_mag = np.abs(y_exact)
-    return GatedResidual(h_exact, h, np.abs(residual) + np.abs(gn), y_exact, y_mag, nb.rstd, rn)
+        # An FP32 evaluation of h may round to the other BF16 neighbour where h sits within
+        # 2^-20 of its term magnitude from a rounding midpoint; the next norm then sees a
+        # stream one ulp away there, which moves that element's y by one more ulp.  Such
+        # elements get a magnitude that admits two ulps; the others one.
+        band = 2.0 ** -20 * h_mag
+        near = bf16_round(h_exact - band) != bf16_round(h_exact + band)
+        y_mag = np.abs(y_exact) * np.where(near, 2.0 ** 15, 1.0)
+    return GatedResidual(h_exact, h, h_mag, y_exact, y_mag, nb.rstd, rn)
 
 
 __all__ = ["gated_residual_rmsnorm", "GatedResidual"]

@@ -48,7 +48,8 @@ def test_header_declares_the_expected_calls():
               "dn_fused_dit_gate_residual_layernorm_gamma_beta",
               "dn_fused_dit_gate_residual_layernorm_scale_shift",
               "dn_fused_dit_residual_layernorm_scale_shift", "dn_fused_qk_rmsnorm_rope",
-              "dn_fused_rmsnorm_silu", "dn_rmsnorm_sigmoid_gate", "dn_last_error"]:
+              "dn_fused_rmsnorm_silu", "dn_rmsnorm_sigmoid_gate", "dn_gated_residual_rmsnorm",
+              "dn_gated_residual_next_rmsnorm", "dn_last_error"]:
         assert n in names
 
 
@@ -245,6 +246,20 @@ def test_sigmoid_gate_checks(lib):
     assert f(A, 64, B, 64, C, 5, 0.0, 4, 64, 1e-6, None) == E_DTYPE         # weight dtype
     assert f(A, 64, B, 60, 0, 0, 0.0, 4, 64, 1e-6, None) == E_SHAPE         # gate stride
     assert f(A, 64, B, 64, C + 2, 0, 0.0, 4, 64, 1e-6, None) == E_ALIGN     # weight base
+
+
+def test_gated_residual_checks(lib):
+    f = lib.dn_gated_residual_rmsnorm
+    assert f(A, 8192, B, 8192, C, 8192, 1, D, 0, 0.0, 0, 8192, 1e-6, None) == OK
+    assert f(A, 8192, B, 8192, C, 8192, 3, D, 0, 0.0, 5, 8192, 1e-6, None) == E_SHAPE  # rows
+    assert b"gate_rows" in lib.dn_last_error()
+    assert f(A, 8192, 0, 8192, C, 8192, 1, D, 0, 0.0, 5, 8192, 1e-6, None) == E_NULL   # branch
+    n = lib.dn_gated_residual_next_rmsnorm
+    assert n(E, 8192, A, 8192, B, 8192, C, 8192, 5, D, 0, 0.0, 0, 0, 0.0, 5, 8192, 1e-6,
+             None) == E_NULL                                                  # w_next
+    assert n(0, 8192, A, 8192, B, 8192, C, 8192, 5, D, 0, 0.0, E, 0, 0.0, 5, 8192, 1e-6,
+             None) == E_NULL                                                  # out
+    assert n(0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 0, 0.0, 0, 0, 0.0, 0, 8192, 1e-6, None) == OK
 
 
 def test_force_threads_per_row(lib):

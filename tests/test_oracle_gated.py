@@ -50,3 +50,17 @@ def test_broadcast_gate_equals_repeated_rows():
     a = G.gated_residual_rmsnorm(b, r, g1, w, 1e-6)
     c = G.gated_residual_rmsnorm(b, r, np.repeat(g1, 7, axis=0), w, 1e-6)
     assert (a.h_exact == c.h_exact).all()
+
+
+def test_next_norm_band_marks_only_elements_at_rounding_ties():
+    b, r, g = bf((50, 1024)), bf((50, 1024)), bf((50, 1024), 0.5)
+    w = bf(1024, 0.1, 1.0)
+    out = G.gated_residual_rmsnorm(b, r, g, w, 1e-6, next_w=w)
+    wide = out.y_mag > np.abs(out.y_exact)
+    # flagged elements are rare and each sits next to a BF16 rounding midpoint of h
+    assert wide.mean() < 1e-2
+    hb = F.bf16_round(out.h_exact)
+    mid_dist = np.abs(hb - out.h_exact)
+    _, e = np.frexp(np.abs(out.h_exact))
+    ulp = np.ldexp(1.0, e - 8)                 # BF16 spacing in |h|'s binade
+    assert (np.abs(mid_dist - ulp / 2)[wide] <= 2.0 ** -19 * out.h_mag[wide] + 1e-30).all()

@@ -185,3 +185,18 @@ def sigmoid_gate(tokens: int = 16384, heads: int = 64, head_dim: int = 64,
         "gate": normal((tokens, heads * head_dim), seed, 1, std=2.0),
         "w": normal((head_dim,), seed, 2, mean=1.0, std=0.1),
     }, {"eps": 1e-6, "tokens": tokens, "heads": heads, "head_dim": head_dim})
+
+
+def gated_residual(rows: int = 16384, hidden: int = 8192, seed: int = 11,
+                   per_token_gate: bool = True) -> Workload:
+    """Gated-residual RMSNorm (+ next RMSNorm): branch, residual BF16 [rows, hidden] ~ N(0,1);
+    gate BF16 ~ N(0, 0.5) per token ([rows, hidden]) or one shared row ([1, hidden]);
+    w, w_next BF16 ~ N(1, 0.1).  Hidden 8192 is the pages' width."""
+    return Workload("gated_residual", {
+        "branch": normal((rows, hidden), seed, 0),
+        "residual": normal((rows, hidden), seed, 1),
+        "gate": normal((rows if per_token_gate else 1, hidden), seed,
+                       2 if per_token_gate else 3, std=0.5),
+        "w": normal((hidden,), seed, 4, mean=1.0, std=0.1),
+        "w_next": normal((hidden,), seed, 5, mean=1.0, std=0.1),
+    }, {"eps": 1e-6, "rows": rows, "hidden": hidden})
