@@ -32,7 +32,8 @@ layernorm and layernorm_quant on BF16 [8192, 4096], and the three DiT gate/resid
 LayerNorm modes on BF16 [16384, 3072] with gate/scale/shift read as row-stride-6*hidden
 chunks of one per-token modulation tensor.  `--family qk_rope` times the fused QK
 RMSNorm + 3-D RoPE + V copy on qkv BF16 [12288, 9216] (both pairings, BF16 and e4m3fn);
-`--family silu` the fused RMSNorm + SiLU at three video-VAE shapes.
+`--family silu` the fused RMSNorm + SiLU at three video-VAE shapes; `--family fixed_width`
+the gated-residual RMSNorm (+ next) at hidden 8192 and the per-head sigmoid-gate norm.
 """
 from __future__ import annotations
 
@@ -474,6 +475,45 @@ def run_silu_family(a) -> int:
                        "BF16 or e4m3fn out")
 
 
+def run_fixed_width_family(a) -> int:
+    """The fixed-width norms at the pages' widths: gated-residual RMSNorm (+ next RMSNorm) at
+    hidden 8192, per-token and shared gate; per-head RMSNorm + sigmoid gate at head dim 64."""
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating fixed-width norm inputs", file=sys.stderr, flush=True)
+    gw = W.gated_residual()
+    b, r, g, w, w2 = (gw.tensors[k].to(dev) for k in ("branch", "residual", "gate", "w", "w_next"))
+    g1 = g[0].contiguous()
+    y = torch.empty_like(b)
+    T, H = b.shape
+    sw = W.sigmoid_gate()
+    sp = sw.params
+    x = sw.tensors["x"].to(dev).reshape(sp["tokens"], sp["heads"], sp["head_dim"])
+    sg = sw.tensors["gate"].to(dev).reshape(sp["tokens"], sp["heads"], sp["head_dim"])
+    sww = sw.tensors["w"].to(dev)
+    calls = {
+        "gated_residual_token_gate": lambda: dn.dn_gated_residual_rmsnorm(b, r, g, w, 1e-6),
+        "gated_residual_shared_gate": lambda: dn.dn_gated_residual_rmsnorm(b, r, g1, w, 1e-6),
+        "gated_residual_next_token_gate": lambda: dn.dn_gated_residual_next_rmsnorm(
+            b, r, g, w, w2, 1e-6, out=y),
+        "rmsnorm_sigmoid_gate": lambda: dn.dn_rmsnorm_sigmoid_gate(x, sg, 1e-6, weight=sww),
+    }
+    e = T * H
+    es = x.numel()
+    ab = {"gated_residual_token_gate": 8 * e + 2 * H,
+          "gated_residual_shared_gate": 6 * e + 4 * H,
+          "gated_residual_next_token_gate": 10 * e + 4 * H,
+          "rmsnorm_sigmoid_gate": 6 * es + 2 * sp["head_dim"]}
+    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fixed-width fused norms",
+                       f"gated-residual RMSNorm (+ next) BF16 [{T},{H}]; per-head RMSNorm + "
+                       f"sigmoid gate BF16 [{sp['tokens']},{sp['heads']}x{sp['head_dim']}]")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,11 +525,12 @@ def main(argv=None) -> int:
                          "library dispatch is then a bench-step kernel)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", metavar="STATS_CSV")
-    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope", "silu"),
+    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope", "silu",
+                                         "fixed_width"),
                     default="rmsnorm",
                     help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm "
                          "family; qk_rope: the fused QK RMSNorm + 3-D RoPE; silu: the fused "
-                         "RMSNorm + SiLU")
+                         "RMSNorm + SiLU; fixed_width: gated-residual and sigmoid-gate norms")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) five "
@@ -517,6 +558,8 @@ def main(argv=None) -> int:
         return run_qk_rope_family(a)
     if a.family == "silu":
         return run_silu_family(a)
+    if a.family == "fixed_width":
+        return run_fixed_width_family(a)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating inputs", file=sys.stderr, flush=True)
