@@ -272,6 +272,46 @@ def device_copy_ceiling(torch, dev, reps: int = 5) -> float:
     return round(2 * (1 << 30) / sorted(ts)[len(ts) // 2] / 1e9, 1)
 
 
+def stream_ceilings(torch, dev, reps: int = 5):
+    """Measured HBM stream ceilings (libdnprobe.so): plain kernels with the norm kernels'
+    16-byte non-temporal buffer loads and stores at their read:write mixes, 256 MiB per
+    stream, each mix at 1 and 2 blocks of 256 threads per CU, chunked and grid-stride; the
+    best configuration's median GB/s of bytes moved per mix."""
+    import ctypes
+    path = os.path.join(ROOT, "dit_normalization_amd", "libdnprobe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.dn_probe_stream
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    n = 256 << 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(5)]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = torch.cuda.current_stream(dev).cuda_stream
+    out = {}
+    for reads, writes in ((1, 1), (2, 2), (2, 1), (3, 1)):
+        best = 0.0
+        for blocks in (cus, 2 * cus):
+            for blocked in (0, 1):
+                ts = []
+                for _ in range(reps):
+                    flush.fill_(1.0)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    rc = f(*(b.data_ptr() for b in bufs), n, reads, writes, blocks, blocked, st)
+                    e1.record()
+                    e1.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe failed ({rc})")
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+                gbs = (reads + writes) * n / sorted(ts)[len(ts) // 2] / 1e9
+                best = max(best, gbs)
+        out[f"stream_{reads}r{writes}w_GB/s"] = round(best, 1)
+    del bufs, flush
+    return out
+
+
 SHARD = (2048, 8192)
 
 
@@ -665,6 +705,11 @@ def main(argv=None) -> int:
         print("[bench] copy ceiling and one GPU's shard of the training shape", file=sys.stderr,
               flush=True)
         ceiling = {"device_copy_1GiB_GB/s": device_copy_ceiling(torch, dev)}
+        ceiling.update(stream_ceilings(torch, dev))
+        mix = {"fused_add_rmsnorm": "stream_2r2w_GB/s", "train_forward": "stream_2r2w_GB/s",
+               "train_backward_partials": "stream_2r1w_GB/s"}
+        for k, m in mix.items():
+            kernels[k]["of_stream_ceiling"] = round(kernels[k]["GB/s"] / ceiling[m], 4)
         shard = shard_measurement(torch, dev, dn, W)
 
     cpu = None
