@@ -221,45 +221,49 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #endif
   double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)16 * kPlanes * nvec : 0));
 
-  if (kPlanes > 0 && p.w_in_lds) {
-    for (int i = tid; i < nvec; i += NT) {
-      if constexpr (kLN) {
-        float ga[8], be[8];
-        load_affine8(p, i, ga, be);
-        if constexpr (kFold) {
+  // Per-block set-up (staged per-column parameters, block-scale padding).  It runs after
+  // the first step's row loads are issued, so the parameter fetch overlaps their latency.
+  auto stage = [&]() {
+    if (kPlanes > 0 && p.w_in_lds) {
+      for (int i = tid; i < nvec; i += NT) {
+        if constexpr (kLN) {
+          float ga[8], be[8];
+          load_affine8(p, i, ga, be);
+          if constexpr (kFold) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            ga[k] *= inv_scale;
-            be[k] *= inv_scale;
+            for (int k = 0; k < 8; ++k) {
+              ga[k] *= inv_scale;
+              be[k] *= inv_scale;
+            }
           }
-        }
-        wl[i] = make_float4(ga[0], ga[1], ga[2], ga[3]);
-        wl[nvec + i] = make_float4(ga[4], ga[5], ga[6], ga[7]);
-        wl[2 * nvec + i] = make_float4(be[0], be[1], be[2], be[3]);
-        wl[3 * nvec + i] = make_float4(be[4], be[5], be[6], be[7]);
-      } else {
-        float e[8];
-        load_weff8(p, i, e);
-        if constexpr (kFold) {
+          wl[i] = make_float4(ga[0], ga[1], ga[2], ga[3]);
+          wl[nvec + i] = make_float4(ga[4], ga[5], ga[6], ga[7]);
+          wl[2 * nvec + i] = make_float4(be[0], be[1], be[2], be[3]);
+          wl[3 * nvec + i] = make_float4(be[4], be[5], be[6], be[7]);
+        } else {
+          float e[8];
+          load_weff8(p, i, e);
+          if constexpr (kFold) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) e[k] *= inv_scale;
+            for (int k = 0; k < 8; ++k) e[k] *= inv_scale;
+          }
+          wl[i] = make_float4(e[0], e[1], e[2], e[3]);
+          wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
         }
-        wl[i] = make_float4(e[0], e[1], e[2], e[3]);
-        wl[nvec + i] = make_float4(e[4], e[5], e[6], e[7]);
+      }
+      __syncthreads();
+    }
+
+    if constexpr (EPI == EPI_FP8_BLOCK) {
+      // Pad entries [rows, bld) of every block-scale column are written as zeros.
+      const int64_t pad = p.bld - p.rows;
+      if (blockIdx.x == 0 && pad > 0) {
+        const int nb = p.hidden / 128;
+        for (int64_t i = tid; i < (int64_t)nb * pad; i += NT)
+          p.bscale[(i / pad) * p.bld + p.rows + (i % pad)] = 0.0f;
       }
     }
-    __syncthreads();
-  }
-
-  if constexpr (EPI == EPI_FP8_BLOCK) {
-    // Pad entries [rows, bld) of every block-scale column are written as zeros.
-    const int64_t pad = p.bld - p.rows;
-    if (blockIdx.x == 0 && pad > 0) {
-      const int nb = p.hidden / 128;
-      for (int64_t i = tid; i < (int64_t)nb * pad; i += NT)
-        p.bscale[(i / pad) * p.bld + p.rows + (i % pad)] = 0.0f;
-    }
-  }
+  };
 
   const double inv_hidden = 1.0 / (double)p.hidden;
   const double eps = (double)p.eps;
@@ -641,6 +645,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     Step s0, s1;
     int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER;
     if (base < p.rows) load(s0, base);
+    stage();
     while (base < p.rows) {
       int64_t nb = base + stride;
       if (nb < p.rows) load(s1, nb);
@@ -653,8 +658,19 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
       base = nb;
     }
   } else {
+    // The first step is peeled so that its loads precede the set-up; the steady-state loop
+    // keeps the load-then-process shape.
     Step s0;
-    for (int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER; base < p.rows; base += stride) {
+    int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER;
+    if (base < p.rows) {
+      load(s0, base);
+      stage();
+      process(s0, base);
+      base += stride;
+    } else {
+      stage();
+    }
+    for (; base < p.rows; base += stride) {
       load(s0, base);
       process(s0, base);
     }
