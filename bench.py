@@ -395,16 +395,66 @@ def run_layernorm_family(a) -> int:
                 dx, chunk["scale"], chunk["shift"], dr, 1e-6, scale_bias=p["scale_bias"],
                 shift_bias=p["shift_bias"], residual_out=ro, norm_out=no)),
     }
+    def cpu():
+        from oracle import layernorm as L
+        xs, gs, bs = _vals(lw.tensors["x"][:128]), _vals(lw.tensors["gamma"]), _vals(lw.tensors["beta"])
+        d = {k: _vals(dw.tensors[k][:128]) for k in ("x", "residual", "gate", "scale", "shift")}
+        dg_, db_ = _vals(dw.tensors["gamma"]), _vals(dw.tensors["beta"])
+        tl, hl = 128, LN[1]
+        hd = DIT[1]
+        per = (4 + 3) * tl * hl + (10 + 14 + 12) * 128 * hd
+
+        def run():
+            L.layernorm_quant(xs, gs, bs, 0.04, 1e-6)
+            L.layernorm(xs, gs, bs, 1e-6)
+            L.dit_gate_residual_layernorm_gamma_beta(d["residual"], d["x"], d["gate"], dg_, db_,
+                                                     p["gate_bias"], 1e-6)
+            L.dit_gate_residual_layernorm_scale_shift(d["residual"], d["x"], d["gate"], d["scale"],
+                                                      d["shift"], p["gate_bias"], p["scale_bias"],
+                                                      p["shift_bias"], 1e-6)
+            L.dit_residual_layernorm_scale_shift(d["x"], d["scale"], d["shift"], d["residual"],
+                                                 p["scale_bias"], p["shift_bias"], 1e-6)
+        return _oracle_rate(run, per, a.cpu_seconds / 2,
+                            "the five LayerNorm-family calls on 128 rows each")
+
     return time_family(a, torch, dev, calls, ln_alg_bytes(), "achieved HBM GB/s, LayerNorm family",
                        "layernorm + layernorm_quant BF16 [8192,4096]; DiT gate/residual "
                        "+ LayerNorm (gamma/beta, scale/shift) and residual + LayerNorm "
                        "scale/shift BF16 [16384,3072], modulation chunks of a "
-                       "[16384,18432] tensor")
+                       "[16384,18432] tensor", cpu)
 
 
-def time_family(a, torch, dev, calls, ab, metric, workload) -> int:
+def _oracle_rate(run, bytes_per_pass: int, seconds: float, what: str):
+    """Time `run` (one oracle pass over a bounded sample of `bytes_per_pass` algorithmic
+    bytes) repeatedly for about `seconds`; the cpu_baseline object of a family line."""
+    done, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(bytes_per_pass * done / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} passes of {what} ({el:.1f} s, single-threaded numpy FP64)"}
+
+
+def _vals(t):
+    """Host float64 values of a BF16 / FP32 torch CPU tensor (the oracle's BF16 decoder)."""
+    import numpy as np
+    import torch
+
+    from oracle import formats as F
+    if t.dtype == torch.bfloat16:
+        return F.bf16_bits_to_f64(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+    return t.double().numpy()
+
+
+def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
     """Warm up, then time `a.steps` rounds of every call in `calls` (one event between every
-    two calls on the calls' stream) and print one JSON line with per-call GB/s."""
+    two calls on the calls' stream) and print one JSON line with per-call GB/s, a roofline
+    object for the call that takes the most time, and (unless --no-cpu-baseline) the
+    oracle's rate from `cpu()`."""
     names = list(calls)
     for _ in range(a.warmup):
         for n in names:
@@ -431,6 +481,14 @@ def time_family(a, torch, dev, calls, ab, metric, workload) -> int:
                           frac=round(gbs / HBM_PEAK_GBS, 4))
     step_bytes = sum(ab.values())
     value = step_bytes / (wall / a.steps) / 1e9
+    dom = max(names, key=lambda n: kernels[n]["us"])
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                "traffic": None, "algorithmic_bytes": ab[dom]}
+    cpu_line = None
+    if cpu is not None and not a.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu_line = cpu()
     line = {
         "metric": metric, "value": round(value, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -439,7 +497,7 @@ def time_family(a, torch, dev, calls, ab, metric, workload) -> int:
         "config": {"workload": workload,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4), "step_bytes": step_bytes,
                    "parallelism": "single GPU"},
-        "kernels": kernels,
+        "roofline": roofline, "cpu_baseline": cpu_line, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -482,9 +540,24 @@ def run_qk_rope_family(a) -> int:
     wbytes = 2 * (p["nq"] + p["nk"]) * p["head_dim"]
     ab = {"qk_rope_interleaved_bf16": 4 * e + wbytes, "qk_rope_neox_bf16": 4 * e + wbytes,
           "qk_rope_interleaved_fp8": 3 * e + wbytes + 8, "qk_rope_neox_fp8": 3 * e + wbytes + 8}
+    def cpu():
+        from oracle import qk_rope as Q
+        n = 64
+        x = _vals(t["qkv"][:n])
+        wq_, wk_ = _vals(t["q_weight"]), _vals(t["k_weight"])
+        ids = list(range(n))
+
+        def run():
+            for il in (True, False):
+                Q.qk_rmsnorm_rope(x, wq_, wk_, p["nq"], p["nk"], p["nv"], p["head_dim"],
+                                  p["channels"], p["ppf"], p["pph"], p["ppw"], p["eps"],
+                                  p["base"], il, token_ids=ids)
+        return _oracle_rate(run, 2 * 4 * n * width, a.cpu_seconds / 2,
+                            f"both pairings on {n} tokens x {width}")
+
     return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused QK RMSNorm + 3-D RoPE",
                        f"fused_qk_rmsnorm_rope qkv BF16 [{T},{width}] (24+24+24 heads x 128, "
-                       f"patches {p['ppf']}x{p['pph']}x{p['ppw']}), BF16 or e4m3fn q/k/v out")
+                       f"patches {p['ppf']}x{p['pph']}x{p['ppw']}), BF16 or e4m3fn q/k/v out", cpu)
 
 
 def run_silu_family(a) -> int:
@@ -510,9 +583,16 @@ def run_silu_family(a) -> int:
             x, w, 1e-6, out=o8, scale=scale))
         ab[f"silu_bf16_{T}x{H}"] = 4 * T * H + 2 * H
         ab[f"silu_fp8_{T}x{H}"] = 3 * T * H + 2 * H + 4
+    def cpu():
+        from oracle import silu as S
+        wl = W.rmsnorm_silu(1024, 512)
+        xs, ws = _vals(wl.tensors["x"]), _vals(wl.tensors["w"])
+        return _oracle_rate(lambda: S.fused_rmsnorm_silu(xs, ws, 1e-6), 4 * 1024 * 512,
+                            a.cpu_seconds / 2, "BF16 out on 1024 rows x 512")
+
     return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused RMSNorm + SiLU",
                        "fused_rmsnorm_silu BF16 [399360,128], [99840,512], [24960,1024]; "
-                       "BF16 or e4m3fn out")
+                       "BF16 or e4m3fn out", cpu)
 
 
 def run_fixed_width_family(a) -> int:
@@ -549,9 +629,26 @@ def run_fixed_width_family(a) -> int:
           "gated_residual_shared_gate": 6 * e + 4 * H,
           "gated_residual_next_token_gate": 10 * e + 4 * H,
           "rmsnorm_sigmoid_gate": 6 * es + 2 * sp["head_dim"]}
+    def cpu():
+        from oracle import gated as Gd
+        from oracle import silu as S
+        n = 64
+        bb, rr_, gg = (_vals(gw.tensors[k][:n]) for k in ("branch", "residual", "gate"))
+        w1, w2_ = _vals(gw.tensors["w"]), _vals(gw.tensors["w_next"])
+        xs = _vals(sw.tensors["x"][:n]).reshape(-1, sp["head_dim"])
+        gs = _vals(sw.tensors["gate"][:n]).reshape(-1, sp["head_dim"])
+        sw_ = _vals(sw.tensors["w"])
+
+        def run():
+            Gd.gated_residual_rmsnorm(bb, rr_, gg, w1, 1e-6, next_w=w2_)
+            S.rmsnorm_sigmoid_gate(xs, gs, sw_, 1e-6)
+        return _oracle_rate(run, 10 * n * H + 6 * xs.size, a.cpu_seconds / 2,
+                            f"gated residual + next on {n} rows x {H} and the sigmoid gate on "
+                            f"{n} tokens")
+
     return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fixed-width fused norms",
                        f"gated-residual RMSNorm (+ next) BF16 [{T},{H}]; per-head RMSNorm + "
-                       f"sigmoid gate BF16 [{sp['tokens']},{sp['heads']}x{sp['head_dim']}]")
+                       f"sigmoid gate BF16 [{sp['tokens']},{sp['heads']}x{sp['head_dim']}]", cpu)
 
 
 def main(argv=None) -> int:
