@@ -110,17 +110,18 @@ def _read_csv(path):
         return list(csv.DictReader(fh))
 
 
-def _step_symbols(rows):
-    """The library's kernel symbols in order of first dispatch: one bench step launches
-    them in STEP_KERNELS order."""
+def _step_symbols(rows, names=None):
+    """The library's kernel symbols in order of first dispatch: one bench step (or family
+    round) launches them in `names` order (STEP_KERNELS by default)."""
+    names = STEP_KERNELS if names is None else names
     seen = []
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         n = r["Kernel_Name"]
         if n.startswith("void dn::") and n not in seen:
             seen.append(n)
-    if len(seen) != len(STEP_KERNELS):
-        raise SystemExit(f"expected {len(STEP_KERNELS)} library kernels, found {seen}")
-    return dict(zip(STEP_KERNELS, seen))
+    if len(seen) != len(names):
+        raise SystemExit(f"expected {len(names)} library kernels, found {seen}")
+    return dict(zip(names, seen))
 
 
 def _counter(rows, name):
@@ -137,20 +138,28 @@ def _counter(rows, name):
     return {k: sum(v) / len(v) for k, v in vals.items()}, scale, len(copies)
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> int:
+def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm") -> int:
+    """Per-kernel HBM traffic from the two counter runs.  For the step (family rmsnorm) the
+    result also goes to profiles/hbm_traffic.json, which bench.py reads for `traffic`."""
     fr, wr = _read_csv(fetch_csv), _read_csv(write_csv)
-    sym = _step_symbols(fr)
-    if _step_symbols(wr) != sym:
+    if family == "layernorm":
+        ab = ln_alg_bytes()
+        names = list(ab)
+        names = [names[0], names[2], names[1], names[3], names[4]]   # dispatch order
+    else:
+        ab = alg_bytes()
+        names = STEP_KERNELS
+    sym = _step_symbols(fr, names)
+    if _step_symbols(wr, names) != sym:
         raise SystemExit("the two counter runs dispatched different kernels")
     fetch, fscale, nf = _counter(fr, "FETCH_SIZE")
     write, wscale, nw = _counter(wr, "WRITE_SIZE")
-    ab = alg_bytes()
     out = {"source_sha256": kernel_source_sha256(), "fetch_scale": fscale, "write_scale": wscale,
            "calibration": f"{nf} and {nw} device copies of 1 GiB", "kernels": {}}
     print("| kernel | symbol | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic MiB | "
           "algorithmic MiB | ratio |")
     print("|---|---|---|---|---|---|---|")
-    for k in STEP_KERNELS:
+    for k in names:
         s_ = sym[k]
         rb = fetch[s_] * 1024 * fscale
         wb = write[s_] * 1024 * wscale
@@ -165,6 +174,8 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> int:
         print(f"| {k} | `{short}` | {fetch[s_]:,.1f} | {write[s_]:,.1f} | {t / 2**20:,.1f} | "
               f"{ab[k] / 2**20:,.1f} | {ratio} |")
     print(f"\nscales: FETCH_SIZE x{fscale:.4f}, WRITE_SIZE x{wscale:.4f}")
+    if family != "rmsnorm":
+        return 0
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -456,6 +467,13 @@ def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
     object for the call that takes the most time, and (unless --no-cpu-baseline) the
     oracle's rate from `cpu()`."""
     names = list(calls)
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(a.warmup):
         for n in names:
             calls[n]()
@@ -674,7 +692,7 @@ def main(argv=None) -> int:
                          "times, to scale profiler byte counters")
     a = ap.parse_args(argv)
     if a.summarize_counters:
-        return summarize_counters(*a.summarize_counters)
+        return summarize_counters(*a.summarize_counters, family=a.family)
     if a.summarize_trace:
         return summarize_trace(a.summarize_trace)
     if a.gpus != 1:
