@@ -204,6 +204,18 @@ __device__ __forceinline__ float sumsq8(const float f[8]) {
   return (s01 + s23) + (s45 + s67);
 }
 
+// The same sum carried to FP64, exact-product safe for any BF16 input: when an FP32 square
+// or the tree overflows (|value| above ~6.5e18) the eight squares are summed in FP64
+// instead (a branch no realistic activation takes).
+__device__ __forceinline__ double sumsq8_d(const float f[8]) {
+  const float t = sumsq8(f);
+  if (__builtin_expect(t <= 3.0e38f, 1)) return (double)t;
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s = fma((double)f[k], (double)f[k], s);
+  return s;
+}
+
 // Butterfly sum over aligned groups of WIDTH lanes (WIDTH a power of two <= 64).  Addition
 // is commutative, so every lane of a group ends with the same bits.
 template <int WIDTH>
@@ -217,6 +229,22 @@ template <int WIDTH>
 __device__ __forceinline__ float group_sum_f(float v) {
 #pragma unroll
   for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Maximum over each aligned group of 16 lanes (one DPP row) with four VALU moves and no
+// LDS traffic: swap neighbours, swap pairs (quad permutations), then mirror each half row
+// and the whole row; after each step every lane holds the maximum of twice as many lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  const int iv = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
   return v;
 }
 

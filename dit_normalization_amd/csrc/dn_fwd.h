@@ -387,7 +387,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
               ss[rr] = fma(d, d, ss[rr]);
             }
           } else {
-            ss[rr] += (double)sumsq8(fh);
+            ss[rr] += sumsq8_d(fh);
           }
         }
       }
@@ -611,11 +611,15 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           float amax = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(fn[k]));
-          amax = group_max<16>(amax);           // one 1x128 block = 16 lanes x 8 values
+          amax = row16_max(amax);               // one 1x128 block = 16 lanes x 8 values
           const float s = amax / kE4M3Max;      // IEEE divide: FP32(amax / 448)
-          const float rcp = s > 0.0f ? 1.0f / s : 0.0f;
+          // n / s as n * (1/s) on the hardware reciprocal (within 2 FP32 ulps).  Blocks with
+          // a scale below 2^-100 (normalised values below ~1e-28) are scaled by 2^100 on
+          // both sides first, so 1/s neither overflows nor leaves the normal range.
+          const float sc = s < 0x1p-100f ? 0x1p100f : 1.0f;
+          const float rcp = s > 0.0f ? __builtin_amdgcn_rcpf(s * sc) : 0.0f;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) fn[k] *= rcp;
+          for (int k = 0; k < 8; ++k) fn[k] = (fn[k] * sc) * rcp;
           bstore8(rq[rr], oq[rr] + d8, pack_fp8x8(fn));
           if ((lane & 15) == 0 && st.rok[rr] && idx < nvec)
             p.bscale[(int64_t)(idx >> 4) * p.bld + st.row[rr]] = s;

@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
       for (int v = 0; v < VMAX; ++v) {
         float f[8];
         unpack8(vb[rr][v], f);
-        ss[rr] += (double)sumsq8(f);
+        ss[rr] += sumsq8_d(f);
       }
 #pragma unroll
       for (int v = 0; v < VMAX; ++v) keep_packed(vb[rr][v]);
@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
           vb[rr][v] = hp;            // the BF16 stream, for the next norm
           float fh[8];
           unpack8(hp, fh);
-          s2[rr] += (double)sumsq8(fh);
+          s2[rr] += sumsq8_d(fh);
         }
       }
     }

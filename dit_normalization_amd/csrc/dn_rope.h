@@ -211,10 +211,10 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
     for (int m = 0; m < UMAX; ++m) {
       float f[8];
       unpack8(va[m], f);
-      double s = (double)sumsq8(f);
+      double s = sumsq8_d(f);
       if constexpr (NEOX) {
         unpack8(vb[m], f);
-        s += (double)sumsq8(f);
+        s += sumsq8_d(f);
       }
       sq += ucls[m] == 0 ? s : 0.0;
       sk += ucls[m] == 1 ? s : 0.0;

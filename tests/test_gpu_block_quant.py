@@ -82,3 +82,20 @@ def test_zero_blocks_get_zero_scale(dn):
     qb = bits8(q)
     assert (qb[0] & 0x7F == 0).all()
     assert (qb[2, :128] == 0x7E).all()       # a repeated value maps to 448
+
+
+def test_tiny_blocks_next_to_a_huge_element(dn):
+    """Rows with one huge element and tiny others: the blocks without it have normalised
+    values near 1e-37 and scales far below FP32's normal range; their codes must still be
+    those of n / s (no overflow of 1/s)."""
+    rows, hidden = 6, 1024
+    x = torch.zeros((rows, hidden), dtype=torch.bfloat16)
+    r = W.normal((rows, hidden), 77, 0, std=1e-8)
+    r[:, 3] = 1e30
+    r[1, 700] = -2e30
+    w = W.normal((hidden,), 77, 1, mean=1.0, std=0.1)
+    rd = dev(r)
+    q, bs = dn.dn_fused_add_rmsnorm_fp8_block_quant(dev(x), rd, dev(w), 1e-6)
+    ref = O.fused_add_rmsnorm_fp8_block_quant(values(x), values(r), values(w), 0.0, 1e-6)
+    assert (ref.scale[:, 1:] < 1e-36).any(), "the case must reach sub-normal-range scales"
+    check_block(q, bs.t()[:rows], None, ref, "tiny blocks")
