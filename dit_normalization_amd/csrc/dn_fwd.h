@@ -687,19 +687,24 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 //  hidden/8: up to 4 vectors per lane a row stays in one wave or less; wider rows spread
 //  over more waves rather than holding more vectors per lane.  On MI355X fewer bytes in
 //  flight per wave stream better (measured: train forward at H=8192 goes from 5.1 to
-//  5.9 TB/s moving from 1 wave x 16 vectors to 4 waves x 4 vectors per row).  The tiers
-//  after the first eleven are reachable only through dn_force_threads_per_row.
+//  5.9 TB/s moving from 1 wave x 16 vectors to 4 waves x 4 vectors per row).  Between
+//  the 4-vector tiers, a 3-vector tier of the same width takes rows of up to 3*TPR
+//  vectors: no slot left empty, fewer registers, more waves resident (measured at H=3072,
+//  5120, 6144, 10240 and 12288: +1-20 %, the most for plain RMSNorm and the Ada FP8 route,
+//  none slower).  The tiers after the first fourteen are reachable only through
+//  dn_force_threads_per_row.
 #define DN_FWD_TIERS(X)                                                         \
   X(0, 8, 1, 4, 256)    X(1, 16, 1, 4, 256)   X(2, 32, 1, 2, 256)              \
   X(3, 64, 1, 2, 256)   X(4, 64, 2, 1, 256)   X(5, 64, 3, 1, 256)              \
-  X(6, 64, 4, 1, 256)   X(7, 128, 4, 1, 256)  X(8, 256, 4, 1, 256)             \
-  X(9, 512, 4, 1, 512)  X(10, 1024, 4, 1, 1024)                                \
-  X(11, 64, 6, 1, 256)  X(12, 64, 8, 1, 256)  X(13, 64, 12, 1, 256)            \
-  X(14, 64, 16, 1, 256) X(15, 128, 8, 1, 256) X(16, 256, 8, 1, 256)            \
-  X(17, 512, 8, 1, 512)
+  X(6, 64, 4, 1, 256)   X(7, 128, 3, 1, 256)  X(8, 128, 4, 1, 256)             \
+  X(9, 256, 3, 1, 256)  X(10, 256, 4, 1, 256) X(11, 512, 3, 1, 512)            \
+  X(12, 512, 4, 1, 512) X(13, 1024, 4, 1, 1024)                                \
+  X(14, 64, 6, 1, 256)  X(15, 64, 8, 1, 256)  X(16, 64, 12, 1, 256)            \
+  X(17, 64, 16, 1, 256) X(18, 128, 8, 1, 256) X(19, 256, 8, 1, 256)            \
+  X(20, 512, 8, 1, 512)
 
-constexpr int kFwdTierCount = 18;
-constexpr int kFwdAutoTiers = 11;   // tiers the automatic choice considers
+constexpr int kFwdTierCount = 21;
+constexpr int kFwdAutoTiers = 14;   // tiers the automatic choice considers
 
 // Largest VMAX an input/epilogue combination is built with: the Ada, gated and
 // modulation routes keep five or six 16-byte vectors per column in flight, so they stop

@@ -45,8 +45,8 @@ def test_rmsnorm_32x4096(dn):
 
 
 @pytest.mark.parametrize("hidden", [8, 16, 24, 64, 72, 128, 136, 256, 264, 512, 520, 1000, 1024,
-                                    1536, 2048, 3072, 4096, 5120, 6144, 7168, 8192, 8200, 12288,
-                                    16384, 24576, 32768])
+                                    1536, 2048, 2056, 3072, 4096, 4104, 5120, 6144, 7168, 8192,
+                                    8200, 10240, 12288, 12296, 16384, 24576, 32768])
 def test_rmsnorm_every_row_tier(dn, hidden):
     x = W.normal((67, hidden), 11, hidden)
     w = W.normal((hidden,), 12, hidden, mean=1.0, std=0.2)
