@@ -14,9 +14,9 @@ the 256 MB Infinity Cache by the previous kernel's traffic.
 synchronisations).  Algorithmic bytes count each tensor the definition reads or writes
 once; the backward's FP64 workspace traffic is not counted.  Inside the timed region only
 the dominant kernel (the training forward, the roofline's kernel) is bracketed by HIP events
-on the kernels' stream; the per-kernel table comes from K more steps with an event between
-every two kernels (each event record costs the stream a few microseconds, so the table's
-durations include that).  `cpu_baseline` times the FP64 numpy oracle on a bounded sample
+(created without the system-scope fence, see HipTimingEvent) on the kernels' stream; the
+per-kernel table comes from K more steps with an event between every two kernels (each
+record still costs the stream about a microsecond, which the table's durations include).  `cpu_baseline` times the FP64 numpy oracle on a bounded sample
 of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
@@ -83,11 +83,17 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
+def traffic_path(family: str = "rmsnorm") -> str:
+    """The committed counter summary of a bench family (the step's is hbm_traffic.json)."""
+    name = "hbm_traffic.json" if family == "rmsnorm" else f"{family}_family_hbm_traffic.json"
+    return os.path.join(ROOT, "profiles", name)
+
+
+def measured_traffic(kernel: str, family: str = "rmsnorm"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE / WRITE_SIZE scaled by a plain copy), or None when the kernel sources have
     changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = traffic_path(family)
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -97,6 +103,86 @@ def measured_traffic(kernel: str):
         return None
     k = d.get("kernels", {}).get(kernel)
     return None if k is None else k["traffic_bytes"]
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
+_EVENT_KIND = {"kind": None}
+
+
+class HipTimingEvent:
+    """A HIP event created with hipEventDisableSystemFence, recorded on a torch stream.
+
+    torch.cuda.Event records with a system-scope fence, whose cache write-back costs the
+    stream ~3 us per record (measured on MI355X: a bench step with an event between every
+    two kernels takes 430 us with torch's events, 418 us with these, 410 us with none).
+    Without that fence the record only timestamps the stream, which is all a timing event
+    needs.  The runtime is the one torch loaded (same soname), so torch's streams are valid
+    handles for it."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self, torch):
+        import ctypes
+        self._torch = torch
+        self._ev = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self._ev),
+                                                     HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream=None):
+        import ctypes
+        st = stream if stream is not None else self._torch.cuda.current_stream()
+        rc = self._hip.hipEventRecord(self._ev, ctypes.c_void_p(st.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def synchronize(self):
+        rc = self._hip.hipEventSynchronize(self._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventSynchronize failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self._ev:
+                self._hip.hipEventDestroy(self._ev)
+        except Exception:
+            pass
+
+
+def timing_event(torch):
+    """A timing event on torch's streams: HipTimingEvent, or torch.cuda.Event where the HIP
+    runtime cannot be reached through ctypes (the kind used is reported in the JSON line)."""
+    if _EVENT_KIND["kind"] != "torch":
+        try:
+            ev = HipTimingEvent(torch)
+            _EVENT_KIND["kind"] = "hipEventDisableSystemFence"
+            return ev
+        except (OSError, AttributeError, RuntimeError):
+            _EVENT_KIND["kind"] = "torch"
+    return torch.cuda.Event(enable_timing=True)
 
 
 STEP_KERNELS = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
@@ -110,50 +196,52 @@ def _read_csv(path):
         return list(csv.DictReader(fh))
 
 
-def _step_symbols(rows, names=None):
-    """The library's kernel symbols in order of first dispatch: one bench step (or family
-    round) launches them in `names` order (STEP_KERNELS by default)."""
-    names = STEP_KERNELS if names is None else names
-    seen = []
-    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
-        n = r["Kernel_Name"]
-        if n.startswith("void dn::") and n not in seen:
-            seen.append(n)
-    if len(seen) != len(names):
-        raise SystemExit(f"expected {len(names)} library kernels, found {seen}")
-    return dict(zip(names, seen))
+def _library_dispatches(rows, names):
+    """Map every library dispatch of a counter run to a call name.  A bench round launches
+    the calls in `names` order, so the k-th library dispatch (by dispatch id) belongs to
+    names[k % len(names)]; each name must always dispatch the same kernel symbol.  Returns
+    {name: (symbol, [rows])}."""
+    lib = [r for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+           if r["Kernel_Name"].startswith("void dn::")]
+    if not lib or len(lib) % len(names):
+        raise SystemExit(f"{len(lib)} library dispatches are not whole rounds of {names}")
+    out = {}
+    for k, r in enumerate(lib):
+        n = names[k % len(names)]
+        sym, rs = out.setdefault(n, (r["Kernel_Name"], []))
+        if sym != r["Kernel_Name"]:
+            raise SystemExit(f"{n} dispatched both {sym} and {r['Kernel_Name']}")
+        rs.append(r)
+    return out
 
 
-def _counter(rows, name):
-    """Per-symbol mean of one counter (KiB per dispatch) and the copy calibration scale:
-    bytes per KiB reported, from the 1 GiB device copies (the largest copy dispatches)."""
-    vals = {}
-    for r in rows:
-        if r["Counter_Name"] == name:
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs if v > GIB_KIB / 4]
+def _counter(rows, name, names):
+    """Per-call mean of one counter (KiB per dispatch), the symbol of each call, and the
+    copy calibration scale: bytes per KiB reported, from the 1 GiB device copies (the
+    copy dispatches above a quarter of a GiB)."""
+    rows = [r for r in rows if r["Counter_Name"] == name]
+    copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+              and float(r["Counter_Value"]) > GIB_KIB / 4]
     if not copies:
         raise SystemExit(f"no 1 GiB calibration copy in the {name} run (use --copy-calibration)")
     scale = GIB_KIB / (sum(copies) / len(copies))
-    return {k: sum(v) / len(v) for k, v in vals.items()}, scale, len(copies)
+    per = _library_dispatches(rows, names)
+    mean = {n: sum(float(r["Counter_Value"]) for r in rs) / len(rs) for n, (_, rs) in per.items()}
+    return mean, {n: sym for n, (sym, _) in per.items()}, scale, len(copies)
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm") -> int:
-    """Per-kernel HBM traffic from the two counter runs.  For the step (family rmsnorm) the
-    result also goes to profiles/hbm_traffic.json, which bench.py reads for `traffic`."""
+def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm",
+                       out_path: str | None = None) -> int:
+    """Per-kernel HBM traffic from the two counter runs of one bench family; the result also
+    goes to `out_path` (default: the family's file under profiles/, traffic_path), which
+    bench.py reads for `traffic`."""
     fr, wr = _read_csv(fetch_csv), _read_csv(write_csv)
-    if family == "layernorm":
-        ab = ln_alg_bytes()
-        names = list(ab)
-        names = [names[0], names[2], names[1], names[3], names[4]]   # dispatch order
-    else:
-        ab = alg_bytes()
-        names = STEP_KERNELS
-    sym = _step_symbols(fr, names)
-    if _step_symbols(wr, names) != sym:
+    ab = FAMILY_BYTES[family]()
+    names = STEP_KERNELS if family == "rmsnorm" else list(ab)   # dispatch order
+    fetch, sym, fscale, nf = _counter(fr, "FETCH_SIZE", names)
+    write, wsym, wscale, nw = _counter(wr, "WRITE_SIZE", names)
+    if wsym != sym:
         raise SystemExit("the two counter runs dispatched different kernels")
-    fetch, fscale, nf = _counter(fr, "FETCH_SIZE")
-    write, wscale, nw = _counter(wr, "WRITE_SIZE")
     out = {"source_sha256": kernel_source_sha256(), "fetch_scale": fscale, "write_scale": wscale,
            "calibration": f"{nf} and {nw} device copies of 1 GiB", "kernels": {}}
     print("| kernel | symbol | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic MiB | "
@@ -161,22 +249,20 @@ def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm") 
     print("|---|---|---|---|---|---|---|")
     for k in names:
         s_ = sym[k]
-        rb = fetch[s_] * 1024 * fscale
-        wb = write[s_] * 1024 * wscale
+        rb = fetch[k] * 1024 * fscale
+        wb = write[k] * 1024 * wscale
         t = rb + wb
-        out["kernels"][k] = {"symbol": s_, "fetch_kib": round(fetch[s_], 1),
-                             "write_kib": round(write[s_], 1), "read_bytes": int(rb),
+        out["kernels"][k] = {"symbol": s_, "fetch_kib": round(fetch[k], 1),
+                             "write_kib": round(write[k], 1), "read_bytes": int(rb),
                              "write_bytes": int(wb), "traffic_bytes": int(t),
                              "algorithmic_bytes": ab[k],
                              "traffic_over_algorithmic": round(t / ab[k], 4)}
         short = s_.replace("void ", "").split("(")[0]
         ratio = f"{t / ab[k]:.3f}" if ab[k] > 1 << 20 else "(workspace)"
-        print(f"| {k} | `{short}` | {fetch[s_]:,.1f} | {write[s_]:,.1f} | {t / 2**20:,.1f} | "
+        print(f"| {k} | `{short}` | {fetch[k]:,.1f} | {write[k]:,.1f} | {t / 2**20:,.1f} | "
               f"{ab[k] / 2**20:,.1f} | {ratio} |")
     print(f"\nscales: FETCH_SIZE x{fscale:.4f}, WRITE_SIZE x{wscale:.4f}")
-    if family != "rmsnorm":
-        return 0
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = out_path or traffic_path(family)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -240,22 +326,67 @@ DIT = (16384, 3072)
 
 
 def ln_alg_bytes():
-    """Algorithmic HBM bytes per launch of the LayerNorm family."""
+    """Algorithmic HBM bytes per launch of the LayerNorm family, in dispatch order (the
+    [8192,4096] and [16384,3072] shapes alternate, so no kernel finds its inputs in the
+    Infinity Cache)."""
     tl, hl = LN
     td, hd = DIT
     el, ed = tl * hl, td * hd
     return {
         # read x; write y; FP32 gamma and beta
         "layernorm": 4 * el + 8 * hl,
-        # read x; write FP8 out; gamma, beta, scale
-        "layernorm_quant": 3 * el + 8 * hl + 4,
         # read x, residual, gate; write residual_out, norm_out; gamma, beta
         "dit_gate_residual_layernorm_gamma_beta": 10 * ed + 8 * hd,
+        # read x; write FP8 out; gamma, beta, scale
+        "layernorm_quant": 3 * el + 8 * hl + 4,
         # read x, residual, gate, scale, shift; write residual_out, norm_out
         "dit_gate_residual_layernorm_scale_shift": 14 * ed,
         # read x, residual, scale, shift; write residual_out, norm_out
         "dit_residual_layernorm_scale_shift": 12 * ed,
     }
+
+
+# Fused QK RMSNorm + 3-D RoPE: a 16 x 24 x 32 patch grid, 24 + 24 + 24 heads of 128.
+QK = {"tokens": 16 * 24 * 32, "nq": 24, "nk": 24, "nv": 24, "head_dim": 128}
+SILU_SHAPES = ((399360, 128), (99840, 512), (24960, 1024))
+GRES = (16384, 8192)
+SIGMOID = (16384, 64, 64)     # tokens, heads, head dim
+
+
+def qk_alg_bytes():
+    """Per launch, in dispatch order: read qkv; write q, k, v (BF16, or e4m3fn plus the two
+    scales); the two BF16 norm weights."""
+    e = QK["tokens"] * (QK["nq"] + QK["nk"] + QK["nv"]) * QK["head_dim"]
+    wb = 2 * (QK["nq"] + QK["nk"]) * QK["head_dim"]
+    return {"qk_rope_interleaved_bf16": 4 * e + wb, "qk_rope_neox_bf16": 4 * e + wb,
+            "qk_rope_interleaved_fp8": 3 * e + wb + 8, "qk_rope_neox_fp8": 3 * e + wb + 8}
+
+
+def silu_alg_bytes():
+    """Per launch, in dispatch order: read x; write y (BF16) or q (e4m3fn, plus the scale);
+    the BF16 weight."""
+    ab = {}
+    for T, H in SILU_SHAPES:
+        ab[f"silu_bf16_{T}x{H}"] = 4 * T * H + 2 * H
+        ab[f"silu_fp8_{T}x{H}"] = 3 * T * H + 2 * H + 4
+    return ab
+
+
+def fixed_alg_bytes():
+    """Per launch, in dispatch order.  Gated residual: read branch, residual and the gate
+    (per token, or one shared row), write residual; + next: also write the next norm's
+    output and read its weight.  Sigmoid gate: read x and gate, write x."""
+    T, H = GRES
+    e = T * H
+    es = SIGMOID[0] * SIGMOID[1] * SIGMOID[2]
+    return {"gated_residual_token_gate": 8 * e + 2 * H,
+            "gated_residual_shared_gate": 6 * e + 4 * H,
+            "gated_residual_next_token_gate": 10 * e + 4 * H,
+            "rmsnorm_sigmoid_gate": 6 * es + 2 * SIGMOID[2]}
+
+
+FAMILY_BYTES = {"rmsnorm": alg_bytes, "layernorm": ln_alg_bytes, "qk_rope": qk_alg_bytes,
+                "silu": silu_alg_bytes, "fixed_width": fixed_alg_bytes}
 
 
 def _stats(ts):
@@ -273,7 +404,7 @@ def device_copy_ceiling(torch, dev, reps: int = 5) -> float:
     dst = torch.empty_like(src)
     ts = []
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = timing_event(torch), timing_event(torch)
         e0.record()
         dst.copy_(src)
         e1.record()
@@ -307,8 +438,8 @@ def stream_ceilings(torch, dev, reps: int = 5):
                 ts = []
                 for _ in range(reps):
                     flush.fill_(1.0)
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0 = timing_event(torch)
+                    e1 = timing_event(torch)
                     e0.record()
                     rc = f(*(b.data_ptr() for b in bufs), n, reads, writes, blocks, blocked, st)
                     e1.record()
@@ -351,7 +482,7 @@ def shard_measurement(torch, dev, dn, W, reps: int = 10):
         ts = []
         for _ in range(reps):
             flush.fill_(1.0)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = timing_event(torch), timing_event(torch)
             e0.record()
             fn()
             e1.record()
@@ -428,7 +559,7 @@ def run_layernorm_family(a) -> int:
         return _oracle_rate(run, per, a.cpu_seconds / 2,
                             "the five LayerNorm-family calls on 128 rows each")
 
-    return time_family(a, torch, dev, calls, ln_alg_bytes(), "achieved HBM GB/s, LayerNorm family",
+    return time_family(a, torch, dev, calls, "achieved HBM GB/s, LayerNorm family",
                        "layernorm + layernorm_quant BF16 [8192,4096]; DiT gate/residual "
                        "+ LayerNorm (gamma/beta, scale/shift) and residual + LayerNorm "
                        "scale/shift BF16 [16384,3072], modulation chunks of a "
@@ -461,12 +592,16 @@ def _vals(t):
     return t.double().numpy()
 
 
-def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
+def time_family(a, torch, dev, calls, metric, workload, cpu=None) -> int:
     """Warm up, then time `a.steps` rounds of every call in `calls` (one event between every
     two calls on the calls' stream) and print one JSON line with per-call GB/s, a roofline
-    object for the call that takes the most time, and (unless --no-cpu-baseline) the
-    oracle's rate from `cpu()`."""
+    object for the call that takes the most time (with its counter-measured traffic while
+    the kernel sources match the family's committed summary), and (unless
+    --no-cpu-baseline) the oracle's rate from `cpu()`."""
+    ab = FAMILY_BYTES[a.family]()
     names = list(calls)
+    if names != list(ab):
+        raise RuntimeError(f"{a.family}: calls {names} differ from the byte table {list(ab)}")
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -479,7 +614,7 @@ def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
             calls[n]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    evs = [[timing_event(torch) for _ in range(len(names) + 1)]
            for _ in range(a.steps)]
     print(f"[bench] timing {a.steps} rounds", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -502,7 +637,7 @@ def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
     dom = max(names, key=lambda n: kernels[n]["us"])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                "traffic": None, "algorithmic_bytes": ab[dom]}
+                "traffic": measured_traffic(dom, a.family), "algorithmic_bytes": ab[dom]}
     cpu_line = None
     if cpu is not None and not a.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
@@ -516,6 +651,7 @@ def time_family(a, torch, dev, calls, ab, metric, workload, cpu=None) -> int:
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4), "step_bytes": step_bytes,
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu_line, "kernels": kernels,
+        "timing_events": _EVENT_KIND["kind"],
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -554,10 +690,8 @@ def run_qk_rope_family(a) -> int:
 
     calls = {"qk_rope_interleaved_bf16": call(True, False), "qk_rope_neox_bf16": call(False, False),
              "qk_rope_interleaved_fp8": call(True, True), "qk_rope_neox_fp8": call(False, True)}
-    e = T * width
-    wbytes = 2 * (p["nq"] + p["nk"]) * p["head_dim"]
-    ab = {"qk_rope_interleaved_bf16": 4 * e + wbytes, "qk_rope_neox_bf16": 4 * e + wbytes,
-          "qk_rope_interleaved_fp8": 3 * e + wbytes + 8, "qk_rope_neox_fp8": 3 * e + wbytes + 8}
+    if any(p[k] != QK[k] for k in QK):
+        raise RuntimeError(f"the QK RoPE workload {p} is not the byte table's {QK}")
     def cpu():
         from oracle import qk_rope as Q
         n = 64
@@ -573,7 +707,7 @@ def run_qk_rope_family(a) -> int:
         return _oracle_rate(run, 2 * 4 * n * width, a.cpu_seconds / 2,
                             f"both pairings on {n} tokens x {width}")
 
-    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused QK RMSNorm + 3-D RoPE",
+    return time_family(a, torch, dev, calls, "achieved HBM GB/s, fused QK RMSNorm + 3-D RoPE",
                        f"fused_qk_rmsnorm_rope qkv BF16 [{T},{width}] (24+24+24 heads x 128, "
                        f"patches {p['ppf']}x{p['pph']}x{p['ppw']}), BF16 or e4m3fn q/k/v out", cpu)
 
@@ -588,9 +722,9 @@ def run_silu_family(a) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] generating RMSNorm + SiLU inputs", file=sys.stderr, flush=True)
-    calls, ab = {}, {}
+    calls = {}
     scale = torch.tensor([0.02], dtype=torch.float32, device=dev)
-    for T, H in ((399360, 128), (99840, 512), (24960, 1024)):
+    for T, H in SILU_SHAPES:
         wl = W.rmsnorm_silu(T, H)
         x, w = wl.tensors["x"].to(dev), wl.tensors["w"].to(dev)
         ob = torch.empty_like(x)
@@ -599,8 +733,6 @@ def run_silu_family(a) -> int:
             x, w, 1e-6, out=ob))
         calls[f"silu_fp8_{T}x{H}"] = (lambda x=x, w=w, o8=o8: dn.dn_fused_rmsnorm_silu(
             x, w, 1e-6, out=o8, scale=scale))
-        ab[f"silu_bf16_{T}x{H}"] = 4 * T * H + 2 * H
-        ab[f"silu_fp8_{T}x{H}"] = 3 * T * H + 2 * H + 4
     def cpu():
         from oracle import silu as S
         wl = W.rmsnorm_silu(1024, 512)
@@ -608,7 +740,7 @@ def run_silu_family(a) -> int:
         return _oracle_rate(lambda: S.fused_rmsnorm_silu(xs, ws, 1e-6), 4 * 1024 * 512,
                             a.cpu_seconds / 2, "BF16 out on 1024 rows x 512")
 
-    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fused RMSNorm + SiLU",
+    return time_family(a, torch, dev, calls, "achieved HBM GB/s, fused RMSNorm + SiLU",
                        "fused_rmsnorm_silu BF16 [399360,128], [99840,512], [24960,1024]; "
                        "BF16 or e4m3fn out", cpu)
 
@@ -624,12 +756,12 @@ def run_fixed_width_family(a) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] generating fixed-width norm inputs", file=sys.stderr, flush=True)
-    gw = W.gated_residual()
+    gw = W.gated_residual(*GRES)
     b, r, g, w, w2 = (gw.tensors[k].to(dev) for k in ("branch", "residual", "gate", "w", "w_next"))
     g1 = g[0].contiguous()
     y = torch.empty_like(b)
     T, H = b.shape
-    sw = W.sigmoid_gate()
+    sw = W.sigmoid_gate(*SIGMOID)
     sp = sw.params
     x = sw.tensors["x"].to(dev).reshape(sp["tokens"], sp["heads"], sp["head_dim"])
     sg = sw.tensors["gate"].to(dev).reshape(sp["tokens"], sp["heads"], sp["head_dim"])
@@ -641,12 +773,6 @@ def run_fixed_width_family(a) -> int:
             b, r, g, w, w2, 1e-6, out=y),
         "rmsnorm_sigmoid_gate": lambda: dn.dn_rmsnorm_sigmoid_gate(x, sg, 1e-6, weight=sww),
     }
-    e = T * H
-    es = x.numel()
-    ab = {"gated_residual_token_gate": 8 * e + 2 * H,
-          "gated_residual_shared_gate": 6 * e + 4 * H,
-          "gated_residual_next_token_gate": 10 * e + 4 * H,
-          "rmsnorm_sigmoid_gate": 6 * es + 2 * sp["head_dim"]}
     def cpu():
         from oracle import gated as Gd
         from oracle import silu as S
@@ -664,7 +790,7 @@ def run_fixed_width_family(a) -> int:
                             f"gated residual + next on {n} rows x {H} and the sigmoid gate on "
                             f"{n} tokens")
 
-    return time_family(a, torch, dev, calls, ab, "achieved HBM GB/s, fixed-width fused norms",
+    return time_family(a, torch, dev, calls, "achieved HBM GB/s, fixed-width fused norms",
                        f"gated-residual RMSNorm (+ next) BF16 [{T},{H}]; per-head RMSNorm + "
                        f"sigmoid gate BF16 [{sp['tokens']},{sp['heads']}x{sp['head_dim']}]", cpu)
 
@@ -766,11 +892,12 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     # Timed region: K steps between synchronisations (wall clock).  Only the dominant kernel
-    # (the training forward) is bracketed by events here: every event record in the stream
-    # costs ~3 us of device time (measured: 409 us per step without events, 428 us with six).
+    # (the training forward) is bracketed by events here: even a fence-free event record
+    # costs the stream about 1 us (measured: 410 us per step with no events, 412 us with two,
+    # 418 us with six).
     dom = "train_forward"
     di = names.index(dom)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    evs = [[timing_event(torch) for _ in range(6)] for _ in range(a.steps)]
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -781,7 +908,7 @@ def main(argv=None) -> int:
     dom_live = [e[di].elapsed_time(e[di + 1]) * 1e-3 for e in evs]
 
     # Per-kernel breakdown: K more steps with an event between every two kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    evs = [[timing_event(torch) for _ in range(6)] for _ in range(a.steps)]
     for i in range(a.steps):
         step(evs[i])
     torch.cuda.synchronize()
@@ -845,7 +972,7 @@ def main(argv=None) -> int:
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "step_bytes": step_bytes, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "headline": headline,
-        "ceilings": ceiling, "shard_2048x8192": shard,
+        "ceilings": ceiling, "shard_2048x8192": shard, "timing_events": _EVENT_KIND["kind"],
     }
     print(json.dumps(line), flush=True)
     return 0
