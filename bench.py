@@ -497,6 +497,92 @@ def shard_measurement(torch, dev, dn, W, reps: int = 10):
                                           f"{reps} cold launches", "kernels": out}
 
 
+def isolated(torch, fn, nbytes: int, flush, reps: int = 20):
+    """Median/p10/p90 of `reps` launches of `fn`, each after a 1 GiB write that evicts L2 and
+    the 256 MB Infinity Cache, so every launch streams its inputs from HBM."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0, e1 = timing_event(torch), timing_event(torch)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    st = _stats(ts)
+    gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+    return dict(st, bytes=nbytes, **{"GB/s": round(gbs, 1)}, frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def config_measurements(torch, dev, dn, W, reps: int = 20):
+    """The other configurations of the hot path, each launch isolated (caches evicted):
+    rmsnorm [32,4096] (launch-bound), fused add + static FP8 per head [8192,32,128] and with
+    the Gemma weight offset, 1x128 block FP8 [16384,7168] (with and without normed_out), and
+    the gated AdaRMSNorm + FP8 [2520,3072] with per-row and broadcast style."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    scale = torch.tensor([0.04], dtype=torch.float32, device=dev)
+    out = {}
+
+    c1 = W.rmsnorm_fwd()
+    x1, w1 = c1.tensors["x"].to(dev), c1.tensors["w"].to(dev)
+    y1 = torch.empty_like(x1)
+    r1 = torch.empty(x1.shape[0], dtype=torch.float32, device=dev)
+    t1, h1 = x1.shape
+    out["rmsnorm_32x4096"] = isolated(torch, lambda: dn.dn_rmsnorm(
+        x1, w1, 1e-6, out=y1, rstd=r1, return_rstd=True), 4 * t1 * h1 + 2 * h1 + 4 * t1, flush,
+        reps)
+
+    c2 = W.fused_add_quant(8192, 128, heads=32)
+    x2, r2, w2 = (c2.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    q2 = torch.empty(x2.shape, dtype=torch.float8_e4m3fn, device=dev)
+    out["fused_add_quant_per_head_8192x32x128"] = isolated(torch, lambda: (
+        dn.dn_fused_add_rmsnorm_quant(x2, r2, w2, scale, 1e-6, out=q2)),
+        7 * x2.numel() + 2 * 128 + 4, flush, reps)
+    del x2, r2, q2
+
+    c2 = W.fused_add_quant()
+    x2, r2, w2 = (c2.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    q2 = torch.empty(x2.shape, dtype=torch.float8_e4m3fn, device=dev)
+    out["fused_add_quant_gemma_8192x4096"] = isolated(torch, lambda: (
+        dn.dn_fused_add_rmsnorm_quant(x2, r2, w2, scale, 1e-6, w_bias=1.0, out=q2)),
+        7 * x2.numel() + 2 * 4096 + 4, flush, reps)
+    del x2, r2, q2
+
+    c3 = W.block_quant()
+    x3, r3, w3 = (c3.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    t3, h3 = x3.shape
+    q3 = torch.empty(x3.shape, dtype=torch.float8_e4m3fn, device=dev)
+    s3 = torch.empty((h3 // 128, (t3 + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    n3 = torch.empty_like(x3)
+    b3 = 7 * t3 * h3 + 4 * t3 * (h3 // 128) + 2 * h3
+    out["block_quant_16384x7168"] = isolated(torch, lambda: (
+        dn.dn_fused_add_rmsnorm_fp8_block_quant(x3, r3, w3, 1e-6, out=q3, block_scale=s3)),
+        b3, flush, reps)
+    out["block_quant_normed_out_16384x7168"] = isolated(torch, lambda: (
+        dn.dn_fused_add_rmsnorm_fp8_block_quant(x3, r3, w3, 1e-6, out=q3, block_scale=s3,
+                                                normed_out=n3)), b3 + 2 * t3 * h3, flush, reps)
+    del x3, r3, q3, s3, n3
+
+    for bc in (False, True):
+        c5 = W.ada(broadcast=bc)
+        x5, r5, g5, w5, st5 = (c5.tensors[k].to(dev) for k in ("x", "residual", "gate", "w",
+                                                                 "style"))
+        t5, d5 = x5.shape
+        q5 = torch.empty(x5.shape, dtype=torch.float8_e4m3fn, device=dev)
+        go5 = torch.empty_like(x5)
+        # read x, residual, gate and the style rows (scale, shift, gate chunks); write
+        # residual, FP8 out and gate_out
+        per_row = 2 * 3 * d5 * (t5 if not bc else 1)
+        b5 = (2 + 2 + 2 + 2 + 1 + 2) * t5 * d5 + per_row + 2 * d5 + 4
+        name = "ada_gated_fp8_" + ("broadcast_" if bc else "") + f"{t5}x{d5}"
+        out[name] = isolated(torch, lambda: dn.dn_gate_residual_ada_norm_fp8(
+            r5, x5, g5, w5, st5, scale, 1e-6, out=q5, gate_out=go5), b5, flush, reps)
+        del x5, r5, g5, st5, q5, go5
+    del flush
+    return out
+
+
 def run_layernorm_family(a) -> int:
     import torch
 
@@ -942,7 +1028,7 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom]}
 
-    ceiling = shard = None
+    ceiling = shard = configs = None
     if not a.step_only:
         print("[bench] copy ceiling and one GPU's shard of the training shape", file=sys.stderr,
               flush=True)
@@ -953,6 +1039,8 @@ def main(argv=None) -> int:
         for k, m in mix.items():
             kernels[k]["of_stream_ceiling"] = round(kernels[k]["GB/s"] / ceiling[m], 4)
         shard = shard_measurement(torch, dev, dn, W)
+        print("[bench] the other configurations, isolated", file=sys.stderr, flush=True)
+        configs = config_measurements(torch, dev, dn, W)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -972,7 +1060,8 @@ def main(argv=None) -> int:
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "step_bytes": step_bytes, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "headline": headline,
-        "ceilings": ceiling, "shard_2048x8192": shard, "timing_events": _EVENT_KIND["kind"],
+        "ceilings": ceiling, "shard_2048x8192": shard, "isolated_configs": configs,
+        "timing_events": _EVENT_KIND["kind"],
     }
     print(json.dumps(line), flush=True)
     return 0
