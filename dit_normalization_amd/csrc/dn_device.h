@@ -204,32 +204,96 @@ __device__ __forceinline__ float sumsq8(const float f[8]) {
   return (s01 + s23) + (s45 + s67);
 }
 
-// The same sum carried to FP64, exact-product safe for any BF16 input: when an FP32 square
-// or the tree overflows (|value| above ~6.5e18) the eight squares are summed in FP64
-// instead (a branch no realistic activation takes).
-__device__ __forceinline__ double sumsq8_d(const float f[8]) {
+// Two cases where the FP32 tree is not good enough: an FP32 square or the tree overflows
+// (|value| above ~6.5e18; no realistic activation), or squares below 2^-126 lose bits to
+// FP32 underflow and eps is too small (below 2^-80) to make that loss negligible next to
+// it.  Then the caller re-sums the row's vectors with sumsq8_f64 (exact products, FP64
+// sums).  sumsq8_flag returns the tree in FP64 and raises `big` on overflow (or NaN); the
+// callers start `big` at (eps < 2^-80) and vote once per step (any_lane(big)), so the FP64
+// re-sum is a branch the wave skips, not a per-vector select that every lane pays for.
+__device__ __forceinline__ double sumsq8_flag(const float f[8], bool& big) {
   const float t = sumsq8(f);
-  if (__builtin_expect(t <= 3.0e38f, 1)) return (double)t;
+  big |= !(t <= 3.0e38f);
+  return (double)t;
+}
+__device__ __forceinline__ double sumsq8_f64(const float f[8]) {
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) s = fma((double)f[k], (double)f[k], s);
   return s;
 }
+// True on every lane when `flag` is set on any active lane of the wave.
+__device__ __forceinline__ bool any_lane(bool flag) {
+  return __builtin_amdgcn_ballot_w64(flag) != 0;
+}
 
-// Butterfly sum over aligned groups of WIDTH lanes (WIDTH a power of two <= 64).  Addition
-// is commutative, so every lane of a group ends with the same bits.
+// ------------------------------------------------------------------ cross-lane sums
+// Partner exchanges on the VALU only, no LDS round trip: DPP quad permutations and row
+// mirrors inside a 16-lane row, and gfx950's permute-swap instructions between rows (they
+// hand both lanes of a lane ^ 16 or lane ^ 32 pair the pair's two values, lower lane first).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ double make_f64(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Step M (1, 2, 4, 8, 16, 32) of a group sum: v plus the value of the partner lane, where
+// after steps 1 .. M/2 every lane holds the sum of its aligned group of M lanes and the
+// partner holds the sum of the neighbouring group: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror, then the row swaps.  Both lanes of a pair add the
+// same two operands (addition commutes), so the whole group ends with the same bits.
+template <int M>
+__device__ __forceinline__ double add_partner(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  if constexpr (M <= 8) {
+    constexpr int C = M == 1 ? 0xB1 : (M == 2 ? 0x4E : (M == 4 ? 0x141 : 0x140));
+    return v + make_f64(dpp_u32<C>(lo), dpp_u32<C>(hi));
+  } else if constexpr (M == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    return make_f64(a[0], b[0]) + make_f64(a[1], b[1]);
+  } else {
+    static_assert(M == 32, "group steps go up to 32");
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    return make_f64(a[0], b[0]) + make_f64(a[1], b[1]);
+  }
+}
+
+// Sum over aligned groups of WIDTH lanes (WIDTH a power of two <= 64); every lane of a
+// group ends with the same bits.
 template <int WIDTH>
 __device__ __forceinline__ double group_sum(double v) {
-#pragma unroll
-  for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  static_assert(WIDTH >= 1 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "power of two");
+  if constexpr (WIDTH >= 2) v = add_partner<1>(v);
+  if constexpr (WIDTH >= 4) v = add_partner<2>(v);
+  if constexpr (WIDTH >= 8) v = add_partner<4>(v);
+  if constexpr (WIDTH >= 16) v = add_partner<8>(v);
+  if constexpr (WIDTH >= 32) v = add_partner<16>(v);
+  if constexpr (WIDTH >= 64) v = add_partner<32>(v);
   return v;
 }
 
-template <int WIDTH>
-__device__ __forceinline__ float group_sum_f(float v) {
-#pragma unroll
-  for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+// FP32(1 / sqrt(x)) for the statistics: the hardware FP64 reciprocal square root (relative
+// error below 2^-24, measured) refined by two Newton steps (below 2^-52, measured over 4M
+// inputs spanning 1e-300 .. 1e301), as close as an IEEE square root followed by an IEEE
+// divide, for a fraction of their instructions.  Inputs outside [2^-1000, 2^1000], zero,
+// infinity and NaN included, take the IEEE path; the test is a wave vote, so the wave
+// branches round it unless one of its lanes needs it.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  const bool plain = x >= 0x1p-1000 && x <= 0x1p1000;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!plain) == 0, 1)) {
+    double y = __builtin_amdgcn_rsq(x);
+    y = fma(0.5 * y, fma(-x * y, y, 1.0), y);
+    y = fma(0.5 * y, fma(-x * y, y, 1.0), y);
+    return y;
+  }
+  asm volatile("");   // keeps the IEEE path behind the branch, not evaluated and selected
+  return 1.0 / sqrt(x);
 }
 
 // Maximum over each aligned group of 16 lanes (one DPP row) with four VALU moves and no
@@ -245,13 +309,6 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm [2, 3, 0, 1]
   v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
   v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
-  return v;
-}
-
-template <int WIDTH>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
 }
 

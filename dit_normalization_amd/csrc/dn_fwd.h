@@ -337,6 +337,9 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     const int64_t first = geo.first(base);
     // 2) h (rounded to BF16, stored early) and per-lane sums of squares of that BF16 h.
     double ss[R], s1[R];
+    // Set when this lane's FP32 trees are not to be trusted: a tree overflowed, or eps is
+    // so small (below 2^-80) that squares lost to FP32 underflow could matter.
+    bool big = p.eps < 0x1p-80f;
     {
       rsrc_t rh[R];
       uint32_t oh[R];
@@ -387,13 +390,29 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
               ss[rr] = fma(d, d, ss[rr]);
             }
           } else {
-            ss[rr] += sumsq8_d(fh);
+            ss[rr] += sumsq8_flag(fh, big);
+          }
+        }
+      }
+    }
+    if constexpr (!kLN) {
+      if (__builtin_expect(any_lane(big), 0)) {
+        asm volatile("");   // keeps the re-sum behind the branch
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          ss[rr] = 0.0;
+#pragma unroll
+          for (int v = 0; v < VMAX; ++v) {
+            float fh[8];
+            unpack8(st.a[rr][v], fh);
+            ss[rr] += sumsq8_f64(fh);
           }
         }
       }
     }
 
-    // 3) Row sums: butterfly inside the wave, then (rows over several waves) through LDS.
+    // 3) Row sums: DPP / row-swap steps inside the wave, then (rows over several waves)
+    //    through LDS.
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
@@ -430,7 +449,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 
     // 4) RMSNorm: rstd = 1/sqrt(mean square + eps).  LayerNorm: mean = sum/H, variance =
     //    (sum of squares)/H - mean^2 (population variance), rstd = 1/sqrt(var + eps).
-    //    IEEE FP64 divide and square root, one FP32 rounding of each result.
+    //    FP64 throughout (rsqrt_f64: within 2^-52), one FP32 rounding of each result.
     float rs[R], mu[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
@@ -439,10 +458,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const double mean = s1[rr] / (double)p.hidden;
         double var = ss[rr] / (double)p.hidden - mean * mean;
         var = var > 0.0 ? var : 0.0;
-        r64 = 1.0 / sqrt(var + eps);
+        r64 = rsqrt_f64(var + eps);
         mu[rr] = (float)mean;
       } else {
-        r64 = 1.0 / sqrt(ss[rr] * inv_hidden + eps);
+        r64 = rsqrt_f64(ss[rr] * inv_hidden + eps);
         mu[rr] = 0.0f;
       }
       rs[rr] = (float)r64;

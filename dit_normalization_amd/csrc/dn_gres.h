@@ -46,7 +46,23 @@ __device__ __forceinline__ void gres_weight8(const void* w, int f32, float bias,
   for (int k = 0; k < 8; ++k) e[k] += bias;
 }
 
-// Sum of a per-lane FP64 value over the row: butterfly, then LDS across the row's waves
+// A lane's FP64 sums of squares of its row vectors, for the rare step where an FP32 tree
+// overflowed (sumsq8_flag).
+template <int R, int VMAX>
+__device__ __forceinline__ void gres_sumsq_f64(const v4u (&vals)[R][VMAX], double (&ss)[R]) {
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    ss[rr] = 0.0;
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) {
+      float f[8];
+      unpack8(vals[rr][v], f);
+      ss[rr] += sumsq8_f64(f);
+    }
+  }
+}
+
+// Sum of a per-lane FP64 value over the row: group_sum in the wave, then LDS across the row's waves
 // (slot set `s` of this step's parity).
 template <int RW, int WPR, int R, int G>
 __device__ __forceinline__ void gres_row_sum(double (&v)[R], double* slots, int parity,
@@ -140,6 +156,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
 
     // rstd of the branch
     double ss[R];
+    bool big = p.eps < 0x1p-80f;   // as in the forward kernel: overflow or a tiny eps
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       ss[rr] = 0.0;
@@ -147,18 +164,23 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
       for (int v = 0; v < VMAX; ++v) {
         float f[8];
         unpack8(vb[rr][v], f);
-        ss[rr] += sumsq8_d(f);
+        ss[rr] += sumsq8_flag(f, big);
       }
 #pragma unroll
       for (int v = 0; v < VMAX; ++v) keep_packed(vb[rr][v]);
     }
+    if (__builtin_expect(any_lane(big), 0)) {
+      asm volatile("");   // keeps the re-sum behind the branch
+      gres_sumsq_f64<R, VMAX>(vb, ss);
+    }
     gres_row_sum<RW, WPR, R, G>(ss, red, parity, geo.grp, lane);
     float rs[R];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) rs[rr] = (float)(1.0 / sqrt(ss[rr] * inv_hidden + eps));
+    for (int rr = 0; rr < R; ++rr) rs[rr] = (float)rsqrt_f64(ss[rr] * inv_hidden + eps);
 
     // h = BF16(FMA(gate, n, residual)), stored over the residual; kept for the next norm
     double s2[R];
+    bool big2 = p.eps < 0x1p-80f;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       s2[rr] = 0.0;
@@ -186,7 +208,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
           vb[rr][v] = hp;            // the BF16 stream, for the next norm
           float fh[8];
           unpack8(hp, fh);
-          s2[rr] += sumsq8_d(fh);
+          s2[rr] += sumsq8_flag(fh, big2);
         }
       }
     }
@@ -197,6 +219,10 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
 #pragma unroll
         for (int v = 0; v < VMAX; ++v) keep_packed(vb[rr][v]);
       }
+      if (__builtin_expect(any_lane(big2), 0)) {
+        asm volatile("");   // keeps the re-sum behind the branch
+        gres_sumsq_f64<R, VMAX>(vb, s2);
+      }
       gres_row_sum<RW, WPR, R, G>(s2, red2, parity, geo.grp, lane);
       rsrc_t ry[R];
       uint32_t oy[R];
@@ -204,7 +230,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
                                lane_ok, ry, oy);
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        const float r2 = (float)(1.0 / sqrt(s2[rr] * inv_hidden + eps));
+        const float r2 = (float)rsqrt_f64(s2[rr] * inv_hidden + eps);
 #pragma unroll
         for (int v = 0; v < VMAX; ++v) {
           __builtin_amdgcn_sched_barrier(0);
