@@ -337,9 +337,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     const int64_t first = geo.first(base);
     // 2) h (rounded to BF16, stored early) and per-lane sums of squares of that BF16 h.
     double ss[R], s1[R];
-    // Set when this lane's FP32 trees are not to be trusted: a tree overflowed, or eps is
-    // so small (below 2^-80) that squares lost to FP32 underflow could matter.
-    bool big = p.eps < 0x1p-80f;
+    const bool tiny_eps = p.eps < 0x1p-80f;   // sums of squares in FP64 (sumsq8_d)
     {
       rsrc_t rh[R];
       uint32_t oh[R];
@@ -390,27 +388,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
               ss[rr] = fma(d, d, ss[rr]);
             }
           } else {
-            ss[rr] += sumsq8_flag(fh, big);
+            ss[rr] += sumsq8_d(fh, tiny_eps);
           }
         }
       }
     }
-    if constexpr (!kLN) {
-      if (__builtin_expect(any_lane(big), 0)) {
-        asm volatile("");   // keeps the re-sum behind the branch
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          ss[rr] = 0.0;
-#pragma unroll
-          for (int v = 0; v < VMAX; ++v) {
-            float fh[8];
-            unpack8(st.a[rr][v], fh);
-            ss[rr] += sumsq8_f64(fh);
-          }
-        }
-      }
-    }
-
     // 3) Row sums: DPP / row-swap steps inside the wave, then (rows over several waves)
     //    through LDS.
 #pragma unroll

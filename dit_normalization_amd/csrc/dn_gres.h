@@ -46,22 +46,6 @@ __device__ __forceinline__ void gres_weight8(const void* w, int f32, float bias,
   for (int k = 0; k < 8; ++k) e[k] += bias;
 }
 
-// A lane's FP64 sums of squares of its row vectors, for the rare step where an FP32 tree
-// overflowed (sumsq8_flag).
-template <int R, int VMAX>
-__device__ __forceinline__ void gres_sumsq_f64(const v4u (&vals)[R][VMAX], double (&ss)[R]) {
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    ss[rr] = 0.0;
-#pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
-      float f[8];
-      unpack8(vals[rr][v], f);
-      ss[rr] += sumsq8_f64(f);
-    }
-  }
-}
-
 // Sum of a per-lane FP64 value over the row: group_sum in the wave, then LDS across the row's waves
 // (slot set `s` of this step's parity).
 template <int RW, int WPR, int R, int G>
@@ -156,7 +140,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
 
     // rstd of the branch
     double ss[R];
-    bool big = p.eps < 0x1p-80f;   // as in the forward kernel: overflow or a tiny eps
+    const bool tiny_eps = p.eps < 0x1p-80f;   // sums of squares in FP64 (sumsq8_d)
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       ss[rr] = 0.0;
@@ -164,14 +148,10 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
       for (int v = 0; v < VMAX; ++v) {
         float f[8];
         unpack8(vb[rr][v], f);
-        ss[rr] += sumsq8_flag(f, big);
+        ss[rr] += sumsq8_d(f, tiny_eps);
       }
 #pragma unroll
       for (int v = 0; v < VMAX; ++v) keep_packed(vb[rr][v]);
-    }
-    if (__builtin_expect(any_lane(big), 0)) {
-      asm volatile("");   // keeps the re-sum behind the branch
-      gres_sumsq_f64<R, VMAX>(vb, ss);
     }
     gres_row_sum<RW, WPR, R, G>(ss, red, parity, geo.grp, lane);
     float rs[R];
@@ -180,7 +160,6 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
 
     // h = BF16(FMA(gate, n, residual)), stored over the residual; kept for the next norm
     double s2[R];
-    bool big2 = p.eps < 0x1p-80f;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       s2[rr] = 0.0;
@@ -208,7 +187,7 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
           vb[rr][v] = hp;            // the BF16 stream, for the next norm
           float fh[8];
           unpack8(hp, fh);
-          s2[rr] += sumsq8_flag(fh, big2);
+          s2[rr] += sumsq8_d(fh, tiny_eps);
         }
       }
     }
@@ -218,10 +197,6 @@ __global__ void __launch_bounds__(NT) gres_kernel(const GresParams p) {
       for (int rr = 0; rr < R; ++rr) {
 #pragma unroll
         for (int v = 0; v < VMAX; ++v) keep_packed(vb[rr][v]);
-      }
-      if (__builtin_expect(any_lane(big2), 0)) {
-        asm volatile("");   // keeps the re-sum behind the branch
-        gres_sumsq_f64<R, VMAX>(vb, s2);
       }
       gres_row_sum<RW, WPR, R, G>(s2, red2, parity, geo.grp, lane);
       rsrc_t ry[R];

@@ -207,34 +207,18 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
 
     // 3) Sums of squares of the Q and K channels.
     double sq = 0.0, sk = 0.0;
-    bool big = p.eps < 0x1p-80f;   // as in the forward kernel: overflow or a tiny eps
+    const bool tiny_eps = p.eps < 0x1p-80f;   // sums of squares in FP64 (sumsq8_d)
 #pragma unroll
     for (int m = 0; m < UMAX; ++m) {
       float f[8];
       unpack8(va[m], f);
-      double s = sumsq8_flag(f, big);
+      double s = sumsq8_d(f, tiny_eps);
       if constexpr (NEOX) {
         unpack8(vb[m], f);
-        s += sumsq8_flag(f, big);
+        s += sumsq8_d(f, tiny_eps);
       }
       sq += ucls[m] == 0 ? s : 0.0;
       sk += ucls[m] == 1 ? s : 0.0;
-    }
-    if (__builtin_expect(any_lane(big), 0)) {
-      asm volatile("");   // keeps the re-sum behind the branch
-      sq = sk = 0.0;
-#pragma unroll
-      for (int m = 0; m < UMAX; ++m) {
-        float f[8];
-        unpack8(va[m], f);
-        double s = sumsq8_f64(f);
-        if constexpr (NEOX) {
-          unpack8(vb[m], f);
-          s += sumsq8_f64(f);
-        }
-        sq += ucls[m] == 0 ? s : 0.0;
-        sk += ucls[m] == 1 ? s : 0.0;
-      }
     }
     sq = group_sum<RW>(sq);
     sk = group_sum<RW>(sk);
