@@ -118,7 +118,7 @@ dn_status check_f32(const void* p, const char* name, bool required) {
 struct DeviceCache {
   std::mutex mu;
   std::map<int, int> cus;
-  std::map<std::tuple<int, const void*, size_t>, int> occ;
+  std::map<std::tuple<int, const void*, size_t, int>, int> occ;
 };
 
 DeviceCache& cache() {
@@ -139,7 +139,7 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int cap, int* 
       return fail(DN_ERR_HIP, "cannot read the compute-unit count of device %d", dev);
     it = c.cus.emplace(dev, n).first;
   }
-  const auto key = std::make_tuple(dev, kernel, lds);
+  const auto key = std::make_tuple(dev, kernel, lds, cap);
   auto ot = c.occ.find(key);
   if (ot == c.occ.end()) {
     int per_cu = 0;

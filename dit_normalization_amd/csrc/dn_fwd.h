@@ -613,7 +613,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(fn[k]));
           amax = row16_max(amax);               // one 1x128 block = 16 lanes x 8 values
-          const float s = amax / kE4M3Max;      // IEEE divide: FP32(amax / 448)
+          const float s = div_by_448(amax);     // FP32(amax / 448), correctly rounded
           // n / s as n * (1/s) on the hardware reciprocal (within 2 FP32 ulps).  Blocks with
           // a scale below 2^-100 (normalised values below ~1e-28) are scaled by 2^100 on
           // both sides first, so 1/s neither overflows nor leaves the normal range.
