@@ -81,8 +81,9 @@ SIGNATURES = {
 }
 
 
-class DnormError(RuntimeError):
-    """A dnorm call was rejected (bad shape, dtype, alignment, workspace) or failed."""
+class DnormError(ValueError, RuntimeError):
+    """A dnorm call was rejected (bad shape, dtype, alignment, workspace: a ValueError naming
+    the broken rule, as the norm docs' Python API raises) or failed on the device."""
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -362,8 +363,13 @@ def _bwd_common(g, x, w, rstd, g_residual, dx):
 
 
 def dn_train_backward(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, workspace=None,
-                      dx=None, dw=None):
-    """(dx, dw): dx BF16 like x, dw FP32 [hidden], deterministic."""
+                      dx=None, dw=None, deterministic: bool = True):
+    """(dx, dw): dx BF16 like x, dw FP32 [hidden], bitwise deterministic.  Only the
+    deterministic dw reduction exists; deterministic=False is rejected (cake bwd docs,
+    Parameters: deterministic)."""
+    if not deterministic:
+        raise DnormError("deterministic=False is not supported: dw is always reduced in a "
+                         "fixed order (bitwise reproducible)")
     gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr = _bwd_common(g, x, w, rstd, g_residual, dx)
     H = xr.size(-1)
     if workspace is None:

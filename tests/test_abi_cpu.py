@@ -168,6 +168,14 @@ def test_train_checks(lib):
     assert r(A, B, ws // 2, 5, 8192, None) == E_WS
 
 
+def test_binding_rejects_a_nondeterministic_backward(dn):
+    """The pages' backward takes deterministic=True only; the binding refuses False before
+    it looks at any tensor, with a ValueError naming the rule."""
+    with pytest.raises(ValueError, match="deterministic"):
+        dn.dn_train_backward(None, None, None, None, deterministic=False)
+    assert issubclass(dn.DnormError, ValueError)
+
+
 def test_layernorm_checks(lib):
     ln = lib.dn_layernorm
     assert ln(A, 3072, B, 3072, C, D, 0, 3072, 1e-6, None) == OK
