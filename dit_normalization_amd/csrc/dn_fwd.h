@@ -194,11 +194,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   // Rows are held packed (BF16 pairs) across the reduction and unpacked again for the
   // epilogue, halving their register footprint, except where the unpacked row fits
   // comfortably: a single input of at most four vectors per lane and row.
-#ifdef DN_ALWAYS_PACK
-  constexpr bool kPackAcross = true;
-#else
   constexpr bool kPackAcross = !(IN == IN_PLAIN && !kAda && !kMod && VMAX * R <= 4);
-#endif
 
   const Geom geo;
   const int tid = threadIdx.x;
@@ -214,11 +210,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   // Static FP8 without a modulation: the reciprocal scale is folded into the staged
   // per-column parameters (w_eff / scale; gamma / scale and beta / scale), one multiply
   // per element fewer in the epilogue.
-#ifdef DN_NO_FOLD_SCALE
-  constexpr bool kFold = false;
-#else
   constexpr bool kFold = (EPI == EPI_FP8 || EPI == EPI_LN_FP8);
-#endif
   double* red = reinterpret_cast<double*>(dn_lds + (p.w_in_lds ? (size_t)16 * kPlanes * nvec : 0));
 
   // Per-block set-up (staged per-column parameters, block-scale padding).  It runs after
@@ -373,9 +365,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           if constexpr (IN != IN_PLAIN) {
             st.a[rr][v] = pack8(fh);
             unpack8(st.a[rr][v], fh);       // the norm sees the BF16 h_new
-#ifndef DN_LATE_H_STORE
             bstore16(rh[rr], oh[rr] + (uint32_t)(v * TPR * 16), st.a[rr][v]);
-#endif
           }
           // Lanes past the row end loaded zeros: they add nothing.
           if constexpr (kLN) {
@@ -475,24 +465,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         // The per-column parameters are the same for every row, so the compiler would keep
         // them in VGPRs across the row loop.  LayerNorm's gamma and beta take 8 VGPRs per
         // vector: 1024-thread blocks (128 VGPRs a lane) re-read them from LDS instead.
-#ifdef DN_LN_NO_HOIST
-        constexpr bool kReread = kLN;
-#else
         constexpr bool kReread = kLN && NT >= 1024;
-#endif
         if constexpr (kReread) asm volatile("" : "+v"(widx));
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
-#ifdef DN_LATE_H_STORE
-        if constexpr (IN != IN_PLAIN) {
-          rsrc_t rh[R];
-          uint32_t oh[R];
-          tensor_span<TPR, R, RPW>(p.h, p.sh, 2, 16, p.h ? row_bf16 : 0u, first,
-                                   p.h ? p.rows : first, lane, geo.j, lane_ok, rh, oh);
-          bstore16(rh[rr], oh[rr] + d16, st.a[rr][v]);
-        }
-#endif
         unpack8(st.a[rr][v], fh);
         if constexpr (kLN) {
           // n = (h - mean) * rstd in FP32, then one FMA with gamma and beta (or with the
