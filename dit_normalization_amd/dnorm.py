@@ -131,14 +131,27 @@ def _rows(t: torch.Tensor, name: str, dtype=torch.bfloat16):
         t = t.unsqueeze(0)
     ok = t.stride(-1) == 1 and all(
         t.stride(i) == t.stride(i + 1) * t.size(i + 1) for i in range(t.dim() - 2))
-    if not ok or (t.dim() >= 2 and t.size(-2) > 1 and t.stride(-2) % 8 != 0) or \
-            t.data_ptr() % 16 != 0:
+    if not ok or (t.dim() >= 2 and t.size(-2) > 1 and t.stride(-2) % 8 != 0):
         t = t.contiguous()
+    if t.data_ptr() % 16 != 0:
+        t = t.clone()             # a fresh (aligned) allocation, even for a contiguous view
     rows = 1
     for s in t.shape[:-1]:
         rows *= s
     stride = t.stride(-2) if t.dim() >= 2 and t.size(-2) > 1 else t.size(-1)
     return t, rows, stride
+
+
+def _rstd_buffer(rstd, rows: int, device, name: str = "rstd"):
+    """A caller's FP32 rstd output (or input): one contiguous float32 value per row on the
+    activations' device.  None passes through."""
+    if rstd is None:
+        return None
+    if rstd.dtype != torch.float32 or not rstd.is_contiguous() or rstd.numel() != rows or \
+            rstd.device != device:
+        raise DnormError(f"{name} must be a contiguous float32 tensor of {rows} values on "
+                         f"{device} (got {rstd.dtype}, {tuple(rstd.shape)}, {rstd.device})")
+    return rstd
 
 
 def _weight(w: torch.Tensor):
@@ -183,6 +196,7 @@ def dn_rmsnorm(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=None, rstd=N
     yr, _, sy = _rows(y, "out")
     if return_rstd and rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _rstd_buffer(rstd, rows, x.device)
     _check(lib.dn_rmsnorm(yr.data_ptr(), sy, _ptr(rstd), xr.data_ptr(), sx, w.data_ptr(), wcode,
                           w_bias, rows, H, eps, _stream(x)), "dn_rmsnorm")
     _writeback(y, yr)
@@ -213,6 +227,7 @@ def dn_fused_add_rmsnorm(x, residual, w, eps: float = 1e-6, *, w_bias: float = 0
     if rows_r != rows or rr.size(-1) != xr.size(-1):
         raise DnormError("x and residual must have the same shape")
     w, wcode = _weight(w)
+    _rstd_buffer(rstd, rows, x.device)
     _check(lib.dn_fused_add_rmsnorm(xr.data_ptr(), sx, rr.data_ptr(), sr, w.data_ptr(), wcode,
                                     w_bias, _ptr(rstd), rows, xr.size(-1), eps, _stream(x)),
            "dn_fused_add_rmsnorm")
@@ -321,6 +336,7 @@ def dn_train_forward(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, residual=N
     yr, _, sy = _rows(y, "out")
     if rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _rstd_buffer(rstd, rows, x.device)
     hr, sh, rsr, srs = None, 0, None, 0
     if residual is not None:
         rsr, _, srs = _rows(residual, "residual")
@@ -352,8 +368,9 @@ def _bwd_common(g, x, w, rstd, g_residual, dx):
     gr, rows, sg = _rows(g, "g")
     xr, _, sx = _rows(x, "x")
     w, wcode = _weight(w)
-    if rstd.dtype != torch.float32 or not rstd.is_contiguous():
-        raise DnormError("rstd must be a contiguous float32 tensor")
+    if rstd is None:
+        raise DnormError("rstd (the forward's FP32 per-row output) is required")
+    _rstd_buffer(rstd, rows, g.device)
     d = dx if dx is not None else _out_like(x, x.shape, torch.bfloat16)
     dr, _, sd = _rows(d, "dx")
     grr, sgr = None, 0

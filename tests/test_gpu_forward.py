@@ -80,6 +80,24 @@ def test_rmsnorm_page_grid_rows_and_strides(dn, hidden, pad):
         assert_rstd(rstd, ref.r64)
 
 
+def test_misaligned_views_are_copied_once(dn):
+    """A view whose base is not 16-byte aligned (one element into a buffer) is read through
+    one aligned copy; an output view like that receives the result through a copy back."""
+    x = W.normal((19, 512), 19, 0)
+    w = W.normal((512,), 19, 1)
+    buf = torch.empty(19 * 512 + 1, dtype=torch.bfloat16, device="cuda")
+    xv = buf[1:].view(19, 512)
+    xv.copy_(dev(x))
+    assert xv.data_ptr() % 16 != 0 and xv.is_contiguous()
+    obuf = torch.zeros(19 * 512 + 3, dtype=torch.bfloat16, device="cuda")
+    ov = obuf[3:].view(19, 512)
+    y = dn.dn_rmsnorm(xv, dev(w), 1e-6, out=ov)
+    ref = O.rmsnorm(values(x), values(w), 0.0, 1e-6)
+    assert y.data_ptr() == ov.data_ptr()
+    assert_bf16(ov, ref.y_exact, "misaligned in and out")
+    assert torch.equal(obuf[:3], torch.zeros(3, dtype=torch.bfloat16, device="cuda"))
+
+
 @pytest.mark.parametrize("rows", [16172, 16231])
 def test_rmsnorm_page_grid_large_rows(dn, rows):
     x = W.normal((rows, 2048), 17, rows)
