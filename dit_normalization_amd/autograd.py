@@ -36,8 +36,9 @@ class RMSNormTrainFunction(torch.autograd.Function):
         gh = grads[1] if ctx.residual and len(grads) > 1 else None
         if gy is None:
             gy = torch.zeros_like(x)
-        dx, dw = dn.dn_train_backward(gy.contiguous(), x, w, rstd.contiguous(), w_bias=ctx.w_bias,
-                                      g_residual=None if gh is None else gh.contiguous())
+        # Gradients are read in place when their rows are addressable (row-strided views
+        # included); broadcast or transposed ones are copied once by the binding.
+        dx, dw = dn.dn_train_backward(gy, x, w, rstd, w_bias=ctx.w_bias, g_residual=gh)
         dw = dw.to(w.dtype)
         if ctx.residual:
             return dx, dw, None, None, dx

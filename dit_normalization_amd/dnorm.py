@@ -131,7 +131,11 @@ def _rows(t: torch.Tensor, name: str, dtype=torch.bfloat16):
         t = t.unsqueeze(0)
     ok = t.stride(-1) == 1 and all(
         t.stride(i) == t.stride(i + 1) * t.size(i + 1) for i in range(t.dim() - 2))
-    if not ok or (t.dim() >= 2 and t.size(-2) > 1 and t.stride(-2) % 8 != 0):
+    if t.dim() >= 2 and t.size(-2) > 1:
+        # rows must not overlap (a broadcast gradient has row stride 0) and must keep
+        # 16-byte alignment from one to the next
+        ok = ok and t.stride(-2) >= t.size(-1) and t.stride(-2) % 8 == 0
+    if not ok:
         t = t.contiguous()
     if t.data_ptr() % 16 != 0:
         t = t.clone()             # a fresh (aligned) allocation, even for a contiguous view

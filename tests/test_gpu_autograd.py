@@ -87,3 +87,26 @@ def test_autograd_3d_input(ag):
     assert_bf16(y.detach().reshape(-1, 1024), fwd.y_exact, "y 3d")
     ref = O.train_backward(g2, x2, values(w0), fwd.rstd, 0.0)
     assert_dx(x.grad.reshape(-1, 1024), ref.dx_exact, "x.grad 3d")
+
+
+def test_autograd_broadcast_and_strided_gradients(ag):
+    """y.sum() hands the backward an expanded gradient (row stride 0), which is copied once;
+    a gradient that is a row-strided slice of a wider buffer is read in place.  Both must
+    give the oracle's gradients."""
+    x0 = W.normal((70, 512), 42, 0)
+    w0 = W.normal((512,), 42, 1, mean=1.0, std=0.1)
+    x = dev(x0).requires_grad_(True)
+    w = dev(w0).requires_grad_(True)
+    ag.rmsnorm_train(x, w, 1e-6).sum().backward()
+    ones = np.ones((70, 512))
+    fwd = O.train_forward(values(x0), values(w0), 0.0, 1e-6)
+    ref = O.train_backward(ones, values(x0), values(w0), fwd.rstd, 0.0)
+    assert_dx(x.grad, ref.dx_exact, "x.grad from y.sum()")
+
+    g_wide = W.normal((70, 640), 42, 2)
+    gv = dev(g_wide)[:, 64:576]            # row stride 640, 16-byte aligned start
+    x.grad = None
+    y = ag.rmsnorm_train(x, w, 1e-6)
+    y.backward(gv)
+    ref2 = O.train_backward(values(g_wide)[:, 64:576], values(x0), values(w0), fwd.rstd, 0.0)
+    assert_dx(x.grad, ref2.dx_exact, "x.grad from a strided gradient")
