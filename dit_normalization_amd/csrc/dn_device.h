@@ -50,11 +50,13 @@ __device__ __forceinline__ v4u pack8(const float f[8]) {
 // Largest finite e4m3fn magnitude; inputs are clamped to it first so every out-of-range
 // value saturates (v_med3_f32), then converted with round-to-nearest-even
 // (v_cvt_pk_fp8_f32: two values into one 16-bit half of a dword, first operand in the
-// lower byte).
+// lower byte).  The clamp follows IEEE minNum/maxNum and would turn a NaN into a finite
+// value, so NaN bypasses it and converts to the e4m3fn NaN.
 constexpr float kE4M3Max = 448.0f;
 
 __device__ __forceinline__ float clamp_e4m3(float v) {
-  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+  const float c = __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+  return v == v ? c : v;
 }
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {

@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
       if constexpr (kLN) {
         const double mean = s1[rr] / (double)p.hidden;
         double var = ss[rr] / (double)p.hidden - mean * mean;
-        var = var > 0.0 ? var : 0.0;
+        var = var < 0.0 ? 0.0 : var;   // rounding can leave -0.x ulp; NaN stays NaN
         r64 = rsqrt_f64(var + eps);
         mu[rr] = (float)mean;
       } else {

@@ -1,0 +1,109 @@
+"""Non-finite inputs propagate as IEEE arithmetic says, on the GPU as in the FP64 oracle: a
+row holding an infinity has rstd 0 and NaN where 0 * inf is taken, a row holding a NaN is
+NaN throughout, and the other rows of the call are untouched by them.  The pages define no
+special case, so the oracle's plain FP64 evaluation is the reference: NaN positions must
+agree, infinities must agree, and every finite value passes the usual gates."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import layernorm as L
+from oracle import rmsnorm as O
+from tests.conftest import bits8, values
+from tests.parity import assert_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dn():
+    from dit_normalization_amd import dnorm
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return dnorm
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def with_specials(rows, hidden, seed):
+    """BF16 rows; row 1 holds +inf, row 2 -inf, row 3 a NaN, row 4 +inf and -inf."""
+    x = W.normal((rows, hidden), seed, 0).float()
+    x[1, 3] = float("inf")
+    x[2, hidden - 1] = float("-inf")
+    x[3, hidden // 2] = float("nan")
+    x[4, 0], x[4, 1] = float("inf"), float("-inf")
+    return x.to(torch.bfloat16)
+
+
+def assert_bf16_nonfinite(gpu, ref_exact, what):
+    g = values(gpu).reshape(ref_exact.shape)
+    r = ref_exact
+    assert (np.isnan(g) == np.isnan(r)).all(), f"{what}: NaN positions differ"
+    inf = np.isinf(r)
+    assert (g[inf] == r[inf]).all() and (np.isinf(g) == inf).all(), f"{what}: infinities differ"
+    fin = np.isfinite(r)
+    assert_bf16(gpu.reshape(-1)[torch.as_tensor(np.flatnonzero(fin), device=gpu.device)],
+                r[fin], what)
+
+
+@pytest.mark.parametrize("hidden", [128, 4096])
+def test_rmsnorm_and_rstd_with_infinities_and_nans(dn, hidden):
+    x = with_specials(9, hidden, 401)
+    w = W.normal((hidden,), 401, 1, mean=1.0, std=0.1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.rmsnorm(values(x), values(w), 0.0, 1e-6)
+    y, rstd = dn.dn_rmsnorm(dev(x), dev(w), 1e-6, return_rstd=True)
+    assert_bf16_nonfinite(y, ref.y_exact, f"y H={hidden}")
+    r = rstd.cpu().double().numpy()
+    assert (np.isnan(r) == np.isnan(ref.r64)).all()
+    ok = np.isfinite(ref.r64)
+    assert (r[~ok & ~np.isnan(ref.r64)] == ref.r64[~ok & ~np.isnan(ref.r64)]).all()
+    assert np.all(np.abs(r[ok] - ref.r64[ok]) <= 2e-7 * np.abs(ref.r64[ok]))
+
+
+def test_fused_add_with_opposite_infinities(dn):
+    x = with_specials(9, 1024, 402)
+    r = W.normal((9, 1024), 402, 1).float()
+    r[5, 7] = float("inf")
+    r = r.to(torch.bfloat16)
+    x2 = x.float()
+    x2[5, 7] = float("-inf")                  # inf + (-inf) = NaN in h_new
+    x = x2.to(torch.bfloat16)
+    w = W.normal((1024,), 402, 2, mean=1.0, std=0.1)
+    xd, rd = dev(x), dev(r)
+    dn.dn_fused_add_rmsnorm(xd, rd, dev(w), 1e-6)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.fused_add_rmsnorm(values(x), values(r), values(w), 0.0, 1e-6)
+    h = values(rd)
+    assert (np.isnan(h) == np.isnan(ref.h_new)).all()
+    fin = ~np.isnan(ref.h_new)
+    assert (h[fin] == ref.h_new[fin]).all(), "h_new"
+    assert_bf16_nonfinite(xd, ref.norm.y_exact, "y")
+
+
+def test_static_fp8_with_infinities_and_nans(dn):
+    x = with_specials(9, 512, 403)
+    w = W.normal((512,), 403, 1, mean=1.0, std=0.1)
+    q = dn.dn_rmsnorm_quant(dev(x), dev(w), 0.04, 1e-6)
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, ref = O.rmsnorm_quant(values(x), values(w), 0.04, 0.0, 1e-6)
+    g = bits8(q).reshape(ref.q.shape)
+    nan_ref = np.isnan(ref.v)
+    assert (((g & 0x7F) == 0x7F) == nan_ref).all(), "e4m3 NaN codes"
+    ok = F.codes_equal_e4m3(g, ref.q) | ref.tie
+    assert ok[~nan_ref].all(), "e4m3 codes"
+
+
+def test_layernorm_with_infinities_and_nans(dn):
+    x = with_specials(9, 1024, 404)
+    g = W.normal((1024,), 404, 1, std=0.1, dtype=torch.float32) + 1.0
+    b = W.normal((1024,), 404, 2, std=0.1, dtype=torch.float32)
+    y = dn.dn_layernorm(dev(x), dev(g), dev(b), 1e-6)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = L.layernorm(values(x), g.double().numpy(), b.double().numpy(), 1e-6)
+    assert_bf16_nonfinite(y, ref.y_exact, "layernorm y")
