@@ -14,12 +14,14 @@
 //
 // The rotation angles depend only on the token and the pair index j < hd/2, not on the
 // head, so each step the row's lanes compute the token's hd/2 (cos, sin) pairs once and
-// share them through LDS.  The angle is the position times an FP64 inverse frequency,
-// reduced modulo 2*pi in FP64 (pi split in two parts), and its sine and cosine are taken
-// in FP32 on the reduced argument (|r| <= pi, where the FP32 routine is accurate to a few
-// ulp): as good as an FP64 sincos rounded to FP32 for this purpose, at a fraction of the
-// cost.  The inverse-frequency table itself (base^(-2i/count) per
-// frame / height / width channel group, with the YaRN blend) is built once per block.
+// share them through LDS.  The angle is kept in revolutions: the position times an FP64
+// inverse frequency over 2*pi, reduced to [-1/2, 1/2] by subtracting the nearest integer
+// (exact in FP64), rounded once to FP32, and handed to the hardware sine and cosine
+// (v_sin_f32 / v_cos_f32 take revolutions; measured within 1.3e-7 absolute over
+// [-1/2, 1/2], as close as an FP32 library sincos of the rounded angle).  Two
+// transcendental instructions per pair instead of a software sincos.  The
+// inverse-frequency table itself (base^(-2i/count) per frame / height / width channel
+// group, with the YaRN blend, divided by 2*pi) is built once per block.
 #pragma once
 
 #include "dn_device.h"
@@ -73,9 +75,7 @@ __device__ __forceinline__ void rope_weight8(const RopeParams& p, int vec, float
   }
 }
 
-// 2*pi as the sum of two doubles, and 1/(2*pi), for the FP64 argument reduction.
-constexpr double k2PiHi = 6.283185307179586232;
-constexpr double k2PiLo = 2.4492935982947064e-16;
+// 1/(2*pi), turning an angular frequency into revolutions per position.
 constexpr double kInv2Pi = 0.15915494309189535;
 
 template <int TPR, int VMAX, int NT, bool NEOX, bool FP8>
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
       ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
       f = f / p.factor * ramp + f * (1.0 - ramp);
     }
-    freq[j] = f;
+    freq[j] = f * kInv2Pi;    // revolutions per position
   }
   __syncthreads();
 
@@ -196,12 +196,10 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
       float2* tab = cs + ((size_t)parity * G + geo.grp) * half;
       for (int j = lane; j < half; j += TPR) {
         const double pos = j < p.cf / 2 ? pf : (j < (p.cf + p.ch) / 2 ? ph : pw);
-        const double th = pos * freq[j];
-        const double k = rint(th * kInv2Pi);
-        const double r = fma(-k, k2PiLo, fma(-k, k2PiHi, th));
-        float sn, cn;
-        sincosf((float)r, &sn, &cn);
-        tab[j] = make_float2(cn * cs_mul, sn * cs_mul);
+        const double rev = pos * freq[j];
+        const float x = (float)(rev - rint(rev));       // in [-1/2, 1/2] revolutions
+        tab[j] = make_float2(__builtin_amdgcn_cosf(x) * cs_mul,
+                             __builtin_amdgcn_sinf(x) * cs_mul);
       }
     }
 
