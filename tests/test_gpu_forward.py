@@ -159,6 +159,40 @@ def test_fp8_conversion_of_every_bf16_value(dn):
                                       f"first w={F.bf16_bits_to_f64(wb[bad])[0]!r}"
 
 
+def test_fp8_conversion_of_every_fp32_rounding_class(dn):
+    """FP32 weights make the value handed to the FP8 rounding any FP32 number (rows of a
+    power of two, eps = 0: x * r = +-1 exactly).  The e4m3fn code of an FP32 value depends
+    only on its binade, its leading mantissa bits and whether the bits below them are zero
+    (the sticky information), so every binade from the FP32 subnormals up to [512, 1024)
+    is fed its 32 five-bit mantissa heads, each with the bits below zero, one, all ones and
+    random: every rounding class of the conversion, ties and saturation included."""
+    rng = np.random.default_rng(31)
+    vals = []
+    for e in range(-150, 10):                  # e = -150: the FP32 subnormal binades
+        for head in range(32):
+            for low in (0, 1, (1 << 18) - 1, int(rng.integers(2, (1 << 18) - 1))):
+                mant = (head << 18) | low
+                if e == -150:
+                    v = np.float32(np.ldexp(float(mant), -149))        # subnormal pattern
+                else:
+                    v = np.float32(np.ldexp(1.0 + mant / 2.0 ** 23, e))
+                vals.append(v)
+    w32 = np.array(vals, dtype=np.float32)
+    hidden = 32768
+    assert w32.size <= hidden
+    w_pad = np.zeros(hidden, np.float32)
+    w_pad[:w32.size] = w32
+    w = torch.from_numpy(w_pad)
+    for scale in [1.0, 2.0 ** -6, 2.0 ** 5]:
+        x = torch.tensor([[0.5] * hidden, [-4.0] * hidden], dtype=torch.bfloat16)
+        q = bits8(dn.dn_rmsnorm_quant(dev(x), dev(w), scale, 0.0))
+        for r, sign in ((0, 1.0), (1, -1.0)):
+            want = F.f64_to_e4m3_code(sign * w_pad.astype(np.float64) / scale)
+            bad = ~F.codes_equal_e4m3(q[r], want)
+            assert not bad.any(), f"scale {scale} sign {sign}: {bad.sum()} codes differ, " \
+                                  f"first w={float(w_pad[bad][0])!r}"
+
+
 def test_rmsnorm_quant(dn):
     x = W.normal((130, 4096), 22, 0)
     w = W.normal((4096,), 22, 1, mean=1.0, std=0.1)
