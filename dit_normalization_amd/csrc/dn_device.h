@@ -54,21 +54,29 @@ __device__ __forceinline__ v4u pack8(const float f[8]) {
 // value, so NaN bypasses it and converts to the e4m3fn NaN.
 constexpr float kE4M3Max = 448.0f;
 
+// kNanSafe = false drops the NaN bypass, for callers that have established that no
+// value can be NaN (finite inputs, statistics and parameters).
+template <bool kNanSafe = true>
 __device__ __forceinline__ float clamp_e4m3(float v) {
   const float c = __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
-  return v == v ? c : v;
+  if constexpr (kNanSafe) return v == v ? c : v;
+  return c;
 }
 
+template <bool kNanSafe = true>
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), r, true);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3<kNanSafe>(a), clamp_e4m3<kNanSafe>(b), 0,
+                                          false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3<kNanSafe>(c), clamp_e4m3<kNanSafe>(d), r,
+                                      true);
   return (uint32_t)r;
 }
 
+template <bool kNanSafe = true>
 __device__ __forceinline__ v2u pack_fp8x8(const float f[8]) {
   v2u v;
-  v.x = pack_fp8x4(f[0], f[1], f[2], f[3]);
-  v.y = pack_fp8x4(f[4], f[5], f[6], f[7]);
+  v.x = pack_fp8x4<kNanSafe>(f[0], f[1], f[2], f[3]);
+  v.y = pack_fp8x4<kNanSafe>(f[4], f[5], f[6], f[7]);
   return v;
 }
 
