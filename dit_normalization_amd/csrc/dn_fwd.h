@@ -57,6 +57,7 @@ constexpr int fwd_weight_planes(int epi) {
 constexpr int fwd_stats(int epi) { return epi_is_ln(epi) ? 2 : 1; }
 
 constexpr float kLog2E = 1.44269504088896341f;   // log2(e), rounded to FP32
+constexpr float kLn2 = 0.693147180559945309f;    // ln(2) = 1/log2(e), rounded to FP32
 
 struct FwdParams {
   const uint16_t* x;     int64_t sx;
@@ -207,6 +208,9 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   float4* wl = reinterpret_cast<float4*>(dn_lds);
   float inv_scale = 1.0f;
   if constexpr (kStaticFp8) inv_scale = 1.0f / *p.scale;
+  // SiLU's denominator factor: log2(e), times the static scale for FP8 outputs.
+  float silu_c = kLog2E;
+  if constexpr (EPI == EPI_SILU_FP8) silu_c = kLog2E * *p.scale;
   // Static FP8 without a modulation: the reciprocal scale is folded into the staged
   // per-column parameters (w_eff / scale; gamma / scale and beta / scale), one multiply
   // per element fewer in the epilogue.
@@ -251,6 +255,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           if constexpr (kFold) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) e[k] *= inv_scale;
+          }
+          if constexpr (kSilu) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] *= kLog2E;   // see the SiLU epilogue
           }
           if constexpr (kFp8Out) {
 #pragma unroll
@@ -549,34 +557,39 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
               for (int k = 0; k < 8; ++k) we[k] *= inv_scale;
             }
+            if constexpr (kSilu) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) we[k] *= kLog2E;
+            }
           }
 #pragma unroll
           for (int k = 0; k < 8; ++k) yv[k] = (fh[k] * rs[rr]) * we[k];
         }
         if constexpr (kSilu) {
-          // SiLU(y) = y / (1 + e^-y), evaluated as (y or y e^y) * 1/(1 + e^-|y|) so that the
-          // exponential never overflows.  e^-|y| = 2^(-|y| log2 e) on the hardware exp2
-          // (v_exp_f32, < 0.75 ulp on normal results, measured) and the reciprocal on
-          // v_rcp_f32 (< 0.9 ulp): together within (|y| + 5) FP32 ulps of SiLU(y).  v_exp_f32
-          // flushes results below 2^-126 to zero, so rows with |y| > 80 take the accurate
-          // library exponential instead.
+          // SiLU(y) = y / (1 + e^-y).  The staged weights carry log2(e), so yv holds
+          // z = y log2(e): e = 2^-|z| = e^-|y| on the hardware exp2 (v_exp_f32, its -|z|
+          // argument an input modifier; < 0.75 ulp on normal results, measured), and
+          //   SiLU(y) = max(z, z e) / (log2(e) (1 + e))
+          // (z e > z exactly when z < 0, so the max picks y e^y / (1 + e^-|y|) for y < 0 and
+          // y / (1 + e^-y) otherwise), the denominator one FMA and the hardware reciprocal
+          // (v_rcp_f32, < 0.9 ulp).  For FP8 outputs the static scale joins the denominator.
+          // Together within (|y| + 5) FP32 ulps of SiLU(y).  v_exp_f32 flushes results below
+          // 2^-126 to zero, so rows with |y| > 80 take the accurate library exponential.
           float e[8];
           float amax = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const float ay = fabsf(yv[k]);
-            amax = fmaxf(amax, ay);
-            e[k] = __builtin_amdgcn_exp2f(-ay * kLog2E);
+            const float az = fabsf(yv[k]);
+            amax = fmaxf(amax, az);
+            e[k] = __builtin_amdgcn_exp2f(-az);
           }
-          if (amax > 80.0f) {
+          if (amax > 80.0f * kLog2E) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) e[k] = expf(-fabsf(yv[k]));
+            for (int k = 0; k < 8; ++k) e[k] = expf(-fabsf(yv[k]) * kLn2);
           }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float num = yv[k] >= 0.0f ? yv[k] : yv[k] * e[k];
-            yv[k] = num * __builtin_amdgcn_rcpf(1.0f + e[k]);
-          }
+          for (int k = 0; k < 8; ++k)
+            yv[k] = fmaxf(yv[k], yv[k] * e[k]) * __builtin_amdgcn_rcpf(fmaf(e[k], silu_c, silu_c));
         }
 
         if constexpr (kSigGate) {
@@ -606,7 +619,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
                       EPI == EPI_SILU_BF16 || EPI == EPI_SIGMOID_GATE) {
           bstore16(ry[rr], oy[rr] + d16, pack8(yv));
         } else if constexpr (EPI == EPI_FP8 || EPI == EPI_LN_FP8 || EPI == EPI_SILU_FP8) {
-          if constexpr (!kFold) {
+          if constexpr (!kFold && !kSilu) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
           }
