@@ -223,15 +223,20 @@ __device__ __forceinline__ float sumsq8(const float f[8]) {
 // make every lane pay for both sums (measured: -10 % on the VALU-heavy SiLU rows).
 __device__ __forceinline__ double sumsq8_d(const float f[8], bool exact) {
   const float t = sumsq8(f);
-  const bool redo = exact || !(t <= 3.0e38f);
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(redo) == 0, 1)) return (double)t;
+  // `exact` lowers the threshold below every sum (then every lane takes the FP64 sum), so
+  // the comparison feeds the vote alone and the vote is its lane mask as it stands; the
+  // rare FP64 path reads this lane's bit of the vote.  (Voting on `exact || big`, or using
+  // the comparison past the branch, costs two VALU instructions per call.)
+  const float limit = exact ? -1.0f : 3.0e38f;
+  const uint64_t redo = __builtin_amdgcn_ballot_w64(!(t <= limit));
+  if (__builtin_expect(redo == 0, 1)) return (double)t;
   // An empty volatile statement keeps the compiler from hoisting this block above the
   // branch (it would otherwise evaluate both sums and select).
   asm volatile("");
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) s = fma((double)f[k], (double)f[k], s);
-  return redo ? s : (double)t;
+  return (redo >> __lane_id()) & 1 ? s : (double)t;
 }
 
 // FP32(a / 448) for a >= 0 the value of a BF16 number (a block's largest |n|), correctly
@@ -316,20 +321,35 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
   return 1.0 / sqrt(x);
 }
 
-// Maximum over each aligned group of 16 lanes (one DPP row) with four VALU moves and no
-// LDS traffic: swap neighbours, swap pairs (quad permutations), then mirror each half row
-// and the whole row; after each step every lane holds the maximum of twice as many lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-  const int iv = __float_as_int(v);
-  return __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, CTRL, 0xf, 0xf, false));
-}
+// Maximum over each aligned group of 16 lanes (one DPP row) of values that are >= +0 and
+// not NaN, with four DPP steps and no LDS traffic: swap neighbours, swap pairs (quad
+// permutations), then mirror each half row and the whole row; after each step every lane
+// holds the maximum of twice as many lanes.  For such values IEEE order is the order of
+// their bit patterns as unsigned integers, so each step is an integer maximum, which the
+// compiler merges with its DPP move (a float maximum would first quiet the moved operand,
+// one more instruction per step).
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm [1, 0, 3, 2]
-  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm [2, 3, 0, 1]
-  v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
-  return v;
+  uint32_t u = __float_as_uint(v);
+  uint32_t t = dpp_u32<0xB1>(u);    // quad_perm [1, 0, 3, 2]
+  u = u > t ? u : t;
+  t = dpp_u32<0x4E>(u);             // quad_perm [2, 3, 0, 1]
+  u = u > t ? u : t;
+  t = dpp_u32<0x141>(u);            // row_half_mirror
+  u = u > t ? u : t;
+  t = dpp_u32<0x140>(u);            // row_mirror
+  u = u > t ? u : t;
+  return __uint_as_float(u);
+}
+
+// Maximum of two results of arithmetic (never signalling NaNs) as one v_max_f32: IEEE
+// maxNum, so a NaN operand yields the other one, the same as fmaxf, without the quieting
+// pass the compiler puts in front of fmaxf operands it cannot prove canonical (one extra
+// instruction per value).  The hazard check does not see registers written by inline
+// assembly, so the result must not be a DPP operand.
+__device__ __forceinline__ float max_of_results(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 }  // namespace dn

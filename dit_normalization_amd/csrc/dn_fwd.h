@@ -589,7 +589,8 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           }
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            yv[k] = fmaxf(yv[k], yv[k] * e[k]) * __builtin_amdgcn_rcpf(fmaf(e[k], silu_c, silu_c));
+            yv[k] = max_of_results(yv[k], yv[k] * e[k]) *
+                    __builtin_amdgcn_rcpf(fmaf(e[k], silu_c, silu_c));
         }
 
         if constexpr (kSigGate) {
