@@ -80,6 +80,17 @@ __device__ __forceinline__ v2u pack_fp8x8(const float f[8]) {
   return v;
 }
 
+// The same codes for values the caller has shown to lie within [-448, 448] (NaN passes
+// through as the NaN code either way): the clamp is the identity there and is left out.
+__device__ __forceinline__ v2u pack_fp8x8_in_range(const float f[8]) {
+  v2u v;
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  v.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  v.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], r, true);
+  return v;
+}
+
 // ------------------------------------------------------------------ memory access
 // Rows are read and written through raw buffer descriptors (SGPRs): the descriptor's base
 // is the first row a wave touches and its record count bounds the bytes that belong to

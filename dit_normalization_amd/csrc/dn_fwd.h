@@ -211,6 +211,13 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   // SiLU's denominator factor: log2(e), times the static scale for FP8 outputs.
   float silu_c = kLog2E;
   if constexpr (EPI == EPI_SILU_FP8) silu_c = kLog2E * *p.scale;
+  // SiLU + FP8: where every |z| of a vector in the wave is at most this limit, no output
+  // needs the e4m3 clamp.  For z >= 0 the output is at most z / silu_c <= 440 (< 448, a few
+  // ulps of rounding aside); for z < 0 its magnitude is at most (1/e) / scale, below 440
+  // once silu_c >= 2e-3.  Any other scale (tiny, negative, NaN, infinite) disables it.
+  float silu_lim = -1.0f;
+  if constexpr (EPI == EPI_SILU_FP8)
+    if (silu_c >= 2e-3f && silu_c <= 1e30f) silu_lim = 440.0f * silu_c;
   // Static FP8 without a modulation: the reciprocal scale is folded into the staged
   // per-column parameters (w_eff / scale; gamma / scale and beta / scale), one multiply
   // per element fewer in the epilogue.
@@ -509,6 +516,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         const uint32_t d16 = (uint32_t)(v * TPR * 16);
         const uint32_t d8 = (uint32_t)(v * TPR * 8);
         float fh[8], we[8], yv[8];
+        float silu_amax = 0.0f;   // largest |z| of the vector (SiLU)
         unpack8(st.a[rr][v], fh);
         if constexpr (kLN) {
           // n = (h - mean) * rstd in FP32, then one FMA with gamma and beta (or with the
@@ -576,14 +584,13 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
           // Together within (|y| + 5) FP32 ulps of SiLU(y).  v_exp_f32 flushes results below
           // 2^-126 to zero, so rows with |y| > 80 take the accurate library exponential.
           float e[8];
-          float amax = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float az = fabsf(yv[k]);
-            amax = fmaxf(amax, az);
+            silu_amax = fmaxf(silu_amax, az);
             e[k] = __builtin_amdgcn_exp2f(-az);
           }
-          if (amax > 80.0f * kLog2E) {
+          if (silu_amax > 80.0f * kLog2E) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) e[k] = expf(-fabsf(yv[k]) * kLn2);
           }
@@ -624,7 +631,15 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) yv[k] *= inv_scale;
           }
-          if (fp8_fast)
+          // SiLU vectors whose outputs all lie within the e4m3 range (a wave vote on the
+          // bound above) convert without the clamp; a NaN, which the running maximum skips,
+          // converts to the NaN code on either path.
+          bool in_range = false;
+          if constexpr (kSilu)
+            in_range = __builtin_amdgcn_ballot_w64(!(silu_amax <= silu_lim)) == 0;
+          if (in_range)
+            bstore8(rq[rr], oq[rr] + d8, pack_fp8x8_in_range(yv));
+          else if (fp8_fast)
             bstore8(rq[rr], oq[rr] + d8, pack_fp8x8<false>(yv));
           else
             bstore8(rq[rr], oq[rr] + d8, pack_fp8x8<true>(yv));

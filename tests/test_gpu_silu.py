@@ -47,6 +47,29 @@ def test_rmsnorm_silu_fp8(dn, hidden):
     assert_fp8(q, ref.q, ref.tie, f"silu e4m3 [{hidden}]")
 
 
+@pytest.mark.parametrize("case", ["spiked rows", "tiny scale", "unit scale"])
+def test_rmsnorm_silu_fp8_saturation(dn, case):
+    """e4m3 outputs beyond +-448 saturate.  At scale 0.02, rows 0..39 carry a spike that
+    normalises to ~21, past 448 after the scale, and the other rows stay inside (both
+    sides of the kernel's in-range vote); at scale 5e-4 SiLU's negative lobe (down to
+    -0.28 / scale) saturates on its own; at scale 1 every output is in range."""
+    x = W.normal((96, 512), 71, 0)
+    w = W.normal((512,), 71, 1, mean=1.0, std=0.1)
+    scale = {"spiked rows": 0.02, "tiny scale": 5e-4, "unit scale": 1.0}[case]
+    if case == "spiked rows":
+        x[:40, 7] = 50.0
+    q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), 1e-6, output_fp8=True, scale=scale)
+    r, ref = S.fused_rmsnorm_silu_fp8(values(x), values(w), scale, 1e-6)
+    sat = (ref.q.astype(np.int64) & 0x7F) == 0x7E
+    if case == "spiked rows":
+        assert sat[:40].any(axis=1).all() and not sat[40:].any()
+    elif case == "tiny scale":
+        assert (ref.q == 0xFE).any()
+    else:
+        assert not sat.any()
+    assert_fp8(q, ref.q, ref.tie, f"silu e4m3 saturation ({case})")
+
+
 def test_rmsnorm_silu_wide_range_and_fp32_weight(dn):
     """Weights of spread 40 push y to +-100 and beyond: the exponential of -|y| never
     overflows, tiny negative outputs round like the exact ones; FP32 weight with bias 1."""
