@@ -91,6 +91,17 @@ __device__ __forceinline__ v2u pack_fp8x8_in_range(const float f[8]) {
   return v;
 }
 
+// pack_fp8x8<true> codes of values the caller bounds by `lim` <= 448 where it can: when
+// no lane of the wave holds a magnitude above `lim` (a vote; the running maximum skips
+// NaN, which converts to the NaN code either way) the clamp is left out.
+__device__ __forceinline__ v2u pack_fp8x8_voted(const float f[8], float lim) {
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(f[k]));
+  if (__builtin_amdgcn_ballot_w64(!(am <= lim)) == 0) return pack_fp8x8_in_range(f);
+  return pack_fp8x8(f);
+}
+
 // ------------------------------------------------------------------ memory access
 // Rows are read and written through raw buffer descriptors (SGPRs): the descriptor's base
 // is the first row a wave touches and its record count bounds the bytes that belong to
@@ -232,22 +243,39 @@ __device__ __forceinline__ float sumsq8(const float f[8]) {
 // squares are summed in FP64 (exact products).  The test is a wave vote, so the FP64 sum
 // is a branch the wave skips unless one of its lanes needs it; a per-lane select would
 // make every lane pay for both sums (measured: -10 % on the VALU-heavy SiLU rows).
+//
+// kJointVote votes on `exact || overflow` instead, which makes the compiler carry the mask
+// through a VGPR (two more VALU instructions per call) and schedules the surrounding code
+// differently: measured 2-3 % faster in the NeoX QK RoPE kernel with BF16 outputs (two
+// waves per SIMD), 2 % slower with FP8 outputs and no different elsewhere, so only that
+// instance asks for it.  Both forms give the same sums.
+template <bool kJointVote = false>
 __device__ __forceinline__ double sumsq8_d(const float f[8], bool exact) {
   const float t = sumsq8(f);
-  // `exact` lowers the threshold below every sum (then every lane takes the FP64 sum), so
-  // the comparison feeds the vote alone and the vote is its lane mask as it stands; the
-  // rare FP64 path reads this lane's bit of the vote.  (Voting on `exact || big`, or using
-  // the comparison past the branch, costs two VALU instructions per call.)
+  if constexpr (kJointVote) {
+    const bool redo = exact || !(t <= 3.0e38f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(redo) == 0, 1)) return (double)t;
+    asm volatile("");   // keeps the FP64 sum behind the branch
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = fma((double)f[k], (double)f[k], s);
+    return redo ? s : (double)t;
+  }
+  // `exact` lowers the limit below every sum (then every lane takes the FP64 sum), so the
+  // comparison feeds the vote alone and the vote is its lane mask as it stands.  (Voting
+  // on `exact || big`, or using the comparison past the branch, makes the compiler carry
+  // the mask through a VGPR: two more VALU instructions per call.)
   const float limit = exact ? -1.0f : 3.0e38f;
-  const uint64_t redo = __builtin_amdgcn_ballot_w64(!(t <= limit));
-  if (__builtin_expect(redo == 0, 1)) return (double)t;
-  // An empty volatile statement keeps the compiler from hoisting this block above the
-  // branch (it would otherwise evaluate both sums and select).
-  asm volatile("");
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(t <= limit)) == 0, 1)) return (double)t;
+  // The empty volatile statement keeps the compiler from hoisting this block above the
+  // branch (it would otherwise evaluate both sums and select), and hides `t` from it, so
+  // the lane's comparison below is made afresh instead of carried past the branch.
+  float tt = t;
+  asm volatile("" : "+v"(tt));
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) s = fma((double)f[k], (double)f[k], s);
-  return (redo >> __lane_id()) & 1 ? s : (double)t;
+  return !(tt <= limit) ? s : (double)tt;
 }
 
 // FP32(a / 448) for a >= 0 the value of a BF16 number (a block's largest |n|), correctly

@@ -146,6 +146,16 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
   }
   // cos and sin carry the attention factor (and, for FP8 outputs, 1/scale).
   const float cs_mul = (float)((double)p.af * (double)inv_qk);
+  // FP8 outputs skip the e4m3 clamp (and its NaN bypass) for a unit whose values a wave
+  // vote shows in range.  A rotation keeps each pair's length, so a rotated value is at
+  // most sqrt(2) max(|a|, |b|) |cs_mul| up to rounding: a Q or K unit whose inputs stay
+  // within qk_lim gives values below 440.  V values only need |v / scale| <= 448, the
+  // largest code (the conversion rounds to nearest and does not saturate).
+  float qk_lim = -1.0f;
+  if constexpr (FP8) {
+    const float m = fabsf(cs_mul);
+    if (m > 0.0f && m <= 1e30f) qk_lim = 440.0f / (1.4143f * m);
+  }
 
   // This lane's units: byte offset of the first vector in the qkv row, class (0 Q, 1 K,
   // 2 V, 3 none), and the unit's index inside its head.
@@ -210,10 +220,11 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
     for (int m = 0; m < UMAX; ++m) {
       float f[8];
       unpack8(va[m], f);
-      double s = sumsq8_d(f, tiny_eps);
+      constexpr bool kJointVote = NEOX && !FP8;   // a measured scheduling preference
+      double s = sumsq8_d<kJointVote>(f, tiny_eps);
       if constexpr (NEOX) {
         unpack8(vb[m], f);
-        s += sumsq8_d(f, tiny_eps);
+        s += sumsq8_d<kJointVote>(f, tiny_eps);
       }
       sq += ucls[m] == 0 ? s : 0.0;
       sk += ucls[m] == 1 ? s : 0.0;
@@ -267,12 +278,12 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
           unpack8(va[m], f);
 #pragma unroll
           for (int k = 0; k < 8; ++k) f[k] *= inv_v;
-          bstore8(rvo[0], ovo[0] + vo, pack_fp8x8(f));
+          bstore8(rvo[0], ovo[0] + vo, pack_fp8x8_voted(f, 448.0f));
           if constexpr (NEOX) {
             unpack8(vb[m], f);
 #pragma unroll
             for (int k = 0; k < 8; ++k) f[k] *= inv_v;
-            bstore8(rvo[0], ovo[0] + vo + (uint32_t)uph * OB, pack_fp8x8(f));
+            bstore8(rvo[0], ovo[0] + vo + (uint32_t)uph * OB, pack_fp8x8_voted(f, 448.0f));
           }
         } else {
           bstore16(rvo[0], ovo[0] + vo, va[m]);
@@ -335,20 +346,42 @@ __global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
           oa[4 * q + 3] = fmaf(a1, c.w, b1 * c.z);
         }
       }
+      bool in_range = false;
+      if constexpr (FP8) {
+        float am = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          am = fmaxf(am, fabsf(fa[k]));
+          if constexpr (NEOX) am = fmaxf(am, fabsf(fb[k]));
+        }
+        in_range = __builtin_amdgcn_ballot_w64(!(am <= qk_lim)) == 0;
+      }
       const int vbase = cls == 0 ? uvec[m] : uvec[m] - p.nq * vph;
       const uint32_t o = (uint32_t)vbase * OB;
       if (cls == 0) {
         if constexpr (FP8) {
-          bstore8(rqo[0], oqo[0] + o, pack_fp8x8(oa));
-          if constexpr (NEOX) bstore8(rqo[0], oqo[0] + o + (uint32_t)uph * OB, pack_fp8x8(ob));
+          if (in_range) {
+            bstore8(rqo[0], oqo[0] + o, pack_fp8x8_in_range(oa));
+            if constexpr (NEOX)
+              bstore8(rqo[0], oqo[0] + o + (uint32_t)uph * OB, pack_fp8x8_in_range(ob));
+          } else {
+            bstore8(rqo[0], oqo[0] + o, pack_fp8x8(oa));
+            if constexpr (NEOX) bstore8(rqo[0], oqo[0] + o + (uint32_t)uph * OB, pack_fp8x8(ob));
+          }
         } else {
           bstore16(rqo[0], oqo[0] + o, pack8(oa));
           if constexpr (NEOX) bstore16(rqo[0], oqo[0] + o + (uint32_t)uph * OB, pack8(ob));
         }
       } else {
         if constexpr (FP8) {
-          bstore8(rko[0], oko[0] + o, pack_fp8x8(oa));
-          if constexpr (NEOX) bstore8(rko[0], oko[0] + o + (uint32_t)uph * OB, pack_fp8x8(ob));
+          if (in_range) {
+            bstore8(rko[0], oko[0] + o, pack_fp8x8_in_range(oa));
+            if constexpr (NEOX)
+              bstore8(rko[0], oko[0] + o + (uint32_t)uph * OB, pack_fp8x8_in_range(ob));
+          } else {
+            bstore8(rko[0], oko[0] + o, pack_fp8x8(oa));
+            if constexpr (NEOX) bstore8(rko[0], oko[0] + o + (uint32_t)uph * OB, pack_fp8x8(ob));
+          }
         } else {
           bstore16(rko[0], oko[0] + o, pack8(oa));
           if constexpr (NEOX) bstore16(rko[0], oko[0] + o + (uint32_t)uph * OB, pack8(ob));

@@ -107,6 +107,29 @@ def test_qk_rope_fp8(dn, interleave):
     assert_fp8(vo, v8.q, v8.tie, "V e4m3")
 
 
+@pytest.mark.parametrize("interleave", [True, False])
+def test_qk_rope_fp8_saturation(dn, interleave):
+    """e4m3 outputs beyond +-448 saturate.  Tokens 0..9 carry a spike in head 0 of Q and
+    of K (normalised to ~11, past 448 after the rotation at scale 0.02) and in V (50 at
+    V scale 0.02); the other tokens stay in range, so both sides of the kernel's in-range
+    vote run."""
+    wl = W.qk_rope(3, 4, 5, 2, 24, 24, 24, 128, (44, 42, 42))
+    wl.params["output_scale"] = 0.02
+    qkv = wl.tensors["qkv"]
+    qkv[:10, 5] = 60.0
+    qkv[:10, 24 * 128 + 3] = 60.0
+    qkv[:10, 48 * 128 + 7] = 50.0
+    qo, ko, vo = run(dn, wl, interleave, fp8=True)
+    r = oracle(wl, interleave)
+    q8, k8, v8 = Q.qk_rmsnorm_rope_fp8(r, wl.params["output_scale"], wl.params["v_scale"])
+    for ref in (q8, k8, v8):
+        sat = ((ref.q.astype(np.int64) & 0x7F) == 0x7E).any(axis=1)
+        assert sat[:10].all() and not sat[10:].any()
+    assert_fp8(qo, q8.q, q8.tie, "Q e4m3 saturation")
+    assert_fp8(ko, k8.q, k8.tie, "K e4m3 saturation")
+    assert_fp8(vo, v8.q, v8.tie, "V e4m3 saturation")
+
+
 def test_qk_rope_fp32_weights_and_3d_input(dn):
     wl = W.qk_rope(2, 3, 4, 2, 4, 4, 4, 128, (44, 42, 42))
     t, p = wl.tensors, wl.params
