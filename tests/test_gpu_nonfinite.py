@@ -13,6 +13,7 @@ import workloads as W
 from oracle import formats as F
 from oracle import layernorm as L
 from oracle import rmsnorm as O
+from oracle import silu as S
 from tests.conftest import bits8, values
 from tests.parity import assert_bf16
 
@@ -40,7 +41,7 @@ def with_specials(rows, hidden, seed):
     return x.to(torch.bfloat16)
 
 
-def assert_bf16_nonfinite(gpu, ref_exact, what):
+def assert_bf16_nonfinite(gpu, ref_exact, what, mag=None):
     g = values(gpu).reshape(ref_exact.shape)
     r = ref_exact
     assert (np.isnan(g) == np.isnan(r)).all(), f"{what}: NaN positions differ"
@@ -48,7 +49,17 @@ def assert_bf16_nonfinite(gpu, ref_exact, what):
     assert (g[inf] == r[inf]).all() and (np.isinf(g) == inf).all(), f"{what}: infinities differ"
     fin = np.isfinite(r)
     assert_bf16(gpu.reshape(-1)[torch.as_tensor(np.flatnonzero(fin), device=gpu.device)],
-                r[fin], what)
+                r[fin], what, mag=None if mag is None else mag[fin])
+
+
+def assert_fp8_nonfinite(q, ref, what):
+    """NaN codes exactly where the oracle's value is NaN; every other code equal (or a
+    neighbour at a flagged tie), infinities saturating to +-448."""
+    g = bits8(q).reshape(ref.q.shape)
+    nan_ref = np.isnan(ref.v)
+    assert (((g & 0x7F) == 0x7F) == nan_ref).all(), f"{what}: e4m3 NaN codes"
+    ok = F.codes_equal_e4m3(g, ref.q) | ref.tie
+    assert ok[~nan_ref].all(), f"{what}: e4m3 codes"
 
 
 @pytest.mark.parametrize("hidden", [128, 4096])
@@ -107,3 +118,49 @@ def test_layernorm_with_infinities_and_nans(dn):
     with np.errstate(invalid="ignore", over="ignore"):
         ref = L.layernorm(values(x), g.double().numpy(), b.double().numpy(), 1e-6)
     assert_bf16_nonfinite(y, ref.y_exact, "layernorm y")
+
+
+def test_silu_with_infinities_and_nans(dn):
+    """SiLU of the IEEE norm: NaN stays NaN (the epilogue's maximum and its in-range vote
+    skip it), rows holding an infinity are SiLU(0) = 0 apart from their NaN elements."""
+    x = with_specials(9, 512, 405)
+    w = W.normal((512,), 405, 1, mean=1.0, std=0.1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = S.fused_rmsnorm_silu(values(x), values(w), 1e-6)
+        _, ref8 = S.fused_rmsnorm_silu_fp8(values(x), values(w), 0.02, 1e-6)
+    y = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), 1e-6)
+    assert_bf16_nonfinite(y, ref.s_exact, "silu y", mag=ref.mag)
+    q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), 1e-6, output_fp8=True, scale=0.02)
+    assert_fp8_nonfinite(q, ref8, "silu e4m3")
+
+
+@pytest.mark.parametrize("interleave", [True, False])
+def test_qk_rope_fp8_with_infinities_and_nans(dn, interleave):
+    """A Q head holding +inf (rstd 0: NaN where 0 * inf is taken, the rest of the head 0),
+    a K head holding a NaN, V holding +-inf (saturating to +-448) and a NaN (the NaN code)."""
+    from oracle import qk_rope as Q
+    wl = W.qk_rope(2, 2, 3, 1, 4, 4, 4, 128, (44, 42, 42))
+    t, p = wl.tensors, wl.params
+    qkv = t["qkv"].float()
+    qkv[1, 5] = float("inf")
+    qkv[2, 4 * 128 + 9] = float("nan")
+    qkv[3, 8 * 128 + 1] = float("inf")
+    qkv[3, 8 * 128 + 2] = float("-inf")
+    qkv[4, 9 * 128 + 3] = float("nan")
+    qkv = qkv.to(torch.bfloat16)
+    qo, ko, vo = dn.dn_fused_qk_rmsnorm_rope(
+        dev(qkv), dev(t["q_weight"]), dev(t["k_weight"]), p["nq"], p["nk"], p["nv"],
+        p["head_dim"], p["ppf"], p["pph"], p["ppw"], p["channels"], p["eps"], base=p["base"],
+        interleave=interleave, output_fp8=True, output_quant_scale=p["output_scale"],
+        v_quant_scale=p["v_scale"])
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = Q.qk_rmsnorm_rope(values(qkv), values(t["q_weight"]), values(t["k_weight"]),
+                              p["nq"], p["nk"], p["nv"], p["head_dim"], p["channels"], p["ppf"],
+                              p["pph"], p["ppw"], p["eps"], p["base"], interleave, 1.0, 0.0, 0.0,
+                              1.0, True)
+        q8, k8, v8 = Q.qk_rmsnorm_rope_fp8(r, p["output_scale"], p["v_scale"])
+    assert np.isnan(q8.v).any() and np.isnan(k8.v).any() and np.isnan(v8.v).any()
+    assert (v8.q == 0x7E).any() and (v8.q == 0xFE).any()
+    assert_fp8_nonfinite(qo, q8, "Q e4m3")
+    assert_fp8_nonfinite(ko, k8, "K e4m3")
+    assert_fp8_nonfinite(vo, v8, "V e4m3")
