@@ -78,8 +78,22 @@ __device__ __forceinline__ void rope_weight8(const RopeParams& p, int vec, float
 // 1/(2*pi), turning an angular frequency into revolutions per position.
 constexpr double kInv2Pi = 0.15915494309189535;
 
+// Waves per SIMD the register allocation must leave room for.  The kernel is latency-bound
+// (vector ALUs and HBM both about half busy) and its occupancy is set by its VGPRs (2-3
+// waves per SIMD unconstrained), so a tighter budget trades a few spills for more waves
+// where that measured faster at the 3072-wide DiT layout: interleaved pairs with FP8
+// outputs at 4 waves +7 %, NeoX pairs with BF16 outputs at 3 waves +3 %; the other two
+// forms lost 7-16 % at 4 waves and gained nothing at 3.  Rows of 512 lanes or more keep
+// the unconstrained budget (a 4-wave budget would spill up to 116 bytes per lane there).
+template <int TPR, bool NEOX, bool FP8>
+constexpr int rope_min_waves() {
+  if (TPR > 256) return 1;
+  return !NEOX && FP8 ? 4 : (NEOX && !FP8 ? 3 : 1);
+}
+
 template <int TPR, int VMAX, int NT, bool NEOX, bool FP8>
-__global__ void __launch_bounds__(NT) qkrope_kernel(const RopeParams p) {
+__global__ void __launch_bounds__(NT, (rope_min_waves<TPR, NEOX, FP8>()))
+qkrope_kernel(const RopeParams p) {
   extern __shared__ __align__(16) unsigned char dn_lds[];
   using Geom = RowGeom<TPR, 1, NT>;
   constexpr int G = Geom::G;
