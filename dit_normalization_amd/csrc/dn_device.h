@@ -364,9 +364,9 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
 // not NaN, with four DPP steps and no LDS traffic: swap neighbours, swap pairs (quad
 // permutations), then mirror each half row and the whole row; after each step every lane
 // holds the maximum of twice as many lanes.  For such values IEEE order is the order of
-// their bit patterns as unsigned integers, so each step is an integer maximum, which the
-// compiler merges with its DPP move (a float maximum would first quiet the moved operand,
-// one more instruction per step).
+// their bit patterns as unsigned integers, so each step is a DPP move and an integer
+// maximum (a float maximum would first quiet the moved operand: one more instruction per
+// step).
 __device__ __forceinline__ float row16_max(float v) {
   uint32_t u = __float_as_uint(v);
   uint32_t t = dpp_u32<0xB1>(u);    // quad_perm [1, 0, 3, 2]
@@ -383,8 +383,8 @@ __device__ __forceinline__ float row16_max(float v) {
 // Maximum of two results of arithmetic (never signalling NaNs) as one v_max_f32: IEEE
 // maxNum, so a NaN operand yields the other one, the same as fmaxf, without the quieting
 // pass the compiler puts in front of fmaxf operands it cannot prove canonical (one extra
-// instruction per value).  The hazard check does not see registers written by inline
-// assembly, so the result must not be a DPP operand.
+// instruction per value).  The compiler's hazard checks cannot be relied on to see a
+// register written by inline assembly, so the result is never fed to a DPP move.
 __device__ __forceinline__ float max_of_results(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
