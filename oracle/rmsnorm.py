@@ -187,17 +187,24 @@ def fused_add_rmsnorm_fp8_block_quant(x, residual, w, bias: float = 0.0,
     steps, normed is BF16 and is what gets quantised; one dynamic FP32 scale per 1x128
     block; hidden a multiple of 128).  A block whose amax is 0 gets scale 0 and zero codes
     (the pages are silent; a zero block has nothing to scale).
+
+    Non-finite inputs (the pages define none; the plain IEEE reading): amax is the largest
+    magnitude that is a number, IEEE maxNum, so a NaN element neither sets nor hides its
+    block's scale (0 when the block holds no number), and a NaN element is coded NaN in
+    every block, a zero-scale block included.
     """
     fa = fused_add_rmsnorm(x, residual, w, bias, eps)
     n = fa.norm.y
     rows, hidden = n.shape
     nb = hidden // BLOCK
     blocks = n.reshape(rows, nb, BLOCK)
-    amax = np.max(np.abs(blocks), axis=2)
+    nan = np.isnan(blocks)
+    mags = np.where(nan, 0.0, np.abs(blocks))            # magnitudes are >= 0: NaN drops out
+    amax = np.max(mags, axis=2)
     s = block_scale_of(amax)
     safe = np.where(s > 0, s, 1.0)
     v = blocks / safe[:, :, None]
-    q = np.where((s > 0)[:, :, None], f64_to_e4m3_code(v), np.uint8(0)).astype(np.uint8)
+    q = np.where((s > 0)[:, :, None] | nan, f64_to_e4m3_code(v), np.uint8(0)).astype(np.uint8)
 
     # Which results are not unique for an FP32 evaluation of the same definition:
     # a normalised value at a BF16 rounding tie may take the other neighbour.
@@ -205,15 +212,14 @@ def fused_add_rmsnorm_fp8_block_quant(x, residual, w, bias: float = 0.0,
     bf_tie = bf16_near_tie(y_ex)
     other = np.where(bf_tie, 2.0 * y_ex - blocks, blocks)  # the other neighbour (mirror)
     other = bf16_round(other)
-    abs_hi = np.maximum(np.abs(blocks), np.abs(other))
+    abs_hi = np.maximum(mags, np.where(nan, 0.0, np.abs(other)))
     # The block's amax may change if a tied element could reach or exceed it.
     touches = bf_tie & (abs_hi >= amax[:, :, None])
     block_flag = np.any(touches, axis=2)
-    amax_alt = np.where(block_flag,
-                        np.max(np.where(bf_tie, abs_hi, np.abs(blocks)), axis=2), amax)
+    amax_alt = np.where(block_flag, np.max(np.where(bf_tie, abs_hi, mags), axis=2), amax)
     # Lower alternative: the tied amax element rounding down.
-    amax_lo = np.max(np.where(bf_tie, np.minimum(np.abs(blocks), np.abs(other)),
-                              np.abs(blocks)), axis=2)
+    amax_lo = np.max(np.where(bf_tie, np.minimum(mags, np.where(nan, 0.0, np.abs(other))),
+                              mags), axis=2)
     scale_alt = np.where(amax_alt != amax, block_scale_of(amax_alt), block_scale_of(amax_lo))
     fp8_tie = e4m3_near_tie(v) & (s > 0)[:, :, None]
     elem_tie = (fp8_tie | bf_tie).reshape(rows, hidden)

@@ -164,3 +164,33 @@ def test_qk_rope_fp8_with_infinities_and_nans(dn, interleave):
     assert_fp8_nonfinite(qo, q8, "Q e4m3")
     assert_fp8_nonfinite(ko, k8, "K e4m3")
     assert_fp8_nonfinite(vo, v8, "V e4m3")
+
+
+def test_block_quant_with_infinities_and_nans(dn):
+    """1x128 FP8 blocks under the IEEE maxNum reading: a NaN element neither sets nor hides
+    its block's scale and is coded NaN.  Rows 1-4 carry infinities and a NaN; a NaN weight
+    column puts one NaN among numbers in every row's first block."""
+    x = with_specials(9, 256, 406)
+    r = W.normal((9, 256), 406, 1)
+    w = W.normal((256,), 406, 2, mean=1.0, std=0.1).float()
+    w[9] = float("nan")
+    w = w.to(torch.bfloat16)
+    rd = dev(r)
+    normed = torch.empty((9, 256), dtype=torch.bfloat16, device="cuda")
+    q, bs = dn.dn_fused_add_rmsnorm_fp8_block_quant(dev(x), rd, dev(w), 1e-6, normed_out=normed)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.fused_add_rmsnorm_fp8_block_quant(values(x), values(r), values(w), 0.0, 1e-6)
+    h = values(rd)
+    assert (np.isnan(h) == np.isnan(ref.h_new)).all()
+    assert (h[~np.isnan(h)] == ref.h_new[~np.isnan(ref.h_new)]).all(), "h_new"
+    s = bs.t()[:9].cpu().double().numpy()
+    ok = (s == ref.scale) | (ref.block_flag & (s == ref.scale_alt))
+    assert ok.all(), f"block scales: {s[~ok]} vs {ref.scale[~ok]}"
+    g = bits8(q).reshape(ref.q.shape)
+    nan_ref = np.isnan(ref.normed)
+    assert nan_ref[:, 9].all() and (ref.scale > 0).any()
+    assert (((g & 0x7F) == 0x7F) == nan_ref).all(), "e4m3 NaN codes"
+    allow = np.repeat(ref.block_flag, 128, axis=1)
+    codes_ok = F.codes_equal_e4m3(g, ref.q) | ref.elem_tie | allow
+    assert codes_ok[~nan_ref].all(), "e4m3 codes"
+    assert_bf16_nonfinite(normed, ref.normed_exact, "normed_out")

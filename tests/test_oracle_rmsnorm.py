@@ -182,6 +182,42 @@ def test_block_quant_zero_block():
     assert (b.scale == 0).all() and (b.q == 0).all()
 
 
+def test_block_quant_nan_elements():
+    """IEEE maxNum reading: a NaN element neither sets nor hides its block's scale and is
+    coded NaN.  Row 0 holds +inf (rstd 0: that element is 0 * inf = NaN, the rest 0, so
+    its blocks have scale 0 and zero codes around the NaN); row 1 holds a NaN (NaN
+    throughout: scale 0, NaN codes); row 2 is finite and equals its own run alone."""
+    x = bf16_values((3, 256))
+    x[0, 5] = np.inf
+    x[1, 200] = np.nan
+    w = bf16_values((256,), mean=1.0, std=0.1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        b = O.fused_add_rmsnorm_fp8_block_quant(x, np.zeros((3, 256)), w, 0.0, 1e-6)
+    nan_code = (b.q & 0x7F) == 0x7F
+    assert (b.scale[:2] == 0).all()
+    assert nan_code[0, 5] and not nan_code[0, np.arange(256) != 5].any()
+    assert (b.q[0, np.arange(256) != 5] == 0).all()
+    assert nan_code[1].all()
+    alone = O.fused_add_rmsnorm_fp8_block_quant(x[2:], np.zeros((1, 256)), w, 0.0, 1e-6)
+    assert (b.scale[2] == alone.scale[0]).all() and (b.q[2] == alone.q[0]).all()
+    # A NaN weight column puts one NaN among numbers in every row's first block: the scale
+    # is the one the same rows get with that weight set to 0 (a zero element never sets a
+    # block's maximum unless every element is zero), every other code is unchanged, and
+    # the NaN element is coded NaN.
+    x = bf16_values((4, 256))
+    w0 = w.copy()
+    w0[9] = 0.0
+    wn = w.copy()
+    wn[9] = np.nan
+    ref = O.fused_add_rmsnorm_fp8_block_quant(x, np.zeros((4, 256)), w0, 0.0, 1e-6)
+    with np.errstate(invalid="ignore"):
+        got = O.fused_add_rmsnorm_fp8_block_quant(x, np.zeros((4, 256)), wn, 0.0, 1e-6)
+    assert (got.scale == ref.scale).all()
+    others = np.arange(256) != 9
+    assert (got.q[:, others] == ref.q[:, others]).all()
+    assert ((got.q[:, 9] & 0x7F) == 0x7F).all()
+
+
 # ----------------------------------------------------------------------------- AdaRMSNorm
 
 def test_ada_matches_torch_float64():
