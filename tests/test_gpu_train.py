@@ -78,7 +78,8 @@ def test_train_forward_plain_bf16_weight(dn):
 
 @pytest.mark.parametrize("rows,hidden", [(257, 8192), (1, 512), (2, 2048), (7, 6144), (63, 64),
                                          (129, 1024), (65, 128), (300, 8), (31, 16384),
-                                         (9, 32768), (1000, 256), (513, 4096)])
+                                         (9, 32768), (1000, 256), (513, 4096),
+                                         (37, 1032), (300, 3072), (45, 5128)])
 def test_train_backward_against_oracle(dn, rows, hidden):
     wl = W.train(rows=rows, hidden=hidden)
     t = wl.tensors
@@ -89,11 +90,14 @@ def test_train_backward_against_oracle(dn, rows, hidden):
     assert_dw(dw, ref.dw_exact, f"dw [{rows},{hidden}]")
 
 
-def test_train_backward_g_residual(dn):
-    wl = W.train(rows=100, hidden=2048)
+@pytest.mark.parametrize("rows,hidden", [(100, 2048), (77, 4096), (259, 8192)])
+def test_train_backward_g_residual(dn, rows, hidden):
+    """The residual gradient on each row-group layout (four 64-lane, four 128-lane and two
+    256-lane groups per block), with chunks whose rows do not divide among the groups."""
+    wl = W.train(rows=rows, hidden=hidden)
     t = wl.tensors
     h, rstd = backward_inputs(t)
-    gres = W.normal((100, 2048), 31, 0)
+    gres = W.normal((rows, hidden), 31, 0)
     dx, dw = dn.dn_train_backward(dev(t["g"]), dev(h), dev(t["w"]), dev(rstd), w_bias=1.0,
                                   g_residual=dev(gres))
     ref = O.train_backward(values(t["g"]), values(h), values(t["w"]), rstd.double().numpy(), 1.0,
