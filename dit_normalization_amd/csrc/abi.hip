@@ -169,19 +169,23 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int cap, int* 
 
 // Grid of a persistent row kernel that needs `needed` block-steps.  Normally at most `cap`
 // blocks per CU (fewer bytes in flight stream better); but when that leaves each block
-// fewer than three steps, the last, partly filled round of steps dominates the launch, so
-// every block-step is put in flight at once as far as occupancy allows (up to
-// kTailBlocksPerCu blocks per CU).  Measured with 2520 rows: gated Ada + FP8 at
-// [2520,3072] 4.96 -> 5.27 TB/s, fused add at [2520,4096] 4.63 -> 5.56 TB/s; launches with
-// three or more steps per block keep the cap (fused add at [8192,4096] and the DiT modes
-// at [4096,3072] measured 2-4 % slower with more blocks per CU).
+// fewer than kTailSteps steps, the ramp and the last, partly filled round of steps weigh on
+// the launch, so every block-step is put in flight at once as far as occupancy allows (up
+// to kTailBlocksPerCu blocks per CU).  Measured: gated Ada + FP8 at [2520,3072] 4.96 ->
+// 5.27 TB/s, fused add at [2520,4096] 4.63 -> 5.56 TB/s (fewer than three steps); with the
+// threshold raised from three to five steps, fused add (+ static FP8) at [4096,4096]
+// +12-13 %, block quant at [2048,7168] +8 %, gated Ada + FP8 at [4096,3072] +4 %, the
+// training forward of the [2048,8192] shard +3 %, the DiT modes at [4096,3072] -0.7 %.
+// At seven steps the DiT modes lost 3 % (at [6144,3072]), so launches of five or more
+// steps per block keep the cap.
 constexpr int kTailBlocksPerCu = 8;
+constexpr int kTailSteps = 5;
 
 dn_status persistent_grid(const void* kernel, int nt, size_t lds, int cap, int64_t needed,
                           int* grid) {
   int capacity = 0;
   DN_CHECK(resident_blocks(kernel, nt, lds, cap, &capacity));
-  if (needed < 3 * (int64_t)capacity) {
+  if (needed < kTailSteps * (int64_t)capacity) {
     int full = 0;
     DN_CHECK(resident_blocks(kernel, nt, lds, kTailBlocksPerCu, &full));
     if (full > capacity) capacity = full;
