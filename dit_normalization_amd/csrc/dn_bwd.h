@@ -299,25 +299,27 @@ __global__ void __launch_bounds__(NT) bwd_reduce_kernel(float* dw, const double*
 
 // (threads per row, vectors per thread, rows per group per step, threads per block).
 // The host takes the first tier, in this order, whose TPR*VB covers hidden/8; the tiers
-// after the tenth are alternatives for tuning builds.  Rows of 129-1024 vectors (H 1032
-// to 8192) take several row groups of 4 vectors per lane (four groups of 64 lanes in a
-// 256-thread block up to H = 2048; four of 128 lanes up to 4096 and two of 256 lanes up
-// to 8192 in a 512-thread block): the chunk's rows alternate between the groups, each
-// group keeps its own FP64 column sums, and they are added in group order at the end
-// (through 64 or 128 KiB of LDS).  Measured against one row group of 1-2 vectors per
+// after the tenth are alternatives for tuning builds.  Rows of 65-1024 vectors (H 520 to
+// 8192) take several row groups per block (four groups of 64 lanes in a 256-thread block,
+// 2 vectors per lane up to H = 1024 and 4 up to 2048; four of 128 lanes up to 4096 and two
+// of 256 lanes up to 8192, 4 vectors each, in a 512-thread block): the chunk's rows
+// alternate between the groups, each group keeps its own FP64 column sums, and they are
+// added in group order at the end (through 32-128 KiB of LDS).  Measured against one row
+// group of 1-2 vectors per
 // lane with several rows per step: at H = 8192 +3.4 % at 16384 rows (+3 % with a
 // residual gradient), +3.7 % at 4096, +7 % at 2048; at H = 4096 +7 %, +7 % and +2 %
 // (+4 % with a residual gradient); at H = 2048 +12 %, +6 % and +3 % (+8 %).  At H = 1024
-// the same shape (32 lanes, 4 vectors) measured +12 % at 16384 rows but -3 to -4 % at
-// 2048-4096, so narrower rows keep 4 rows per step.  Wider rows span the whole block.
+// four groups of 64 lanes with 2 vectors and 2 rows per step: +15 %, +4 % and +3 % (+13 %,
+// +5.5 %, -1 % with a residual gradient; 32 lanes with 4 vectors lost 3-4 % at 2048-4096
+// rows).  Wider rows span the whole block.
 #define DN_BWD_TIERS(X)                                                         \
   X(0, 8, 1, 4, 256)     X(1, 16, 1, 4, 256)    X(2, 32, 1, 4, 256)            \
-  X(3, 64, 1, 4, 256)    X(4, 128, 1, 4, 256)   X(5, 64, 4, 1, 256)            \
+  X(3, 64, 1, 4, 256)    X(4, 64, 2, 2, 256)    X(5, 64, 4, 1, 256)            \
   X(6, 128, 4, 1, 512)   X(7, 256, 4, 1, 512)   X(8, 512, 4, 1, 512)           \
   X(9, 1024, 4, 1, 1024) X(10, 1024, 1, 4, 1024) X(11, 512, 2, 4, 512)         \
   X(12, 1024, 1, 2, 1024) X(13, 512, 1, 2, 512) X(14, 512, 2, 2, 512)           \
-  X(15, 512, 1, 4, 512)  X(16, 256, 1, 4, 256)
+  X(15, 512, 1, 4, 512)  X(16, 256, 1, 4, 256)  X(17, 128, 1, 4, 256)
 
-constexpr int kBwdTierCount = 17;
+constexpr int kBwdTierCount = 18;
 
 }  // namespace dn
