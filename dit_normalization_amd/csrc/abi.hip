@@ -169,23 +169,27 @@ dn_status resident_blocks(const void* kernel, int nt, size_t lds, int cap, int* 
 
 // Grid of a persistent row kernel that needs `needed` block-steps.  Normally at most `cap`
 // blocks per CU (fewer bytes in flight stream better); but when that leaves each block
-// fewer than kTailSteps steps, the ramp and the last, partly filled round of steps weigh on
-// the launch, so every block-step is put in flight at once as far as occupancy allows (up
-// to kTailBlocksPerCu blocks per CU).  Measured: gated Ada + FP8 at [2520,3072] 4.96 ->
-// 5.27 TB/s, fused add at [2520,4096] 4.63 -> 5.56 TB/s (fewer than three steps); with the
-// threshold raised from three to five steps, fused add (+ static FP8) at [4096,4096]
+// fewer than `tail_steps` steps, the ramp and the last, partly filled round of steps weigh
+// on the launch, so every block-step is put in flight at once as far as occupancy allows
+// (up to kTailBlocksPerCu blocks per CU).  Measured: gated Ada + FP8 at [2520,3072] 4.96
+// -> 5.27 TB/s, fused add at [2520,4096] 4.63 -> 5.56 TB/s (fewer than three steps); with
+// the threshold raised from three to five steps, fused add (+ static FP8) at [4096,4096]
 // +12-13 %, block quant at [2048,7168] +8 %, gated Ada + FP8 at [4096,3072] +4 %, the
 // training forward of the [2048,8192] shard +3 %, the DiT modes at [4096,3072] -0.7 %.
 // At seven steps the DiT modes lost 3 % (at [6144,3072]), so launches of five or more
-// steps per block keep the cap.
+// steps per block keep the cap.  The fused add with a static FP8 output (a lighter write
+// share than the BF16 forms) gains from full occupancy up to eight steps per block: fused
+// add + FP8 [8192,4096] +3.8 %, [6144,4096] +6.8 %, per head [8192,32,128] +5.9 %,
+// unchanged at twelve steps; the single-input rmsnorm_quant lost 1.8 % at eight steps.
 constexpr int kTailBlocksPerCu = 8;
 constexpr int kTailSteps = 5;
+constexpr int kTailStepsAddFp8 = 9;
 
 dn_status persistent_grid(const void* kernel, int nt, size_t lds, int cap, int64_t needed,
-                          int* grid) {
+                          int* grid, int tail_steps = kTailSteps) {
   int capacity = 0;
   DN_CHECK(resident_blocks(kernel, nt, lds, cap, &capacity));
-  if (needed < kTailSteps * (int64_t)capacity) {
+  if (needed < tail_steps * (int64_t)capacity) {
     int full = 0;
     DN_CHECK(resident_blocks(kernel, nt, lds, kTailBlocksPerCu, &full));
     if (full > capacity) capacity = full;
@@ -233,7 +237,8 @@ dn_status launch_fwd(FwdParams p, hipStream_t stream) {
                   : single_stream ? DN_BLOCKS_PER_CU_SINGLE
                                   : DN_BLOCKS_PER_CU;
   int grid = 0;
-  DN_CHECK(persistent_grid(kernel, s.nt, lds, cap, needed, &grid));
+  constexpr int tail_steps = IN == IN_ADD && EPI == EPI_FP8 ? kTailStepsAddFp8 : kTailSteps;
+  DN_CHECK(persistent_grid(kernel, s.nt, lds, cap, needed, &grid, tail_steps));
   const hipError_t e = fwd_launch<IN, EPI>(p, tier, grid, lds, stream, nullptr);
   if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return DN_OK;
