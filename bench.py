@@ -270,6 +270,71 @@ def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm",
     return 0
 
 
+def kernel_resources(lib_path: str | None = None):
+    """Register, scratch and LDS figures of every kernel in libdnorm.so, from the AMDGPU
+    metadata notes of its gfx950 code objects (one per compile unit in the .hip_fatbin
+    section; extracted with the ROCm LLVM tools).  Returns a list of dicts with the
+    demangled name and: vgpr, agpr, sgpr, scratch bytes per lane (private segment),
+    vgpr/sgpr spill counts, static LDS bytes, the largest block size, and the waves one
+    SIMD can hold by registers (512 VGPRs per lane, allocated in groups of 8, at most 8)."""
+    import re
+    import shutil
+    import subprocess
+    import tempfile
+
+    import yaml
+    llvm = "/opt/rocm/llvm/bin"
+    so = lib_path or os.path.join(ROOT, "dit_normalization_amd", "libdnorm.so")
+    kernels = []
+    with tempfile.TemporaryDirectory() as d:
+        fb = os.path.join(d, "fatbin")
+        subprocess.run([f"{llvm}/llvm-objcopy", "--dump-section", f".hip_fatbin={fb}", so,
+                        os.path.join(d, "stripped")], check=True, capture_output=True)
+        data = open(fb, "rb").read()
+        starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
+        for i, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+            part, co = os.path.join(d, f"{i}.bundle"), os.path.join(d, f"{i}.co")
+            with open(part, "wb") as fh:
+                fh.write(data[a:b])
+            subprocess.run([f"{llvm}/clang-offload-bundler", "--unbundle", "--type=o",
+                            "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={part}",
+                            f"--output={co}"], check=True, capture_output=True)
+            notes = subprocess.run([f"{llvm}/llvm-readelf", "--notes", co], check=True,
+                                   capture_output=True, text=True).stdout
+            doc = notes[notes.index("---"):]
+            doc = doc[:doc.index("\n...")] if "\n..." in doc else doc
+            kernels += yaml.safe_load(doc)["amdhsa.kernels"]
+    names = [k[".name"] for k in kernels]
+    if shutil.which("c++filt"):
+        names = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True,
+                               text=True, check=True).stdout.split("\n")[:len(kernels)]
+    out = []
+    for n, k in zip(names, kernels):
+        regs = k[".vgpr_count"] + k.get(".agpr_count", 0)
+        alloc = max(8, (regs + 7) // 8 * 8)
+        out.append({"name": n.replace("void ", "").split("(")[0], "vgpr": k[".vgpr_count"],
+                    "agpr": k.get(".agpr_count", 0), "sgpr": k[".sgpr_count"],
+                    "scratch": k[".private_segment_fixed_size"],
+                    "vgpr_spill": k.get(".vgpr_spill_count", 0),
+                    "sgpr_spill": k.get(".sgpr_spill_count", 0),
+                    "lds_static": k[".group_segment_fixed_size"],
+                    "max_block": k[".max_flat_workgroup_size"],
+                    "waves_per_simd": min(8, 512 // alloc)})
+    return out
+
+
+def print_kernel_resources(match: str = "") -> int:
+    rows = [r for r in kernel_resources() if match in r["name"]]
+    print("| kernel | VGPR | AGPR | SGPR | scratch B/lane | spills (V/S) | static LDS B | "
+          "block | waves/SIMD by registers |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: r["name"]):
+        print(f"| `{r['name']}` | {r['vgpr']} | {r['agpr']} | {r['sgpr']} | {r['scratch']} | "
+              f"{r['vgpr_spill']}/{r['sgpr_spill']} | {r['lds_static']} | {r['max_block']} | "
+              f"{r['waves_per_simd']} |")
+    return 0
+
+
 def summarize_trace(stats_csv: str) -> int:
     rows = _read_csv(stats_csv)
     print("| kernel | calls | average ns | min ns | max ns | share |")
@@ -282,43 +347,68 @@ def summarize_trace(stats_csv: str) -> int:
     return 0
 
 
+def host_cores() -> int:
+    """Host threads the CPU baseline uses: the CPUs this process may run on, at most 16 (one
+    GPU's share of the GPU machine's host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _oracle_rate(run, bytes_per_pass: int, seconds: float, what: str):
+    """Time the oracle: `run` (one pass over a bounded sample of `bytes_per_pass` algorithmic
+    bytes) repeated for about `seconds` on every host core (one thread per core, each
+    looping the same pass; the oracle's numpy arithmetic releases the interpreter lock),
+    after a quarter as long on one core.  The cpu_baseline object of a bench line."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def loop(sec):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            done += 1
+            if time.perf_counter() - t0 >= sec:
+                return done
+
+    t0 = time.perf_counter()
+    one = loop(seconds / 4)
+    single = bytes_per_pass * one / (time.perf_counter() - t0) / 1e9
+    cores = host_cores()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        done = sum(ex.map(loop, [seconds] * cores))
+    el = time.perf_counter() - t0
+    return {"value": round(bytes_per_pass * done / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "single_core_value": round(single, 4),
+            "sample": f"{done} passes of {what} on {cores} threads in {el:.1f} s (numpy FP64; "
+                      f"{one} passes on one thread first)"}
+
+
 def cpu_baseline(seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same workload: row blocks of the
     fused-add + static-FP8 forward [*, 4096] and of the training forward and backward
-    [*, 8192], repeated until `seconds` of CPU time have passed."""
-    import numpy as np
-
+    [*, 8192], repeated for about `seconds` on every host core."""
     import workloads as W
-    from oracle import formats as F
     from oracle import rmsnorm as O
-
-    def vals(t):
-        import torch
-        if t.dtype == torch.bfloat16:
-            return F.bf16_bits_to_f64(t.contiguous().view(torch.int16).numpy().view(np.uint16))
-        return t.double().numpy()
 
     fa = W.fused_add_quant(rows=256)
     tr = W.train(rows=128)
-    x, r, w = vals(fa.tensors["x"]), vals(fa.tensors["residual"]), vals(fa.tensors["w"])
-    h, u, w4, g = (vals(tr.tensors[k]) for k in ("h", "residual", "w", "g"))
+    x, r, w = (_vals(fa.tensors[k]) for k in ("x", "residual", "w"))
+    h, u, w4, g = (_vals(tr.tensors[k]) for k in ("h", "residual", "w", "g"))
     b2 = 256 * C2[1]
     b4 = 128 * C4[1]
     per_pass = (7 * b2 + 2 * C2[1]) + (8 * b4 + 4 * 128 + 4 * C4[1]) + (6 * b4 + 4 * 128 + 8 * C4[1])
-    done, t0 = 0, time.perf_counter()
-    while True:
+
+    def run():
         O.fused_add_rmsnorm_quant(x, r, w, 0.04, 0.0, 1e-6)
         tf = O.train_forward(h, w4, 1.0, 1e-6, residual=u)
         O.train_backward(g, tf.h_new, w4, tf.rstd, 1.0)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(per_pass * done / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} passes of: fused add + RMSNorm + static FP8 on 256 rows x 4096, "
-                      f"training forward and backward on 128 rows x 8192 "
-                      f"({el:.1f} s, single-threaded numpy FP64)"}
+
+    return _oracle_rate(run, per_pass, seconds,
+                        "fused add + RMSNorm + static FP8 on 256 rows x 4096 and the training "
+                        "forward and backward on 128 rows x 8192")
 
 
 LN = (8192, 4096)
@@ -385,8 +475,113 @@ def fixed_alg_bytes():
             "rmsnorm_sigmoid_gate": 6 * es + 2 * SIGMOID[2]}
 
 
-FAMILY_BYTES = {"rmsnorm": alg_bytes, "layernorm": ln_alg_bytes, "qk_rope": qk_alg_bytes,
-                "silu": silu_alg_bytes, "fixed_width": fixed_alg_bytes}
+C3 = (16384, 7168)
+C5 = (2520, 3072)
+
+
+def configs_alg_bytes():
+    """Algorithmic HBM bytes per launch of the other hot-path configurations, in dispatch
+    order (large and small shapes alternate, so no launch finds its inputs in the Infinity
+    Cache)."""
+    t3, h3 = C3
+    t5, d5 = C5
+    t2, h2 = C2
+    e3, e5, e2 = t3 * h3, t5 * d5, t2 * h2
+    bq = 7 * e3 + 4 * t3 * (h3 // 128) + 2 * h3
+    # read x, residual, gate and the style rows' three chunks; write residual, e4m3 out and
+    # gate_out (each tensor of the definition once)
+    ada = (2 + 2 + 2 + 2 + 1 + 2) * e5 + 2 * d5 + 4
+    return {
+        # read x, residual; write h_new, e4m3 out, FP32 scales (MN-major); BF16 weight
+        "block_quant_16384x7168": bq,
+        "ada_gated_fp8_2520x3072": ada + 6 * e5,
+        # ... and normed_out
+        "block_quant_normed_out_16384x7168": bq + 2 * e3,
+        "ada_gated_fp8_broadcast_2520x3072": ada + 6 * d5,
+        # read x, residual; write h_new, e4m3 out; weight [128]
+        "fused_add_quant_per_head_8192x32x128": 7 * e2 + 2 * 128 + 4,
+        "fused_add_quant_gemma_8192x4096": 7 * e2 + 2 * h2 + 4,
+    }
+
+
+def run_configs_family(a) -> int:
+    """The other configurations of the hot path, back to back: 1x128 block FP8
+    [16384,7168] (with and without normed_out), the gated AdaRMSNorm + FP8 [2520,3072] with
+    per-row and broadcast style, and the fused add + static FP8 per head [8192,32,128] and
+    with the Gemma offset [8192,4096]."""
+    import torch
+
+    import workloads as W
+    from dit_normalization_amd import dnorm as dn
+    from oracle import rmsnorm as O
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating the configurations' inputs", file=sys.stderr, flush=True)
+    scale = torch.tensor([0.04], dtype=torch.float32, device=dev)
+    c3 = W.block_quant()
+    x3, r3, w3 = (c3.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    t3, h3 = C3
+    q3 = torch.empty(C3, dtype=torch.float8_e4m3fn, device=dev)
+    s3 = torch.empty((h3 // 128, (t3 + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    n3 = torch.empty_like(x3)
+    ada = {}
+    for bc in (False, True):
+        c5 = W.ada(broadcast=bc)
+        t = {k: c5.tensors[k].to(dev) for k in ("x", "residual", "gate", "w", "style")}
+        t["q"] = torch.empty(C5, dtype=torch.float8_e4m3fn, device=dev)
+        t["go"] = torch.empty(C5, dtype=torch.bfloat16, device=dev)
+        ada[bc] = t
+    c2h = W.fused_add_quant(8192, 128, heads=32)
+    x2h, r2h, w2h = (c2h.tensors[k].to(dev) for k in ("x", "residual", "w"))
+    q2h = torch.empty(x2h.shape, dtype=torch.float8_e4m3fn, device=dev)
+    c2 = W.fused_add_quant()
+    x2, r2 = c2.tensors["x"].to(dev), c2.tensors["residual"].to(dev)
+    wg = W.normal((C2[1],), 2, 7, std=0.1).to(dev)
+    q2 = torch.empty(C2, dtype=torch.float8_e4m3fn, device=dev)
+
+    def ada_call(bc):
+        t = ada[bc]
+        return lambda: dn.dn_gate_residual_ada_norm_fp8(t["residual"], t["x"], t["gate"], t["w"],
+                                                        t["style"], scale, 1e-6, out=t["q"],
+                                                        gate_out=t["go"])
+
+    calls = {
+        "block_quant_16384x7168": lambda: dn.dn_fused_add_rmsnorm_fp8_block_quant(
+            x3, r3, w3, 1e-6, out=q3, block_scale=s3),
+        "ada_gated_fp8_2520x3072": ada_call(False),
+        "block_quant_normed_out_16384x7168": lambda: dn.dn_fused_add_rmsnorm_fp8_block_quant(
+            x3, r3, w3, 1e-6, out=q3, block_scale=s3, normed_out=n3),
+        "ada_gated_fp8_broadcast_2520x3072": ada_call(True),
+        "fused_add_quant_per_head_8192x32x128": lambda: dn.dn_fused_add_rmsnorm_quant(
+            x2h, r2h, w2h, scale, 1e-6, out=q2h),
+        "fused_add_quant_gemma_8192x4096": lambda: dn.dn_fused_add_rmsnorm_quant(
+            x2, r2, wg, scale, 1e-6, w_bias=1.0, out=q2),
+    }
+
+    def cpu():
+        b = W.block_quant(rows=64)
+        xb, rb, wb = (_vals(b.tensors[k]) for k in ("x", "residual", "w"))
+        c5 = W.ada(rows=64)
+        d = {k: _vals(c5.tensors[k]) for k in ("x", "residual", "gate", "w", "style")}
+        per = 7 * 64 * h3 + 17 * 64 * C5[1]
+
+        def run():
+            O.fused_add_rmsnorm_fp8_block_quant(xb, rb, wb, 0.0, 1e-6)
+            O.gate_residual_ada_norm_fp8(d["residual"], d["x"], d["gate"], d["w"], d["style"],
+                                         0.04, 1e-6)
+        return _oracle_rate(run, per, a.cpu_seconds / 2,
+                            "block FP8 on 64 rows x 7168 and the gated AdaRMSNorm + FP8 on 64 "
+                            "rows x 3072")
+
+    return time_family(a, torch, dev, calls, "achieved HBM GB/s, the other hot-path "
+                       "configurations", "block FP8 [16384,7168] (+normed_out), gated "
+                       "AdaRMSNorm + FP8 [2520,3072] per-row and broadcast style, fused add + "
+                       "static FP8 per head [8192,32,128] and Gemma [8192,4096]", cpu)
+
+
+FAMILY_BYTES = {"rmsnorm": alg_bytes, "configs": configs_alg_bytes, "layernorm": ln_alg_bytes,
+                "qk_rope": qk_alg_bytes, "silu": silu_alg_bytes, "fixed_width": fixed_alg_bytes}
 
 
 def _stats(ts):
@@ -414,14 +609,35 @@ def device_copy_ceiling(torch, dev, reps: int = 5) -> float:
     return round(2 * (1 << 30) / sorted(ts)[len(ts) // 2] / 1e9, 1)
 
 
+PROBE_SRC = os.path.join(ROOT, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "probe", "libdnprobe.so")
+
+
+def probe_library(rebuild: bool = False) -> str:
+    """Path of the stream-ceiling probe library (probe/stream_probe.hip, a measurement aid
+    outside the norm library), compiled with hipcc for gfx950 when it is missing."""
+    if rebuild or not os.path.exists(PROBE_LIB):
+        import subprocess
+
+        from dit_normalization_amd import build as B
+        obj = B._compile(PROBE_SRC, False, objdir=os.path.dirname(PROBE_LIB))
+        tmp = PROBE_LIB + ".tmp"
+        r = subprocess.run([B.HIPCC, f"--offload-arch={B.ARCH}", "-shared", "-fPIC", "-o", tmp,
+                            obj], capture_output=True, text=True)
+        os.remove(obj)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe link failed:\n{r.stdout}{r.stderr}")
+        os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def stream_ceilings(torch, dev, reps: int = 5):
     """Measured HBM stream ceilings (libdnprobe.so): plain kernels with the norm kernels'
     16-byte non-temporal buffer loads and stores at their read:write mixes, 256 MiB per
     stream, each mix at 1 and 2 blocks of 256 threads per CU, chunked and grid-stride; the
     best configuration's median GB/s of bytes moved per mix."""
     import ctypes
-    path = os.path.join(ROOT, "dit_normalization_amd", "libdnprobe.so")
-    lib = ctypes.CDLL(path)
+    lib = ctypes.CDLL(probe_library())
     f = lib.dn_probe_stream
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
     f.restype = ctypes.c_int
@@ -652,21 +868,6 @@ def run_layernorm_family(a) -> int:
                        "[16384,18432] tensor", cpu)
 
 
-def _oracle_rate(run, bytes_per_pass: int, seconds: float, what: str):
-    """Time `run` (one oracle pass over a bounded sample of `bytes_per_pass` algorithmic
-    bytes) repeatedly for about `seconds`; the cpu_baseline object of a family line."""
-    done, t0 = 0, time.perf_counter()
-    while True:
-        run()
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(bytes_per_pass * done / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} passes of {what} ({el:.1f} s, single-threaded numpy FP64)"}
-
-
 def _vals(t):
     """Host float64 values of a BF16 / FP32 torch CPU tensor (the oracle's BF16 decoder)."""
     import numpy as np
@@ -892,7 +1093,10 @@ def main(argv=None) -> int:
                          "library dispatch is then a bench-step kernel)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", metavar="STATS_CSV")
-    ap.add_argument("--family", choices=("rmsnorm", "layernorm", "qk_rope", "silu",
+    ap.add_argument("--kernel-resources", nargs="?", const="", metavar="MATCH",
+                    help="print the registers, scratch and LDS of the library's kernels "
+                         "(those whose name contains MATCH) from the code objects; no GPU")
+    ap.add_argument("--family", choices=("rmsnorm", "configs", "layernorm", "qk_rope", "silu",
                                          "fixed_width"),
                     default="rmsnorm",
                     help="rmsnorm: the hot-path step (default); layernorm: the LayerNorm "
@@ -907,6 +1111,8 @@ def main(argv=None) -> int:
         return summarize_counters(*a.summarize_counters, family=a.family)
     if a.summarize_trace:
         return summarize_trace(a.summarize_trace)
+    if a.kernel_resources is not None:
+        return print_kernel_resources(a.kernel_resources)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the RMSNorm path here is built and timed on a single "
               f"MI355X (rows shard across GPUs with no communication except dw); --gpus {a.gpus} "
@@ -919,6 +1125,8 @@ def main(argv=None) -> int:
     from dit_normalization_amd import dnorm as dn
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.family == "configs":
+        return run_configs_family(a)
     if a.family == "layernorm":
         return run_layernorm_family(a)
     if a.family == "qk_rope":

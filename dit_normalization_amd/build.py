@@ -81,24 +81,6 @@ def build(jobs: int | None = None, verbose: bool = False, extra=(), out: str = L
     return out
 
 
-PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
-PROBE_LIB = os.path.join(PKG, "libdnprobe.so")
-
-
-def build_probe(verbose: bool = False) -> str:
-    """Compile the HBM stream-ceiling probe (a measurement aid loaded by bench.py only) into
-    libdnprobe.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    obj = _compile(PROBE_SRC, verbose)
-    tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, PROBE_LIB)
-    return PROBE_LIB
-
-
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
@@ -106,7 +88,6 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     path = build(a.jobs, a.verbose)
     print(path)
-    print(build_probe(a.verbose))
     return 0
 
 

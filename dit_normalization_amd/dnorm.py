@@ -116,34 +116,58 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _rows(t: torch.Tensor, name: str, dtype=torch.bfloat16):
+def _rows(t: torch.Tensor, name: str, dtype=torch.bfloat16, width=None, rows=None):
     """(tensor, rows, row_stride) of an activation [..., H] read row by row.
 
     Leading dimensions collapse into rows when the feature dimension is contiguous and the
-    leading dimensions are contiguous with one another (stride(i) == stride(i+1)*size(i+1));
-    any other layout is copied once, the rule of cake_rmsnorm_det_train_forward (x).
+    leading dimensions of size above one are contiguous with one another
+    (stride(i) == stride(j) * size(j) for consecutive such dimensions i < j); the row stride
+    is then the stride of the innermost of them, which must keep rows apart (>= H) and
+    16-byte vectors aligned (a multiple of 8).  Dimensions of size one carry no rows and
+    their strides do not matter.  Any other layout is copied once, the rule of
+    cake_rmsnorm_det_train_forward (x).  `width` and `rows`, when given, are the shape the
+    tensor must have (H, and the number of rows).
     """
     if not t.is_cuda:
         raise DnormError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise DnormError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() == 0:
+        raise DnormError(f"{name} must have at least one dimension")
     if t.dim() == 1:
         t = t.unsqueeze(0)
-    ok = t.stride(-1) == 1 and all(
-        t.stride(i) == t.stride(i + 1) * t.size(i + 1) for i in range(t.dim() - 2))
-    if t.dim() >= 2 and t.size(-2) > 1:
-        # rows must not overlap (a broadcast gradient has row stride 0) and must keep
-        # 16-byte alignment from one to the next
-        ok = ok and t.stride(-2) >= t.size(-1) and t.stride(-2) % 8 == 0
+    H = t.size(-1)
+    n = 1
+    for sz in t.shape[:-1]:
+        n *= sz
+    if width is not None and H != width:
+        raise DnormError(f"{name} has rows of {H} elements, {width} expected")
+    if rows is not None and n != rows:
+        raise DnormError(f"{name} holds {n} rows, {rows} expected")
+    lead = [(sz, st) for sz, st in zip(t.shape[:-1], t.stride()[:-1]) if sz != 1]
+    ok = t.stride(-1) == 1 or H <= 1
+    for (_, st0), (sz1, st1) in zip(lead, lead[1:]):
+        ok = ok and st0 == st1 * sz1
+    stride = lead[-1][1] if lead else H
+    if lead:
+        ok = ok and stride >= H and stride % 8 == 0
     if not ok:
         t = t.contiguous()
+        stride = H
     if t.data_ptr() % 16 != 0:
-        t = t.clone()             # a fresh (aligned) allocation, even for a contiguous view
-    rows = 1
-    for s in t.shape[:-1]:
-        rows *= s
-    stride = t.stride(-2) if t.dim() >= 2 and t.size(-2) > 1 else t.size(-1)
-    return t, rows, stride
+        t = t.clone(memory_format=torch.contiguous_format)   # a fresh, aligned allocation
+        stride = H
+    return t, n, stride
+
+
+def _vector(t: torch.Tensor, name: str, n: int, dtypes=(torch.bfloat16, torch.float32)):
+    """A per-column parameter vector: n values of one of `dtypes`, on a device."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise DnormError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise DnormError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if t.numel() != n:
+        raise DnormError(f"{name} must hold {n} values, got {t.numel()}")
 
 
 def _rstd_buffer(rstd, rows: int, device, name: str = "rstd"):
@@ -158,16 +182,25 @@ def _rstd_buffer(rstd, rows: int, device, name: str = "rstd"):
     return rstd
 
 
-def _weight(w: torch.Tensor):
+def _weight(w: torch.Tensor, n: int, name: str = "weight"):
+    _vector(w, name, n)
     if w.dtype == torch.bfloat16:
         code = DN_WEIGHT_BF16
     elif w.dtype == torch.float32:
         code = DN_WEIGHT_F32
     else:
-        raise DnormError(f"weight must be bfloat16 or float32, got {w.dtype}")
+        raise DnormError(f"{name} must be bfloat16 or float32, got {w.dtype}")
     if not w.is_contiguous() or w.data_ptr() % 16 != 0:
         w = w.contiguous().clone()
     return w, code
+
+
+def _style(style, rows: int, dim: int):
+    """Ada style rows: [rows, 3*dim] (one per token) or [1, 3*dim] / [3*dim] (broadcast)."""
+    st, srows, sst = _rows(style, "style", width=3 * dim)
+    if srows not in (1, rows):
+        raise DnormError(f"style must hold 1 or {rows} rows, got {srows}")
+    return st, srows, sst
 
 
 def _scale_tensor(scale, device):
@@ -195,9 +228,9 @@ def dn_rmsnorm(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=None, rstd=N
     """y = BF16(x * r * (w + w_bias)) per row; returns y (and rstd)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
-    yr, _, sy = _rows(y, "out")
+    yr, _, sy = _rows(y, "out", width=H, rows=rows)
     if return_rstd and rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _rstd_buffer(rstd, rows, x.device)
@@ -211,9 +244,9 @@ def dn_rmsnorm_quant(x, w, scale, eps: float = 1e-6, *, w_bias: float = 0.0, out
     """out = e4m3fn(rmsnorm(x) / scale)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
-    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn, width=H, rows=rows)
     s = _scale_tensor(scale, x.device)
     _check(lib.dn_rmsnorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, w.data_ptr(), wcode, w_bias,
                                 s.data_ptr(), rows, H, eps, _stream(x)), "dn_rmsnorm_quant")
@@ -225,12 +258,10 @@ def dn_fused_add_rmsnorm(x, residual, w, eps: float = 1e-6, *, w_bias: float = 0
     """In place: residual <- x + residual; x <- rmsnorm(residual).  Both must be views the
     kernel can address directly (leading dimensions collapsible)."""
     xr, rows, sx = _rows(x, "x")
-    rr, rows_r, sr = _rows(residual, "residual")
+    rr, _, sr = _rows(residual, "residual", width=xr.size(-1), rows=rows)
     if xr.data_ptr() != x.data_ptr() or rr.data_ptr() != residual.data_ptr():
         raise DnormError("fused_add_rmsnorm works in place: x and residual need row-addressable layouts")
-    if rows_r != rows or rr.size(-1) != xr.size(-1):
-        raise DnormError("x and residual must have the same shape")
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, xr.size(-1))
     _rstd_buffer(rstd, rows, x.device)
     _check(lib.dn_fused_add_rmsnorm(xr.data_ptr(), sx, rr.data_ptr(), sr, w.data_ptr(), wcode,
                                     w_bias, _ptr(rstd), rows, xr.size(-1), eps, _stream(x)),
@@ -241,12 +272,13 @@ def dn_fused_add_rmsnorm_quant(x, residual, w, scale, eps: float = 1e-6, *, w_bi
                                out=None):
     """residual <- x + residual (in place); returns out = e4m3fn(rmsnorm(residual) / scale)."""
     xr, rows, sx = _rows(x, "x")
-    rr, _, sr = _rows(residual, "residual")
+    H = xr.size(-1)
+    rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
     if rr.data_ptr() != residual.data_ptr():
         raise DnormError("residual is updated in place: it needs a row-addressable layout")
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
-    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn, width=H, rows=rows)
     s = _scale_tensor(scale, x.device)
     _check(lib.dn_fused_add_rmsnorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, rr.data_ptr(), sr,
                                           w.data_ptr(), wcode, w_bias, s.data_ptr(), rows,
@@ -262,21 +294,29 @@ def dn_fused_add_rmsnorm_fp8_block_quant(x, residual, w, eps: float = 1e-6, *, w
     shape (hidden/128, round_up(rows, 4)) -- column-major per row, the logical
     [rows, hidden/128] scales being block_scale.T[:rows]."""
     xr, rows, sx = _rows(x, "x")
-    rr, _, sr = _rows(residual, "residual")
+    H = xr.size(-1)
+    rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
     if rr.data_ptr() != residual.data_ptr():
         raise DnormError("residual is updated in place: it needs a row-addressable layout")
-    H = xr.size(-1)
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
-    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn, width=H, rows=rows)
     ld = (rows + 3) // 4 * 4
     if block_scale is None:
         block_scale = torch.empty((H // 128, ld), dtype=torch.float32, device=x.device)
     else:
-        ld = block_scale.stride(0)
+        # The kernel writes every entry [k][t] for t < ld (pads included): the caller's
+        # buffer must own all of them.
+        if block_scale.dtype != torch.float32 or not block_scale.is_cuda or \
+                block_scale.dim() != 2 or block_scale.size(0) != H // 128 or \
+                block_scale.size(1) < rows or not block_scale.is_contiguous():
+            raise DnormError(f"block_scale must be a contiguous float32 device tensor of shape "
+                             f"({H // 128}, >= {rows}), got {block_scale.dtype} "
+                             f"{tuple(block_scale.shape)}")
+        ld = block_scale.size(1)
     nr, sn = None, 0
     if normed_out is not None:
-        nr, _, sn = _rows(normed_out, "normed_out")
+        nr, _, sn = _rows(normed_out, "normed_out", width=H, rows=rows)
     _check(lib.dn_fused_add_rmsnorm_fp8_block_quant(
         qr.data_ptr(), sq, block_scale.data_ptr(), ld, _ptr(nr), sn, xr.data_ptr(), sx,
         rr.data_ptr(), sr, w.data_ptr(), wcode, w_bias, rows, H, eps, _stream(x)),
@@ -291,12 +331,12 @@ def dn_ada_rms_norm(x, w, style, eps: float = 1e-6, *, out=None, gate_out=None):
     """out = BF16(rmsnorm(x, w) * (1 + style_scale) + style_shift); returns (out, gate_out)."""
     xr, rows, sx = _rows(x, "x")
     dim = xr.size(-1)
-    w, _ = _weight(w)
-    st, srows, sst = _rows(style, "style")
+    w, _ = _weight(w, dim)
+    st, srows, sst = _style(style, rows, dim)
     o = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
-    orr, _, so = _rows(o, "out")
+    orr, _, so = _rows(o, "out", width=dim, rows=rows)
     g = gate_out if gate_out is not None else _out_like(x, x.shape, torch.bfloat16)
-    gr, _, sg = _rows(g, "gate_out")
+    gr, _, sg = _rows(g, "gate_out", width=dim, rows=rows)
     _check(lib.dn_ada_rms_norm(orr.data_ptr(), so, gr.data_ptr(), sg, xr.data_ptr(), sx,
                                w.data_ptr(), st.data_ptr(), sst, srows, rows, dim, eps,
                                _stream(x)), "dn_ada_rms_norm")
@@ -312,14 +352,14 @@ def dn_gate_residual_ada_norm_fp8(residual, x, gate, w, style, scale, eps: float
     if rr.data_ptr() != residual.data_ptr():
         raise DnormError("residual is updated in place: it needs a row-addressable layout")
     dim = rr.size(-1)
-    xr, _, sx = _rows(x, "x")
-    gtr, _, sgt = _rows(gate, "gate")
-    w, _ = _weight(w)
-    st, srows, sst = _rows(style, "style")
+    xr, _, sx = _rows(x, "x", width=dim, rows=rows)
+    gtr, _, sgt = _rows(gate, "gate", width=dim, rows=rows)
+    w, _ = _weight(w, dim)
+    st, srows, sst = _style(style, rows, dim)
     q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
-    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn, width=dim, rows=rows)
     g = gate_out if gate_out is not None else _out_like(x, x.shape, torch.bfloat16)
-    gr, _, sg = _rows(g, "gate_out")
+    gr, _, sg = _rows(g, "gate_out", width=dim, rows=rows)
     s = _scale_tensor(scale, x.device)
     _check(lib.dn_gate_residual_ada_norm_fp8(
         rr.data_ptr(), sr, qr.data_ptr(), sq, gr.data_ptr(), sg, xr.data_ptr(), sx,
@@ -335,18 +375,18 @@ def dn_train_forward(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, residual=N
     """(y, rstd) or, with a residual, (y, rstd, h_new)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
-    yr, _, sy = _rows(y, "out")
+    yr, _, sy = _rows(y, "out", width=H, rows=rows)
     if rstd is None:
         rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _rstd_buffer(rstd, rows, x.device)
     hr, sh, rsr, srs = None, 0, None, 0
     if residual is not None:
-        rsr, _, srs = _rows(residual, "residual")
+        rsr, _, srs = _rows(residual, "residual", width=H, rows=rows)
         if residual_out is None:
             residual_out = _out_like(x, x.shape, torch.bfloat16)
-        hr, _, sh = _rows(residual_out, "residual_out")
+        hr, _, sh = _rows(residual_out, "residual_out", width=H, rows=rows)
     _check(lib.dn_train_forward(yr.data_ptr(), sy, rstd.data_ptr(), _ptr(hr), sh, xr.data_ptr(), sx,
                                 _ptr(rsr), srs, w.data_ptr(), wcode, w_bias, rows, H, eps,
                                 _stream(x)), "dn_train_forward")
@@ -370,16 +410,17 @@ def train_backward_workspace(hidden: int, device) -> torch.Tensor:
 
 def _bwd_common(g, x, w, rstd, g_residual, dx):
     gr, rows, sg = _rows(g, "g")
-    xr, _, sx = _rows(x, "x")
-    w, wcode = _weight(w)
+    H = gr.size(-1)
+    xr, _, sx = _rows(x, "x", width=H, rows=rows)
+    w, wcode = _weight(w, H)
     if rstd is None:
         raise DnormError("rstd (the forward's FP32 per-row output) is required")
     _rstd_buffer(rstd, rows, g.device)
     d = dx if dx is not None else _out_like(x, x.shape, torch.bfloat16)
-    dr, _, sd = _rows(d, "dx")
+    dr, _, sd = _rows(d, "dx", width=H, rows=rows)
     grr, sgr = None, 0
     if g_residual is not None:
-        grr, _, sgr = _rows(g_residual, "g_residual")
+        grr, _, sgr = _rows(g_residual, "g_residual", width=H, rows=rows)
     return gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr
 
 
@@ -429,10 +470,9 @@ def dn_train_backward_reduce(workspace, rows: int, hidden: int, *, dw=None):
     return dw
 
 
-def _affine(t: torch.Tensor, name: str):
+def _affine(t: torch.Tensor, name: str, n: int):
     """LayerNorm gamma / beta: FP32 [hidden], contiguous and 16-byte aligned."""
-    if t.dtype != torch.float32:
-        raise DnormError(f"{name} must be float32, got {t.dtype}")
+    _vector(t, name, n, (torch.float32,))
     if not t.is_contiguous() or t.data_ptr() % 16 != 0:
         t = t.contiguous().clone()
     return t
@@ -442,9 +482,9 @@ def dn_layernorm(x, gamma, beta, eps: float = 1e-6, *, out=None):
     """y = BF16(LayerNorm(x) * gamma + beta) per row (population variance)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
+    g, b = _affine(gamma, "gamma", H), _affine(beta, "beta", H)
     y = out if out is not None else _out_like(x, x.shape, torch.bfloat16)
-    yr, _, sy = _rows(y, "out")
+    yr, _, sy = _rows(y, "out", width=H, rows=rows)
     _check(lib.dn_layernorm(yr.data_ptr(), sy, xr.data_ptr(), sx, g.data_ptr(), b.data_ptr(), rows,
                             H, eps, _stream(x)), "dn_layernorm")
     _writeback(y, yr)
@@ -455,9 +495,9 @@ def dn_layernorm_quant(x, gamma, beta, scale, eps: float = 1e-6, *, out=None):
     """out = e4m3fn((LayerNorm(x) * gamma + beta) / scale)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
+    g, b = _affine(gamma, "gamma", H), _affine(beta, "beta", H)
     q = out if out is not None else _out_like(x, x.shape, torch.float8_e4m3fn)
-    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn)
+    qr, _, sq = _rows(q, "out", torch.float8_e4m3fn, width=H, rows=rows)
     s = _scale_tensor(scale, x.device)
     _check(lib.dn_layernorm_quant(qr.data_ptr(), sq, xr.data_ptr(), sx, g.data_ptr(), b.data_ptr(),
                                   s.data_ptr(), rows, H, eps, _stream(x)), "dn_layernorm_quant")
@@ -465,13 +505,13 @@ def dn_layernorm_quant(x, gamma, beta, scale, eps: float = 1e-6, *, out=None):
     return q
 
 
-def _dit_outputs(x, residual_out, norm_out, want_residual_out: bool):
+def _dit_outputs(x, residual_out, norm_out, want_residual_out: bool, rows: int, H: int):
     n = norm_out if norm_out is not None else _out_like(x, x.shape, torch.bfloat16)
-    nr, _, sn = _rows(n, "norm_out")
+    nr, _, sn = _rows(n, "norm_out", width=H, rows=rows)
     ro, ror, sro = None, None, 0
     if want_residual_out:
         ro = residual_out if residual_out is not None else _out_like(x, x.shape, torch.bfloat16)
-        ror, _, sro = _rows(ro, "residual_out")
+        ror, _, sro = _rows(ro, "residual_out", width=H, rows=rows)
     return n, nr, sn, ro, ror, sro
 
 
@@ -483,10 +523,10 @@ def dn_fused_dit_gate_residual_layernorm_gamma_beta(x, residual, gate, gamma, be
     per-token chunk view (row stride 6*hidden)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    rr, _, sr = _rows(residual, "residual")
-    gt, _, sg = _rows(gate, "gate")
-    g, b = _affine(gamma, "gamma"), _affine(beta, "beta")
-    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True)
+    rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
+    gt, _, sg = _rows(gate, "gate", width=H, rows=rows)
+    g, b = _affine(gamma, "gamma", H), _affine(beta, "beta", H)
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True, rows, H)
     _check(lib.dn_fused_dit_gate_residual_layernorm_gamma_beta(
         ror.data_ptr(), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, rr.data_ptr(), sr,
         gt.data_ptr(), sg, gate_bias, g.data_ptr(), b.data_ptr(), rows, H, eps, _stream(x)),
@@ -506,11 +546,11 @@ def dn_fused_dit_gate_residual_layernorm_scale_shift(x, residual, gate, scale, s
     (residual_out, norm_out)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    rr, _, sr = _rows(residual, "residual")
-    gt, _, sg = _rows(gate, "gate")
-    sc, _, ssc = _rows(scale, "scale")
-    sh, _, ssh = _rows(shift, "shift")
-    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True)
+    rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
+    gt, _, sg = _rows(gate, "gate", width=H, rows=rows)
+    sc, _, ssc = _rows(scale, "scale", width=H, rows=rows)
+    sh, _, ssh = _rows(shift, "shift", width=H, rows=rows)
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, True, rows, H)
     _check(lib.dn_fused_dit_gate_residual_layernorm_scale_shift(
         ror.data_ptr(), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, rr.data_ptr(), sr,
         gt.data_ptr(), sg, gate_bias, sc.data_ptr(), ssc, scale_bias, sh.data_ptr(), ssh,
@@ -530,12 +570,13 @@ def dn_fused_dit_residual_layernorm_scale_shift(x, scale, shift, residual=None,
     residual_out None without a residual."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    sc, _, ssc = _rows(scale, "scale")
-    sh, _, ssh = _rows(shift, "shift")
+    sc, _, ssc = _rows(scale, "scale", width=H, rows=rows)
+    sh, _, ssh = _rows(shift, "shift", width=H, rows=rows)
     rr, sr = None, 0
     if residual is not None:
-        rr, _, sr = _rows(residual, "residual")
-    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, residual is not None)
+        rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
+    n, nr, sn, ro, ror, sro = _dit_outputs(x, residual_out, norm_out, residual is not None, rows,
+                                           H)
     _check(lib.dn_fused_dit_residual_layernorm_scale_shift(
         _ptr(ror), sro, nr.data_ptr(), sn, xr.data_ptr(), sx, _ptr(rr), sr, sc.data_ptr(), ssc,
         scale_bias, sh.data_ptr(), ssh, shift_bias, rows, H, eps, _stream(x)),
@@ -552,11 +593,11 @@ def dn_fused_rmsnorm_silu(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=N
     `out` is a float8_e4m3fn tensor)."""
     xr, rows, sx = _rows(x, "x")
     H = xr.size(-1)
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     fp8 = bool(output_fp8) or (out is not None and out.dtype == torch.float8_e4m3fn)
     odt = torch.float8_e4m3fn if fp8 else torch.bfloat16
     o = out if out is not None else _out_like(x, x.shape, odt)
-    orr, _, so = _rows(o, "out", odt)
+    orr, _, so = _rows(o, "out", odt, width=H, rows=rows)
     s = _scale_tensor(scale, x.device) if fp8 else None
     _check(lib.dn_fused_rmsnorm_silu(orr.data_ptr(), so, int(fp8), _ptr(s), xr.data_ptr(), sx,
                                      w.data_ptr(), wcode, w_bias, rows, H, eps, _stream(x)),
@@ -567,15 +608,14 @@ def dn_fused_rmsnorm_silu(x, w, eps: float = 1e-6, *, w_bias: float = 0.0, out=N
 
 def _gres_args(branch, residual, gate, w):
     br, rows, sb = _rows(branch, "branch")
-    rr, rrows, sr = _rows(residual, "residual")
+    H = br.size(-1)
+    rr, _, sr = _rows(residual, "residual", width=H, rows=rows)
     if rr.data_ptr() != residual.data_ptr():
         raise DnormError("residual is updated in place: it needs a row-addressable layout")
-    if rrows != rows or rr.size(-1) != br.size(-1):
-        raise DnormError("branch and residual must have the same shape")
-    gr, grows, sg = _rows(gate, "gate")
-    if gr.size(-1) != br.size(-1) or grows not in (1, rows):
+    gr, grows, sg = _rows(gate, "gate", width=H)
+    if grows not in (1, rows):
         raise DnormError("gate must be [hidden], [1, hidden] or branch-shaped")
-    w, wcode = _weight(w)
+    w, wcode = _weight(w, H)
     return br, rows, sb, rr, sr, gr, grows, sg, w, wcode
 
 
@@ -595,9 +635,9 @@ def dn_gated_residual_next_rmsnorm(branch, residual, gate, w, w_next, eps: float
     """As dn_gated_residual_rmsnorm, then out = RMSNorm(residual, w_next) in the same launch;
     returns (residual, out)."""
     br, rows, sb, rr, sr, gr, grows, sg, w, wcode = _gres_args(branch, residual, gate, w)
-    w2, wcode2 = _weight(w_next)
+    w2, wcode2 = _weight(w_next, br.size(-1), "w_next")
     o = out if out is not None else _out_like(branch, branch.shape, torch.bfloat16)
-    orr, _, so = _rows(o, "out")
+    orr, _, so = _rows(o, "out", width=br.size(-1), rows=rows)
     _check(lib.dn_gated_residual_next_rmsnorm(
         orr.data_ptr(), so, rr.data_ptr(), sr, br.data_ptr(), sb, gr.data_ptr(), sg, grows,
         w.data_ptr(), wcode, w_bias, w2.data_ptr(), wcode2, w_next_bias, rows, br.size(-1), eps,
@@ -613,10 +653,8 @@ def dn_rmsnorm_sigmoid_gate(x, gate, eps: float = 1e-6, *, weight=None, w_bias: 
     if xr.data_ptr() != x.data_ptr():
         raise DnormError("rmsnorm_sigmoid_gate works in place: x needs a row-addressable layout")
     hd = xr.size(-1)
-    gr, grows, sg = _rows(gate, "gate")
-    if grows != rows or gr.size(-1) != hd:
-        raise DnormError("gate must have x's shape")
-    w, wcode = (None, DN_WEIGHT_BF16) if weight is None else _weight(weight)
+    gr, _, sg = _rows(gate, "gate", width=hd, rows=rows)
+    w, wcode = (None, DN_WEIGHT_BF16) if weight is None else _weight(weight, hd)
     _check(lib.dn_rmsnorm_sigmoid_gate(xr.data_ptr(), sx, gr.data_ptr(), sg, _ptr(w), wcode, w_bias,
                                        rows, hd, eps, _stream(x)), "dn_rmsnorm_sigmoid_gate")
     return x
@@ -633,15 +671,15 @@ def dn_fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, num_heads_q: int, num_head
     """Cross-head RMSNorm of Q and K, 3-D RoPE (frame/height/width channel groups
     `channels`), V copy.  qkv: BF16 [tokens, (nq+nk+nv)*head_dim] or [batch, seq, ...].
     Returns (q_out, k_out, v_out), BF16 or (output_fp8) e4m3fn."""
-    xr, rows, sx = _rows(qkv, "qkv")
-    lead = qkv.shape[:-1]
     nq, nk, nv, hd = int(num_heads_q), int(num_heads_k), int(num_heads_v), int(head_dim)
+    xr, rows, sx = _rows(qkv, "qkv", width=(nq + nk + nv) * hd)
+    lead = qkv.shape[:-1]
     odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
 
     def out(t, heads, name):
         if t is None:
             t = torch.empty((*lead, heads * hd), dtype=odt, device=qkv.device)
-        tr, _, st = _rows(t, name, odt)
+        tr, _, st = _rows(t, name, odt, width=heads * hd, rows=rows)
         if tr.data_ptr() != t.data_ptr():
             raise DnormError(f"{name} needs a row-addressable layout")
         return t, tr, st
@@ -652,8 +690,8 @@ def dn_fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, num_heads_q: int, num_head
     wq = wk = None
     wcode = DN_WEIGHT_BF16
     if is_qk_norm:
-        wq, wcode = _weight(q_weight)
-        wk, wcode_k = _weight(k_weight)
+        wq, wcode = _weight(q_weight, nq * hd, "q_weight")
+        wk, wcode_k = _weight(k_weight, nk * hd, "k_weight")
         if wcode_k != wcode:
             raise DnormError("q_weight and k_weight must have the same dtype")
     qs = vs = None

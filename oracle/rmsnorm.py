@@ -168,14 +168,30 @@ class BlockQuant:
     rstd: np.ndarray
     scale: np.ndarray           # FP32 [rows, hidden/128], logical layout
     q: np.ndarray               # e4m3fn codes [rows, hidden]
-    elem_tie: np.ndarray        # FP8 rounding tie, or BF16 tie of the normed value
-    block_flag: np.ndarray      # [rows, hidden/128]: the block's amax itself is uncertain
-    scale_alt: np.ndarray       # FP32 scale that a flagged block may take instead
+    fp8_tie: np.ndarray         # normed / scale lies next to an e4m3 rounding midpoint
+    bf_tie: np.ndarray          # the normalised value lies next to a BF16 midpoint
+    q_nb: np.ndarray            # codes of the other BF16 neighbour (bf_tie elements)
+    nb_tie: np.ndarray          # fp8_tie of the other neighbour
+    block_flag: np.ndarray      # [rows, hidden/128]: the block's amax has two possible values
+    scale_alt: np.ndarray       # the other possible FP32 scale of a flagged block (else scale)
+    q_alt: np.ndarray           # q, fp8_tie, q_nb and nb_tie under scale_alt
+    fp8_tie_alt: np.ndarray
+    q_nb_alt: np.ndarray
+    nb_tie_alt: np.ndarray
 
 
 def block_scale_of(amax) -> np.ndarray:
     """s = FP32(amax / 448): the per-block dynamic scale (norm guide §3.3, step 3)."""
     return f32_round(np.asarray(amax, dtype=np.float64) / E4M3_MAX)
+
+
+def _block_codes(blocks, s, nan):
+    """e4m3fn codes of blocks / s (a zero-scale block coded 0 except its NaN elements), and
+    where blocks / s lies next to an e4m3 rounding midpoint."""
+    safe = np.where(s > 0, s, 1.0)
+    v = blocks / safe[:, :, None]
+    q = np.where((s > 0)[:, :, None] | nan, f64_to_e4m3_code(v), np.uint8(0)).astype(np.uint8)
+    return q, e4m3_near_tie(v) & (s > 0)[:, :, None]
 
 
 def fused_add_rmsnorm_fp8_block_quant(x, residual, w, bias: float = 0.0,
@@ -192,6 +208,18 @@ def fused_add_rmsnorm_fp8_block_quant(x, residual, w, bias: float = 0.0,
     magnitude that is a number, IEEE maxNum, so a NaN element neither sets nor hides its
     block's scale (0 when the block holds no number), and a NaN element is coded NaN in
     every block, a zero-scale block included.
+
+    Results that are not unique: an FP32 evaluation of the normalised value may round an
+    element that lies next to a BF16 midpoint (bf16_near_tie) to either neighbour, so each
+    such element takes one of two adjacent BF16 magnitudes lo < hi, and every other element
+    its nominal magnitude.  The block's amax is then one of at most two values: with m the
+    largest of the fixed magnitudes and of every tied element's lo, any tied element whose
+    hi exceeds m has lo <= m < hi, and as lo and hi are adjacent BF16 magnitudes and m is a
+    BF16 magnitude, lo = m and hi is m's successor.  So the amax is m, or m's successor when
+    some tied element has lo = m; block_flag marks the blocks where both are possible, and
+    the *_alt fields give the codes under the value the nominal rounding did not take.
+    Under either scale, a tied element is coded from either neighbour (q or q_nb), and a
+    value next to an e4m3 midpoint may take either adjacent code (fp8_tie, nb_tie).
     """
     fa = fused_add_rmsnorm(x, residual, w, bias, eps)
     n = fa.norm.y
@@ -202,29 +230,26 @@ def fused_add_rmsnorm_fp8_block_quant(x, residual, w, bias: float = 0.0,
     mags = np.where(nan, 0.0, np.abs(blocks))            # magnitudes are >= 0: NaN drops out
     amax = np.max(mags, axis=2)
     s = block_scale_of(amax)
-    safe = np.where(s > 0, s, 1.0)
-    v = blocks / safe[:, :, None]
-    q = np.where((s > 0)[:, :, None] | nan, f64_to_e4m3_code(v), np.uint8(0)).astype(np.uint8)
 
-    # Which results are not unique for an FP32 evaluation of the same definition:
-    # a normalised value at a BF16 rounding tie may take the other neighbour.
     y_ex = fa.norm.y_exact.reshape(rows, nb, BLOCK)
     bf_tie = bf16_near_tie(y_ex)
-    other = np.where(bf_tie, 2.0 * y_ex - blocks, blocks)  # the other neighbour (mirror)
-    other = bf16_round(other)
-    abs_hi = np.maximum(mags, np.where(nan, 0.0, np.abs(other)))
-    # The block's amax may change if a tied element could reach or exceed it.
-    touches = bf_tie & (abs_hi >= amax[:, :, None])
-    block_flag = np.any(touches, axis=2)
-    amax_alt = np.where(block_flag, np.max(np.where(bf_tie, abs_hi, mags), axis=2), amax)
-    # Lower alternative: the tied amax element rounding down.
-    amax_lo = np.max(np.where(bf_tie, np.minimum(mags, np.where(nan, 0.0, np.abs(other))),
-                              mags), axis=2)
-    scale_alt = np.where(amax_alt != amax, block_scale_of(amax_alt), block_scale_of(amax_lo))
-    fp8_tie = e4m3_near_tie(v) & (s > 0)[:, :, None]
-    elem_tie = (fp8_tie | bf_tie).reshape(rows, hidden)
-    return BlockQuant(fa.h_new, n, fa.norm.y_exact, fa.norm.rstd, s,
-                      q.reshape(rows, hidden), elem_tie, block_flag, scale_alt)
+    other = bf16_round(np.where(bf_tie, 2.0 * y_ex - blocks, blocks))  # mirror: the other
+    lo = np.where(bf_tie, np.minimum(mags, np.abs(other)), mags)       # neighbour
+    hi = np.where(bf_tie, np.maximum(mags, np.abs(other)), mags)
+    m_lo = np.max(lo, axis=2)                            # every tied element rounded down
+    m_hi = np.max(hi, axis=2)                            # ... or up
+    block_flag = m_hi != m_lo
+    scale_alt = np.where(block_flag, block_scale_of(np.where(amax == m_lo, m_hi, m_lo)), s)
+
+    shape = (rows, hidden)
+    q, fp8_tie = _block_codes(blocks, s, nan)
+    q_nb, nb_tie = _block_codes(other, s, nan)
+    q_alt, fp8_tie_alt = _block_codes(blocks, scale_alt, nan)
+    q_nb_alt, nb_tie_alt = _block_codes(other, scale_alt, nan)
+    r = lambda a: a.reshape(shape)
+    return BlockQuant(fa.h_new, n, fa.norm.y_exact, fa.norm.rstd, s, r(q), r(fp8_tie),
+                      r(bf_tie), r(q_nb), r(nb_tie), block_flag, scale_alt, r(q_alt),
+                      r(fp8_tie_alt), r(q_nb_alt), r(nb_tie_alt))
 
 
 def dequantize_blocks(q, scale) -> np.ndarray:
@@ -324,6 +349,8 @@ class TrainBackward:
     dx: np.ndarray
     dw_exact: np.ndarray
     dw: np.ndarray
+    dx_mag_direct: np.ndarray   # |r*g*w_eff| + |g_residual|: magnitude of dx's direct terms
+    dx_mag_coupled: np.ndarray  # |x|*r^3*mean_j|g*w_eff*x|: bound of the coupled term
 
 
 def train_backward(g, x, w, rstd, bias: float = 0.0, g_residual=None) -> TrainBackward:
@@ -345,7 +372,11 @@ def train_backward(g, x, w, rstd, bias: float = 0.0, g_residual=None) -> TrainBa
     gw = g * w_eff[None, :]
     c = np.sum(gw * x, axis=1) / hidden
     dx_exact = r[:, None] * gw - x * (r ** 3 * c)[:, None]
+    direct = np.abs(r[:, None] * gw)
     if g_residual is not None:
         dx_exact = dx_exact + _2d(g_residual)
+        direct = direct + np.abs(_2d(g_residual))
+    coupled = np.abs(x) * (r ** 3 * np.sum(np.abs(gw * x), axis=1) / hidden)[:, None]
     dw_exact = np.sum(g * x * r[:, None], axis=0)
-    return TrainBackward(dx_exact, bf16_round(dx_exact), dw_exact, f32_round(dw_exact))
+    return TrainBackward(dx_exact, bf16_round(dx_exact), dw_exact, f32_round(dw_exact), direct,
+                         coupled)

@@ -31,8 +31,13 @@ def test_step_bytes_are_each_tensor_once():
 
 
 def test_family_tables_cover_every_family():
-    assert set(bench.FAMILY_BYTES) == {"rmsnorm", "layernorm", "qk_rope", "silu",
+    assert set(bench.FAMILY_BYTES) == {"rmsnorm", "configs", "layernorm", "qk_rope", "silu",
                                        "fixed_width"}
+    cf = bench.configs_alg_bytes()
+    assert cf["block_quant_16384x7168"] == 825_767_936            # 7 B/elem + scales + w
+    assert cf["block_quant_normed_out_16384x7168"] == 825_767_936 + 2 * 16384 * 7168
+    assert cf["ada_gated_fp8_2520x3072"] == 17 * 2520 * 3072 + 2 * 3072 + 4
+    assert cf["ada_gated_fp8_broadcast_2520x3072"] == 11 * 2520 * 3072 + 8 * 3072 + 4
     qk = bench.qk_alg_bytes()
     e = 12288 * 72 * 128
     assert qk["qk_rope_neox_bf16"] == 4 * e + 2 * 48 * 128
@@ -120,3 +125,24 @@ def test_traffic_is_withheld_once_the_sources_change(tmp_path, monkeypatch):
     path.write_text(json.dumps({"source_sha256": bench.kernel_source_sha256(),
                                 "kernels": {"k": {"traffic_bytes": 5}}}))
     assert bench.measured_traffic("k") == 5
+
+
+def test_kernel_resources_of_the_hot_path():
+    """Registers and scratch of the library's kernels, read from the gfx950 code objects: the
+    kernels of the benchmark step and of the other hot-path configurations keep their rows
+    in registers without spilling to scratch memory, and every kernel declares wave64."""
+    res = {r["name"]: r for r in bench.kernel_resources()}
+    assert len(res) > 100
+    hot = ["dn::fwd_kernel<1, 0, 128, 4, 1, 256>",      # fused_add_rmsnorm [8192,4096]
+           "dn::fwd_kernel<1, 0, 256, 4, 1, 256>",      # train_forward [16384,8192]
+           "dn::fwd_kernel<1, 1, 128, 4, 1, 256>",      # fused add + static FP8 [8192,4096]
+           "dn::fwd_kernel<1, 1, 16, 1, 4, 256>",       # ... per head [8192,32,128]
+           "dn::fwd_kernel<1, 2, 256, 4, 1, 256>",      # block FP8 [16384,7168]
+           "dn::fwd_kernel<2, 4, 128, 3, 1, 256>",      # gated Ada + FP8 [2520,3072]
+           "dn::fwd_kernel<0, 0, 128, 4, 1, 256>",      # rmsnorm [32,4096]
+           "dn::bwd_partials_kernel<256, 4, 1, 512, false>",   # backward [16384,8192]
+           "dn::bwd_reduce_kernel<512>"]
+    for k in hot:
+        r = res[k]
+        assert r["scratch"] == 0 and r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, r
+        assert r["agpr"] == 0, r

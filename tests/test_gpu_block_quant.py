@@ -9,7 +9,8 @@ import workloads as W
 from oracle import formats as F
 from oracle import rmsnorm as O
 from tests.conftest import bits16, bits8, values
-from tests.parity import assert_bf16, assert_bits_equal, assert_fp8, rows_of, sample_rows
+from tests.parity import (assert_bf16, assert_bits_equal, assert_block_quant, rows_of,
+                          sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,17 +28,7 @@ def dev(t):
 
 def check_block(gpu_q, gpu_scale_t, gpu_normed, ref: O.BlockQuant, what: str):
     """gpu_scale_t: logical [rows, hidden/128] scales."""
-    s = gpu_scale_t.detach().cpu().double().numpy()
-    flag = ref.block_flag
-    exact = s == ref.scale
-    alt = s == ref.scale_alt
-    bad = ~exact & ~(flag & alt)
-    assert not bad.any(), f"{what}: {bad.sum()} block scales differ " \
-                          f"(first {np.argwhere(bad)[0]}: {s[tuple(np.argwhere(bad)[0])]!r} vs " \
-                          f"{ref.scale[tuple(np.argwhere(bad)[0])]!r})"
-    rows, hidden = ref.q.shape
-    allow = np.repeat(flag, 128, axis=1)
-    assert_fp8(gpu_q, ref.q, ref.elem_tie, what + " codes", allow=allow)
+    assert_block_quant(gpu_q, gpu_scale_t, ref, what)
     if gpu_normed is not None:
         assert_bf16(gpu_normed, ref.normed_exact, what + " normed_out")
 

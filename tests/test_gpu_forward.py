@@ -213,6 +213,27 @@ def test_fused_add_rmsnorm_in_place(dn):
     assert_rstd(rstd, ref.norm.r64)
 
 
+@pytest.mark.parametrize("gemma", [False, True])
+def test_fused_add_rmsnorm_8192x4096_in_place(dn, gemma):
+    """The plain in-place fused add at its benchmark shape, every row against the oracle:
+    there each block walks several grid-stride steps and rows that span two waves meet in
+    alternating reduction slots, which launches of a few hundred rows never reach.  With
+    gemma the BF16 weight takes the +1 offset (w_bias = 1)."""
+    wl = W.fused_add_quant()
+    x, r = wl.tensors["x"], wl.tensors["residual"]
+    w = W.normal((4096,), 2, 7, std=0.1) if gemma else wl.tensors["w"]
+    bias = 1.0 if gemma else 0.0
+    xd, rd = dev(x), dev(r)
+    rstd = torch.empty(8192, dtype=torch.float32, device="cuda")
+    dn.dn_fused_add_rmsnorm(xd, rd, dev(w), 1e-6, w_bias=bias, rstd=rstd)
+    torch.cuda.synchronize()
+    ref = O.fused_add_rmsnorm(values(x), values(r), values(w), bias, 1e-6)
+    what = "gemma " if gemma else ""
+    assert_bits_equal(rd, ref.h_new, f"{what}h_new [8192,4096]")
+    assert_bf16(xd, ref.norm.y_exact, f"{what}y (in input) [8192,4096]")
+    assert_rstd(rstd, ref.norm.r64, f"{what}rstd [8192,4096]")
+
+
 def test_fused_add_equals_add_then_norm(dn):
     x = W.normal((77, 2048), 23, 0)
     r = W.normal((77, 2048), 23, 1)

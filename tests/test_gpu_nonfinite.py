@@ -15,7 +15,7 @@ from oracle import layernorm as L
 from oracle import rmsnorm as O
 from oracle import silu as S
 from tests.conftest import bits8, values
-from tests.parity import assert_bf16
+from tests.parity import assert_bf16, block_quant_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -184,13 +184,11 @@ def test_block_quant_with_infinities_and_nans(dn):
     assert (np.isnan(h) == np.isnan(ref.h_new)).all()
     assert (h[~np.isnan(h)] == ref.h_new[~np.isnan(ref.h_new)]).all(), "h_new"
     s = bs.t()[:9].cpu().double().numpy()
-    ok = (s == ref.scale) | (ref.block_flag & (s == ref.scale_alt))
-    assert ok.all(), f"block scales: {s[~ok]} vs {ref.scale[~ok]}"
     g = bits8(q).reshape(ref.q.shape)
+    scale_ok, codes_ok = block_quant_ok(s, g, ref)
+    assert scale_ok.all(), f"block scales: {s[~scale_ok]} vs {ref.scale[~scale_ok]}"
     nan_ref = np.isnan(ref.normed)
     assert nan_ref[:, 9].all() and (ref.scale > 0).any()
     assert (((g & 0x7F) == 0x7F) == nan_ref).all(), "e4m3 NaN codes"
-    allow = np.repeat(ref.block_flag, 128, axis=1)
-    codes_ok = F.codes_equal_e4m3(g, ref.q) | ref.elem_tie | allow
     assert codes_ok[~nan_ref].all(), "e4m3 codes"
     assert_bf16_nonfinite(normed, ref.normed_exact, "normed_out")

@@ -11,6 +11,7 @@ import torch
 
 from oracle import formats as F
 from oracle import rmsnorm as O
+from tests.parity import block_quant_ok
 
 RNG = np.random.default_rng(7)
 
@@ -218,6 +219,204 @@ def test_block_quant_nan_elements():
     assert ((got.q[:, 9] & 0x7F) == 0x7F).all()
 
 
+# The gate of the block quantiser where results are not unique.  Rows of ones with eps = 0
+# have rstd exactly 1, so the normalised value is exactly the FP32 weight; weights that
+# sit on BF16 midpoints (1 + odd * 2^-8) make elements whose BF16 rounding an FP32 kernel
+# may take either way.  Every choice of those roundings is enumerated and its result is
+# computed from the definition with exact rationals (block maximum, FP32 scale by nearest
+# search, e4m3 codes by nearest search over the decoded code table), independently of the
+# oracle; the gate must admit each of them and nothing further than one code step.
+
+def _e4m3_table():
+    """(code, exact value) of every finite e4m3fn code, from the format definition."""
+    from fractions import Fraction
+    out = []
+    for c in range(256):
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 0xF and m == 7:
+            continue                                  # NaN
+        mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else \
+            (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        out.append((c, -mag if c & 0x80 else mag))
+    return out
+
+
+E4M3_TABLE = _e4m3_table()
+
+
+def _e4m3_codes_exact(v):
+    """Nearest e4m3fn code of an exact rational (ties to the even code, saturating at 448),
+    and the codes an evaluation within 2^-21 relative of v may produce."""
+    from fractions import Fraction
+    v = max(min(v, Fraction(448)), Fraction(-448))
+    dist = sorted((abs(val - v), c & 1, c) for c, val in E4M3_TABLE
+                  if (val >= 0) == (v >= 0) or val == 0)
+    best = dist[0][2]
+    reach = {best}
+    for lo, hi in ((v * (1 - Fraction(1, 2 ** 21)), v * (1 + Fraction(1, 2 ** 21))),):
+        for w in (lo, hi):
+            w = max(min(w, Fraction(448)), Fraction(-448))
+            reach.add(sorted((abs(val - w), c & 1, c) for c, val in E4M3_TABLE
+                             if (val >= 0) == (w >= 0) or val == 0)[0][2])
+    return best, reach
+
+
+def _f32_nearest(q):
+    """FP32 nearest-even rounding of an exact rational, by search around float()."""
+    from fractions import Fraction
+    f = np.float32(float(q))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - q),
+                                     int(np.array(c).view(np.uint32)) & 1))
+
+
+def _enumerate_block(w_block):
+    """Every (scale, codes, reachable codes) an evaluation may produce for one block of
+    normalised values w_block (exact FP32 numbers), over all roundings of its BF16 ties."""
+    from fractions import Fraction
+    import itertools
+    exact = [Fraction(float(v)) for v in w_block]
+    nominal = F.bf16_round(np.asarray(w_block, dtype=np.float64))
+    tied = [j for j, v in enumerate(exact) if Fraction(float(nominal[j])) != v]
+    results = []
+    for choice in itertools.product((0, 1), repeat=len(tied)):
+        n = [Fraction(float(v)) for v in nominal]
+        for j, up in zip(tied, choice):
+            lo = Fraction(float(F.bf16_round(np.float64(float(exact[j]) * (1 - 2 ** -12)))))
+            hi = Fraction(float(F.bf16_round(np.float64(float(exact[j]) * (1 + 2 ** -12)))))
+            n[j] = hi if up else lo
+        amax = max(abs(v) for v in n)
+        s = _f32_nearest(amax / 448)
+        codes, reach = [], []
+        for v in n:
+            best, r = _e4m3_codes_exact(v / Fraction(float(s))) if s > 0 else (0, {0})
+            codes.append(best)
+            reach.append(r)
+        results.append((float(s), np.array(codes, dtype=np.uint8), reach))
+    return results
+
+
+def _tie_rows():
+    """Rows of FP32 weights (the normalised values at x = 1, eps = 0) built on BF16
+    midpoints; two blocks of 128 per row."""
+    base = np.array([0.5 * (1 + (j % 96) * 2.0 ** -7) for j in range(256)])  # exact BF16
+    rows = []
+    def row(**at):
+        r = base.copy()
+        for j, v in at.items():
+            r[int(j[1:])] = v
+        return r
+    m = lambda k: 1.0 + k * 2.0 ** -8            # k odd: a BF16 midpoint
+    rows.append(row(c0=m(1), c1=1.0))            # amax 1 (nominal) or 1 + 2^-7
+    rows.append(row(c0=m(3), c1=1.0))            # nominal up to 1 + 2^-6, or 1 + 2^-7
+    rows.append(row(c0=m(3), c1=m(5)))           # two ties moving in opposite directions
+    # a tie whose upper value equals the untied amax cannot move it: not flagged
+    rows.append(row(c0=m(1), c1=1.0 + 2.0 ** -7, c130=-m(1), c131=-(1.0 + 2.0 ** -7)))
+    rows.append(row(c0=-m(3), c1=m(5), c2=-m(5), c129=m(7), c130=-m(9)))
+    # ties below an untied amax (block 0); a tie just below 1 above the rest (block 1)
+    rows.append(row(c0=2.0, c5=m(1), c7=-m(3), c200=m(255) / 2))
+    return np.array(rows)
+
+
+TIE_ROW_FLAGS = [[1, 0], [1, 0], [1, 0], [0, 0], [1, 1], [0, 1]]
+
+
+def _tie_refs():
+    """The oracle's block-quant results of each tie row (x = 1, residual 0, eps = 0, the
+    row's FP32 weights), one row per call (the weight is shared by a call's rows)."""
+    w = _tie_rows()
+    refs = []
+    for t in range(w.shape[0]):
+        x = np.ones((1, w.shape[1]))
+        refs.append(O.fused_add_rmsnorm_fp8_block_quant(x, np.zeros_like(x), w[t], 0.0, 0.0))
+        assert (refs[-1].normed_exact[0] == w[t]).all(), "rstd must be exactly 1 here"
+    return w, refs
+
+
+def test_block_quant_tie_gate_admits_every_reachable_result():
+    w, refs = _tie_refs()
+    rows, hidden = w.shape
+    flagged = 0
+    for t in range(rows):
+        ref = refs[t]
+        per_block = [_enumerate_block(w[t, b * 128:(b + 1) * 128]) for b in range(2)]
+        scales_seen = [sorted({r[0] for r in res}) for res in per_block]
+        for b in range(2):
+            # The oracle flags exactly the blocks with two reachable scales and names both.
+            want = {float(ref.scale[0, b]), float(ref.scale_alt[0, b])}
+            assert set(scales_seen[b]) == want, (t, b, scales_seen[b], want)
+            assert bool(ref.block_flag[0, b]) == (len(scales_seen[b]) == 2), (t, b)
+            flagged += int(ref.block_flag[0, b])
+        import itertools
+        for r0, r1 in itertools.product(*per_block):
+            s = np.array([[r0[0], r1[0]]])
+            q = np.concatenate([r0[1], r1[1]])[None, :]
+            sub = ref
+            scale_ok, codes_ok = block_quant_ok(s, q, sub)
+            assert scale_ok.all() and codes_ok.all(), (t, s)
+            # every code an evaluation may reach, one element at a time
+            for j, reach in enumerate(r0[2] + r1[2]):
+                for c in reach:
+                    q2 = q.copy()
+                    q2[0, j] = c
+                    assert block_quant_ok(s, q2, sub)[1][0, j], (t, j, c)
+    assert flagged == sum(map(sum, TIE_ROW_FLAGS))
+    assert [[int(f) for f in r.block_flag[0]] for r in refs] == TIE_ROW_FLAGS
+
+
+def test_block_quant_tie_gate_rejects_the_rest():
+    w, refs = _tie_refs()
+    rows, hidden = w.shape
+    # Two code steps anywhere, or one step where no reachable result has it, fail.
+    for t in range(rows):
+        ref = sub = refs[t]
+        nominal = ref.scale
+        reach = [set() for _ in range(hidden)]
+        for b in range(2):
+            for s_b, codes, rc in _enumerate_block(w[t, b * 128:(b + 1) * 128]):
+                if s_b != nominal[0, b]:
+                    continue                  # codes under the other scale: checked above
+                for j in range(128):
+                    reach[b * 128 + j] |= rc[j]
+        for j in range(0, hidden, 5):
+            ordinal = lambda c: -(c & 0x7F) if c & 0x80 else (c & 0x7F)
+            code = int(ref.q[0, j])
+            for step in (-2, -1, 1, 2):
+                o = ordinal(code) + step
+                if abs(o) > 0x7E:
+                    continue
+                c2 = (0x80 | -o) if o < 0 else o
+                reached = c2 in reach[j]
+                # the gate's e4m3 band (2^-16) is wider than what an evaluation reaches
+                band = ref.fp8_tie[0, j] or (ref.bf_tie[0, j] and ref.nb_tie[0, j])
+                q2 = ref.q.copy()
+                q2[0, j] = c2
+                ok = block_quant_ok(nominal, q2, sub)[1][0, j]
+                if abs(step) == 2:
+                    assert not ok, (t, j, step)
+                elif not reached and not band:
+                    assert not ok, (t, j, step)
+                if reached:
+                    assert ok, (t, j, step)
+        # A scale that no rounding reaches fails, flagged block or not.
+        for b in range(2):
+            bad = nominal.copy()
+            bad[0, b] = float(np.nextafter(np.float32(nominal[0, b]), np.float32(1e30)))
+            if bad[0, b] != ref.scale_alt[0, b]:
+                assert not block_quant_ok(bad, ref.q, sub)[0][0, b], (t, b)
+    # Codes must follow the scale the block took: nominal codes under the other scale fail
+    # where an untied element's code differs between the two.
+    ref, b = refs[0], 0
+    assert ref.block_flag[0, b]
+    diff = (ref.q_alt[0, :128] != ref.q[0, :128]) & ~ref.fp8_tie_alt[0, :128] & \
+        ~ref.fp8_tie[0, :128] & ~ref.bf_tie[0, :128]
+    assert diff.any(), "the case needs an element whose code follows the scale"
+    s = ref.scale.copy()
+    s[0, b] = ref.scale_alt[0, b]
+    assert block_quant_ok(s, ref.q_alt, ref)[1].all()
+    assert not block_quant_ok(s, ref.q, ref)[1].all()
+
+
 # ----------------------------------------------------------------------------- AdaRMSNorm
 
 def test_ada_matches_torch_float64():
@@ -359,3 +558,39 @@ def test_train_forward_residual_route_is_fused_add():
     ref = torch_rms_norm64(F.bf16_round(h + u), F.f32_round(1.0 + w), 1e-6)
     np.testing.assert_allclose(t.y_exact, ref, rtol=1e-13)
     assert (t.h_new == F.bf16_round(h + u)).all()
+
+
+def _dx_fp32_model(g, x, w_eff, r, coef_error: float = 0.0):
+    """dx as an FP32 kernel evaluates it (lane partials of g*w*x over 32 terms, the row sum
+    in FP64, coef = FP32(r^3*c), dx = FMA(-x, coef, (g*w)*r)), rounded to BF16; coef_error
+    perturbs the coupled coefficient."""
+    f32 = np.float32
+    H = x.shape[1]
+    gw = (g.astype(f32) * w_eff.astype(f32)).astype(f32)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        lanes = [f32(0)] * (H // 32)
+        for k in range(32):
+            for ln in range(H // 32):
+                j = ln + k * (H // 32)
+                lanes[ln] = f32(float(gw[t, j]) * float(x[t, j]) + float(lanes[ln]))
+        c = sum(float(v) for v in lanes) / H
+        coef = f32(float(r[t]) ** 3 * c * (1.0 + coef_error))
+        first = f32(gw[t] * f32(r[t]))
+        out[t] = (-x[t] * float(coef) + first.astype(np.float64)).astype(f32)
+    return F.bf16_round(out)
+
+
+def test_dx_gate_admits_fp32_evaluation_and_rejects_a_wrong_coefficient():
+    """The per-element dx gate of the GPU tests: an FP32 evaluation of the formula passes;
+    the same evaluation with the coupled term's coefficient off by 0.1 % does not."""
+    from tests.parity import assert_dx
+    g = bf16_values((6, 1024))
+    x = bf16_values((6, 1024))
+    w = bf16_values((1024,), mean=1.0, std=0.1)
+    r = F.f32_round(1.0 / np.sqrt(np.mean(x * x, axis=1) + 1e-6))
+    ref = O.train_backward(g, x, w, r, 0.0)
+    to_t = lambda v: torch.from_numpy(F.f64_to_bf16_bits(v).view(np.int16)).view(torch.bfloat16)
+    assert_dx(to_t(_dx_fp32_model(g, x, w, r)), ref, "fp32 model")
+    with pytest.raises(AssertionError, match="per-element"):
+        assert_dx(to_t(_dx_fp32_model(g, x, w, r, 1e-3)), ref, "perturbed model")
