@@ -1,23 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of the RMSNorm family's hot path on one MI355X, as achieved HBM GB/s.
 
-One step is one pass of the hot path over one batch of synthetic input:
+The metric is the pair the target names: the fused_add_rmsnorm forward and the training
+backward.  One timed round is
   1. fused_add_rmsnorm forward, in place, x/residual BF16 [8192, 4096]      (plain BF16 y)
-  2. training RMSNorm forward with residual, BF16 [16384, 8192], FP32 w = 1 + w0
-  3. fused_add_rmsnorm + static FP8 forward, BF16 [8192, 4096] -> e4m3fn    (scale 0.04)
-  4. training backward on (2)'s h_new and rstd: dx BF16 and deterministic FP32 dw
-     (stage 1: dx + per-chunk FP64 column sums; stage 2: fixed-order dw reduction)
-The order interleaves the two shapes so that each kernel's inputs have been pushed out of
-the 256 MB Infinity Cache by the previous kernel's traffic.
+  2. training backward, BF16 [16384, 8192]: dx and the deterministic FP32 dw, in one
+     launch, on the h_new and rstd of a training forward with residual (FP32 w = 1 + w0)
+     run once before anything is timed
+and `value` = algorithmic bytes of a round / wall time of a round (K rounds between device
+synchronisations; inputs resident in HBM).  The two shapes alternate, so each kernel's
+inputs have been pushed out of the 256 MB Infinity Cache by the other's traffic.
 
-`value` = algorithmic bytes of a step / wall time of a step (K steps between device
-synchronisations).  Algorithmic bytes count each tensor the definition reads or writes
-once; the backward's FP64 workspace traffic is not counted.  Inside the timed region only
-the dominant kernel (the training forward, the roofline's kernel) is bracketed by HIP events
-(created without the system-scope fence, see HipTimingEvent) on the kernels' stream; the
-per-kernel table comes from K more steps with an event between every two kernels (each
-record still costs the stream about a microsecond, which the table's durations include).  `cpu_baseline` times the FP64 numpy oracle on a bounded sample
-of the same workload on this host.
+`whole_step` times the whole hot-path step the same way: the pair plus the training
+forward with residual [16384, 8192] and the fused add + static FP8 forward [8192, 4096]
+(scale 0.04), in the order fused add, training forward, fused add + FP8, backward.
+
+Algorithmic bytes count each tensor the definition reads or writes once; the backward's
+FP64 chunk rows in the workspace are not counted.  Inside the timed region only the
+dominant kernel (the backward, the roofline's kernel) is bracketed by HIP events (created
+without the system-scope fence, see HipTimingEvent) on the kernels' stream; the per-kernel
+tables come from K more rounds with an event between every two kernels (each record still
+costs the stream about a microsecond, which the tables' durations include).
+`cpu_baseline` times the FP64 numpy oracle on a bounded sample of the same workload on
+this host's cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 
@@ -64,10 +69,9 @@ def alg_bytes():
         "fused_add_rmsnorm_quant": 7 * e2 + 2 * h2 + 4,
         # read h, residual; write y, h_new; FP32 rstd out; FP32 weight
         "train_forward": 8 * e4 + 4 * t4 + 4 * h4,
-        # stage 1: read g, x (h_new), rstd, FP32 weight; write dx
-        "train_backward_partials": 6 * e4 + 4 * t4 + 4 * h4,
-        # stage 2: write dw (its workspace reads are not algorithmic)
-        "train_backward_reduce": 4 * h4,
+        # read g, x (h_new), rstd, FP32 weight; write dx and FP32 dw (the FP64 chunk rows it
+        # passes through the workspace are not algorithmic)
+        "train_backward": 6 * e4 + 4 * t4 + 4 * h4 + 4 * h4,
     }
 
 
@@ -101,7 +105,11 @@ def measured_traffic(kernel: str, family: str = "rmsnorm"):
         return None
     if d.get("source_sha256") != kernel_source_sha256():
         return None
-    k = d.get("kernels", {}).get(kernel)
+    ks = d.get("kernels", {})
+    if kernel not in ks and kernel == "train_backward":
+        parts = [ks.get(n) for n in ("train_backward_partials", "train_backward_reduce")]
+        return None if None in parts else sum(k["traffic_bytes"] for k in parts)
+    k = ks.get(kernel)
     return None if k is None else k["traffic_bytes"]
 
 
@@ -186,7 +194,25 @@ def timing_event(torch):
 
 
 STEP_KERNELS = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
-                "train_backward_partials", "train_backward_reduce"]
+                "train_backward"]
+# The library dispatches of a step: the backward is two launches (dx and the FP64 chunk
+# rows, then the fixed-order dw reduction).
+STEP_DISPATCHES = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
+                   "train_backward_partials", "train_backward_reduce"]
+
+
+def step_dispatch_bytes():
+    """Algorithmic bytes per library dispatch of a step (the backward split into its two
+    launches: the reduction's algorithmic bytes are dw's; the chunk rows it reads are
+    workspace traffic)."""
+    ab = alg_bytes()
+    dw = 4 * C4[1]
+    out = {n: ab[n] for n in STEP_DISPATCHES[:3]}
+    out["train_backward_partials"] = ab["train_backward"] - dw
+    out["train_backward_reduce"] = dw
+    return out
+# The metric's pair: the fused add forward and the training backward.
+PAIR_KERNELS = ["fused_add_rmsnorm", "train_backward"]
 GIB_KIB = float(1 << 20)
 
 
@@ -236,8 +262,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, family: str = "rmsnorm",
     goes to `out_path` (default: the family's file under profiles/, traffic_path), which
     bench.py reads for `traffic`."""
     fr, wr = _read_csv(fetch_csv), _read_csv(write_csv)
-    ab = FAMILY_BYTES[family]()
-    names = STEP_KERNELS if family == "rmsnorm" else list(ab)   # dispatch order
+    ab = step_dispatch_bytes() if family == "rmsnorm" else FAMILY_BYTES[family]()
+    names = list(ab)   # dispatch order
     fetch, sym, fscale, nf = _counter(fr, "FETCH_SIZE", names)
     write, wsym, wscale, nw = _counter(wr, "WRITE_SIZE", names)
     if wsym != sym:
@@ -1153,26 +1179,48 @@ def main(argv=None) -> int:
     scale = torch.tensor([0.04], dtype=torch.float32, device=dev)
     ws = dn.train_backward_workspace(H4, dev)
 
-    names = ["fused_add_rmsnorm", "train_forward", "fused_add_rmsnorm_quant",
-             "train_backward_partials", "train_backward_reduce"]
+    calls = {
+        "fused_add_rmsnorm": lambda: dn.dn_fused_add_rmsnorm(x2, r2, w2, 1e-6),
+        "train_forward": lambda: dn.dn_train_forward(h4, w4, 1e-6, w_bias=1.0, residual=u4,
+                                                     out=y4, rstd=rs4, residual_out=hn4),
+        "fused_add_rmsnorm_quant": lambda: dn.dn_fused_add_rmsnorm_quant(x2q, r2q, w2, scale,
+                                                                         1e-6, out=q2),
+        "train_backward": lambda: dn.dn_train_backward(g4, hn4, w4, rs4, w_bias=1.0,
+                                                       workspace=ws, dx=dx4, dw=dw4),
+    }
 
-    def step(events=None, only=None):
-        def mark(i):
-            if events is not None and (only is None or i in only):
-                events[i].record()
-        mark(0)
-        dn.dn_fused_add_rmsnorm(x2, r2, w2, 1e-6)
-        mark(1)
-        dn.dn_train_forward(h4, w4, 1e-6, w_bias=1.0, residual=u4, out=y4, rstd=rs4,
-                            residual_out=hn4)
-        mark(2)
-        dn.dn_fused_add_rmsnorm_quant(x2q, r2q, w2, scale, 1e-6, out=q2)
-        mark(3)
-        dn.dn_train_backward_partials(g4, hn4, w4, rs4, ws, w_bias=1.0, dx=dx4)
-        mark(4)
-        dn.dn_train_backward_reduce(ws, T4, H4, dw=dw4)
-        mark(5)
+    def run(names, events=None, only=None):
+        """One round of `names`; events[j] is recorded before names[j] (and events[-1] after
+        the last) when j is in `only` (every j when only is None)."""
+        def mark(j):
+            if events is not None and (only is None or j in only):
+                events[j].record()
+        for j, n in enumerate(names):
+            mark(j)
+            calls[n]()
+        mark(len(names))
 
+    def rounds(names, k, events_per_round=False, only=None):
+        evs = [[timing_event(torch) for _ in range(len(names) + 1)] for _ in range(k)] \
+            if events_per_round else [None] * k
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in evs:
+            run(names, e, only)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, evs
+
+    def durations(names, evs):
+        return {n: [e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs] for j, n in enumerate(names)}
+
+    ab = alg_bytes()
+    pair_bytes = sum(ab[n] for n in PAIR_KERNELS)
+    step_bytes = sum(ab[n] for n in STEP_KERNELS)
+    # The backward reads the training forward's h_new and rstd: one forward before anything
+    # is timed (inputs resident in HBM).  Profiler runs leave it out, so that their library
+    # dispatches are whole steps (the first warm-up step's forward precedes its backward).
+    if not a.step_only:
+        calls["train_forward"]()
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -1182,54 +1230,51 @@ def main(argv=None) -> int:
         del src, dst
     print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
-        step()
+        run(STEP_KERNELS)
     torch.cuda.synchronize()
 
-    # Timed region: K steps between synchronisations (wall clock).  Only the dominant kernel
-    # (the training forward) is bracketed by events here: even a fence-free event record
-    # costs the stream about 1 us (measured: 410 us per step with no events, 412 us with two,
-    # 418 us with six).
-    dom = "train_forward"
-    di = names.index(dom)
-    evs = [[timing_event(torch) for _ in range(6)] for _ in range(a.steps)]
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(evs[i], only=(di, di + 1))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dom_live = [e[di].elapsed_time(e[di + 1]) * 1e-3 for e in evs]
-
-    # Per-kernel breakdown: K more steps with an event between every two kernels.
-    evs = [[timing_event(torch) for _ in range(6)] for _ in range(a.steps)]
-    for i in range(a.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    per = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e-3)
-    ab = alg_bytes()
-    step_bytes = sum(ab.values())
+    dom = "train_backward"
+    if not a.step_only:
+        # Timed region: K rounds of the metric's pair between synchronisations (wall clock);
+        # only the dominant kernel (the backward) is bracketed by events, since even a
+        # fence-free event record costs the stream about a microsecond.
+        print(f"[bench] timing {a.steps} rounds of the pair", file=sys.stderr, flush=True)
+        di = PAIR_KERNELS.index(dom)
+        wall, evs = rounds(PAIR_KERNELS, a.steps, True, only=(di, di + 1))
+        dom_live = [e[di].elapsed_time(e[di + 1]) * 1e-3 for e in evs]
+        # The pair's per-kernel breakdown: K more rounds with an event between the kernels.
+        _, evs = rounds(PAIR_KERNELS, a.steps, True)
+        pair_per = durations(PAIR_KERNELS, evs)
+    # The whole hot-path step (all four kernels), K rounds: wall clock, then per kernel.
+    print(f"[bench] timing {a.steps} whole steps", file=sys.stderr, flush=True)
+    step_wall, _ = rounds(STEP_KERNELS, a.steps)
+    _, evs = rounds(STEP_KERNELS, a.steps, True)
+    per = durations(STEP_KERNELS, evs)
+    if a.step_only:
+        # profiler runs time whole steps only: the pair's figures come from their events
+        pair_per = {n: per[n] for n in PAIR_KERNELS}
+        dom_live = per[dom]
+        wall = sum(sum(pair_per[n]) for n in PAIR_KERNELS)
     ms_per_step = wall / a.steps * 1e3
-    value = step_bytes / (wall / a.steps) / 1e9
+    value = pair_bytes / (wall / a.steps) / 1e9
 
     kernels = {}
-    for n in names:
+    for n in STEP_KERNELS:
         st = _stats(per[n])
         gbs = ab[n] / (st["us"] * 1e-6) / 1e9
         kernels[n] = dict(st, bytes=ab[n], **{"GB/s": round(gbs, 1)},
                           frac=round(gbs / HBM_PEAK_GBS, 4))
-    bwd_s = (sum(per["train_backward_partials"]) + sum(per["train_backward_reduce"])) / a.steps
-    bwd_b = ab["train_backward_partials"] + ab["train_backward_reduce"]
-    fa_s = sum(per["fused_add_rmsnorm"]) / a.steps
+    fa_s = sum(pair_per["fused_add_rmsnorm"]) / a.steps
+    bwd_s = sum(pair_per["train_backward"]) / a.steps
     headline = {
         "fused_add_rmsnorm_fwd_GB/s": round(ab["fused_add_rmsnorm"] / fa_s / 1e9, 1),
-        "train_bwd_GB/s": round(bwd_b / bwd_s / 1e9, 1),
-        "fused_add_fwd_plus_train_bwd_GB/s": round((ab["fused_add_rmsnorm"] + bwd_b) /
-                                                  (fa_s + bwd_s) / 1e9, 1),
+        "train_bwd_GB/s": round(ab["train_backward"] / bwd_s / 1e9, 1),
+        "fused_add_fwd_plus_train_bwd_GB/s": round(pair_bytes / (fa_s + bwd_s) / 1e9, 1),
     }
+    whole_step = {"GB/s": round(step_bytes / (step_wall / a.steps) / 1e9, 1),
+                  "ms_per_step": round(step_wall / a.steps * 1e3, 4), "bytes": step_bytes,
+                  "frac": round(step_bytes / (step_wall / a.steps) / 1e9 / HBM_PEAK_GBS, 4),
+                  "kernels": STEP_KERNELS}
     dom_avg = sum(dom_live) / len(dom_live)
     achieved = ab[dom] / dom_avg / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
@@ -1243,7 +1288,7 @@ def main(argv=None) -> int:
         ceiling = {"device_copy_1GiB_GB/s": device_copy_ceiling(torch, dev)}
         ceiling.update(stream_ceilings(torch, dev))
         mix = {"fused_add_rmsnorm": "stream_2r2w_GB/s", "train_forward": "stream_2r2w_GB/s",
-               "train_backward_partials": "stream_2r1w_GB/s"}
+               "train_backward": "stream_2r1w_GB/s"}
         for k, m in mix.items():
             kernels[k]["of_stream_ceiling"] = round(kernels[k]["GB/s"] / ceiling[m], 4)
         shard = shard_measurement(torch, dev, dn, W)
@@ -1261,13 +1306,14 @@ def main(argv=None) -> int:
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "fused_add_rmsnorm fwd BF16 [8192,4096] (plain and static FP8) + "
-                               "training RMSNorm fwd+bwd with residual BF16 [16384,8192], "
-                               "FP32 weight 1+w",
-                   "storage": "bf16 activations, fp32 statistics/weights, e4m3fn outputs",
+        "config": {"workload": "fused_add_rmsnorm fwd BF16 [8192,4096] in place + training "
+                               "RMSNorm bwd BF16 [16384,8192] (dx and deterministic FP32 dw of "
+                               "the residual-route forward, FP32 weight 1+w)",
+                   "storage": "bf16 activations, fp32 statistics/weights/dw",
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-                   "step_bytes": step_bytes, "parallelism": "single GPU"},
+                   "step_bytes": pair_bytes, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "headline": headline,
+        "whole_step": whole_step,
         "ceilings": ceiling, "shard_2048x8192": shard, "isolated_configs": configs,
         "timing_events": _EVENT_KIND["kind"],
     }

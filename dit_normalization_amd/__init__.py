@@ -16,7 +16,8 @@ __all__ = [
     "dn_fused_dit_residual_layernorm_scale_shift", "dn_fused_qk_rmsnorm_rope",
     "dn_fused_rmsnorm_silu", "dn_rmsnorm_sigmoid_gate", "dn_gated_residual_rmsnorm",
     "dn_gated_residual_next_rmsnorm",
-    "dn_force_threads_per_row", "dn_max_hidden", "DnormError", "rmsnorm_train",
+    "dn_force_threads_per_row", "dn_max_hidden", "DnormError",
+    "rmsnorm_train",
     "RMSNormTrainFunction",
 ]
 

@@ -5,7 +5,8 @@ is one dn_train_backward call (norm docs, "Training RMSNorm (Cake)": cake_rmsnor
 CakeRMSNormFunction; norm guide §6.4).  With a residual the forward returns (y, h_new),
 h_new = BF16(x + residual); the gradient reaching h_new directly is passed to the kernel as
 g_residual, and the resulting dx is the gradient of both x and residual (norm guide §6.2).
-dw is accumulated in FP32 by the kernel and returned in w's dtype.
+dw is accumulated in FP32 by the kernel and written in w's dtype (for a BF16 weight, the FP32
+value rounded once more, in the kernel).
 """
 from __future__ import annotations
 
@@ -38,8 +39,8 @@ class RMSNormTrainFunction(torch.autograd.Function):
             gy = torch.zeros_like(x)
         # Gradients are read in place when their rows are addressable (row-strided views
         # included); broadcast or transposed ones are copied once by the binding.
-        dx, dw = dn.dn_train_backward(gy, x, w, rstd, w_bias=ctx.w_bias, g_residual=gh)
-        dw = dw.to(w.dtype)
+        dx, dw = dn.dn_train_backward(gy, x, w, rstd, w_bias=ctx.w_bias, g_residual=gh,
+                                      dw_dtype=w.dtype)
         if ctx.residual:
             return dx, dw, None, None, dx
         return dx, dw, None, None, None

@@ -266,6 +266,7 @@ int pick_bwd_tier(int nvec) {
   return -1;
 }
 
+// Workspace: kMaxChunks rows of FP64 column sums.
 size_t workspace_bytes(int64_t hidden) {
   if (hidden <= 0 || hidden > kMaxHidden) return 0;
   return (size_t)kMaxChunks * (size_t)hidden * sizeof(double);
@@ -509,22 +510,31 @@ dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd, void* h_new,
 
 size_t dn_train_backward_workspace_bytes(int64_t hidden) { return workspace_bytes(hidden); }
 
-dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
-                                     int64_t g_stride, const void* x, int64_t x_stride,
-                                     const void* w, int w_dtype, float w_bias,
-                                     const float* rstd, const void* g_residual,
-                                     int64_t g_residual_stride, void* workspace,
-                                     size_t workspace_bytes_, int64_t rows, int64_t hidden,
-                                     dn_stream_t stream) {
-  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
-  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+namespace {
+
+dn_status check_dw(const void* dw, int dw_dtype) {
+  if (dw_dtype != DN_WEIGHT_BF16 && dw_dtype != DN_WEIGHT_F32)
+    return fail(DN_ERR_DTYPE, "dw_dtype must be DN_WEIGHT_BF16 (0) or DN_WEIGHT_F32 (1), got %d",
+                dw_dtype);
+  if (!dw) return fail(DN_ERR_NULL, "dw must not be NULL");
+  if (!aligned(dw, dw_dtype == DN_WEIGHT_F32 ? 4 : 2))
+    return fail(DN_ERR_ALIGN, "dw must be %d-byte aligned", dw_dtype == DN_WEIGHT_F32 ? 4 : 2);
+  return DN_OK;
+}
+
+// Checks of the backward's row arguments and the BwdParams of a producer launch over
+// `part` (chunk rows) and `ctr` (counters, one-launch form).  *tier_out receives the row
+// tier.  rows == 0 is handled by the caller.
+dn_status bwd_prepare(BwdParams* out, int* tier_out, void* dx, int64_t dx_stride, const void* g,
+                      int64_t g_stride, const void* x, int64_t x_stride, const void* w,
+                      int w_dtype, float w_bias, const float* rstd, const void* g_residual,
+                      int64_t g_residual_stride, int64_t rows, int64_t hidden) {
   DN_CHECK(check_matrix(dx, dx_stride, hidden, 2, "dx"));
   DN_CHECK(check_matrix(g, g_stride, hidden, 2, "g"));
   DN_CHECK(check_matrix(x, x_stride, hidden, 2, "x"));
   if (g_residual) DN_CHECK(check_matrix(g_residual, g_residual_stride, hidden, 2, "g_residual"));
   DN_CHECK(check_weight(w, w_dtype));
   DN_CHECK(check_f32(rstd, "rstd", true));
-  DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
   BwdParams p{};
   p.dx = static_cast<uint16_t*>(dx); p.sdx = dx_stride;
   p.g = static_cast<const uint16_t*>(g); p.sg = g_stride;
@@ -532,7 +542,6 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
   p.gres = static_cast<const uint16_t*>(g_residual); p.sgr = g_residual_stride;
   p.w = w; p.w_f32 = w_dtype == DN_WEIGHT_F32; p.w_bias = w_bias;
   p.rstd = rstd;
-  p.part = static_cast<double*>(workspace);
   p.rows = rows;
   p.hidden = (int)hidden;
   p.nvec = (int)(hidden / 8);
@@ -548,38 +557,76 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
       return fail(DN_ERR_SHAPE, "row strides up to %lld elements are supported at hidden %lld",
                   (long long)(((int64_t)1 << 30) / (64 * p.chunks) - 1), (long long)hidden);
   }
+  *out = p;
+  *tier_out = tier;
+  return DN_OK;
+}
+
+// Launch the producers of `p` (dx and the chunk rows in p.part); with `dw`, also the
+// reduction of the chunk rows into dw on the same stream.
+dn_status bwd_launch(const BwdParams& p, int tier, void* dw, int dw_dtype,
+                     hipStream_t stream) {
   const TierShape s = bwd_tier_shape(tier);
   const int gcount = s.nt / s.tpr;
   const int wpr = s.tpr > 64 ? s.tpr / 64 : 1;
   const size_t lds = bwd_lds_bytes(gcount, wpr, s.r, s.nt, s.vmax);
-  const hipError_t e = bwd_partials_launch(p, tier, lds, static_cast<hipStream_t>(stream), nullptr);
+  hipError_t e = bwd_partials_launch(p, tier, lds, stream, nullptr);
+  if (e == hipSuccess && dw)
+    e = bwd_reduce_launch(dw, dw_dtype == DN_WEIGHT_BF16, p.part, p.hidden, p.chunks, stream);
   if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return DN_OK;
 }
 
-dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes_,
-                                   int64_t rows, int64_t hidden, dn_stream_t stream) {
+}  // namespace
+
+dn_status dn_train_backward_partials(void* dx, int64_t dx_stride, const void* g,
+                                     int64_t g_stride, const void* x, int64_t x_stride,
+                                     const void* w, int w_dtype, float w_bias,
+                                     const float* rstd, const void* g_residual,
+                                     int64_t g_residual_stride, void* workspace,
+                                     size_t workspace_bytes_, int64_t rows, int64_t hidden,
+                                     dn_stream_t stream) {
   DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
   if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
-  DN_CHECK(check_f32(dw, "dw", true));
+  BwdParams p;
+  int tier = 0;
+  DN_CHECK(bwd_prepare(&p, &tier, dx, dx_stride, g, g_stride, x, x_stride, w, w_dtype, w_bias,
+                       rstd, g_residual, g_residual_stride, rows, hidden));
   DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
-  const hipError_t e = bwd_reduce_launch(dw, static_cast<const double*>(workspace), (int)hidden,
+  p.part = static_cast<double*>(workspace);
+  return bwd_launch(p, tier, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+dn_status dn_train_backward_reduce(void* dw, int dw_dtype, const void* workspace,
+                                   size_t workspace_bytes_, int64_t rows, int64_t hidden,
+                                   dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_dw(dw, dw_dtype));
+  DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
+  const hipError_t e = bwd_reduce_launch(dw, dw_dtype == DN_WEIGHT_BF16,
+                                         static_cast<const double*>(workspace), (int)hidden,
                                          chunk_count(rows), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return DN_OK;
 }
 
-dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw, const void* g,
+dn_status dn_train_backward(void* dx, int64_t dx_stride, void* dw, int dw_dtype, const void* g,
                             int64_t g_stride, const void* x, int64_t x_stride, const void* w,
                             int w_dtype, float w_bias, const float* rstd,
                             const void* g_residual, int64_t g_residual_stride,
                             void* workspace, size_t workspace_bytes_, int64_t rows,
                             int64_t hidden, dn_stream_t stream) {
-  DN_CHECK(check_f32(dw, "dw", true));
-  DN_CHECK(dn_train_backward_partials(dx, dx_stride, g, g_stride, x, x_stride, w, w_dtype,
-                                      w_bias, rstd, g_residual, g_residual_stride, workspace,
-                                      workspace_bytes_, rows, hidden, stream));
-  return dn_train_backward_reduce(dw, workspace, workspace_bytes_, rows, hidden, stream);
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_dw(dw, dw_dtype));
+  BwdParams p;
+  int tier = 0;
+  DN_CHECK(bwd_prepare(&p, &tier, dx, dx_stride, g, g_stride, x, x_stride, w, w_dtype, w_bias,
+                       rstd, g_residual, g_residual_stride, rows, hidden));
+  DN_CHECK(check_workspace(workspace, workspace_bytes_, hidden));
+  p.part = static_cast<double*>(workspace);
+  return bwd_launch(p, tier, dw, dw_dtype, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ LayerNorm family

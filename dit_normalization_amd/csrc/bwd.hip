@@ -1,4 +1,5 @@
-// Training-backward kernels: stage 1 over every row tier, and the fixed-order dw reduction.
+// Training-backward kernels: the producers (dx and per-chunk FP64 column sums) over every
+// row tier, and the fixed-order dw reduction.
 #include "dn_launch.h"
 
 namespace dn {
@@ -24,12 +25,12 @@ hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStre
   }
 }
 
-hipError_t bwd_reduce_launch(float* dw, const double* part, int hidden, int chunks,
-                             hipStream_t s) {
+hipError_t bwd_reduce_launch(void* dw, int dw_bf16, const double* part, int hidden,
+                             int chunks, hipStream_t s) {
   constexpr int NT = 512;
-  const int grid = (hidden + 63) / 64;
-  hipLaunchKernelGGL(bwd_reduce_kernel<NT>, dim3(grid), dim3(NT), 0, s, dw, part, hidden,
-                     chunks);
+  const int grid = (hidden + reduce_cols(NT) - 1) / reduce_cols(NT);
+  hipLaunchKernelGGL(bwd_reduce_kernel<NT>, dim3(grid), dim3(NT), 0, s, dw, dw_bf16, part,
+                     hidden, chunks);
   return hipGetLastError();
 }
 

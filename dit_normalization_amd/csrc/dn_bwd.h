@@ -1,10 +1,10 @@
 // Training backward of RMSNorm for gfx950: dx plus a bitwise-deterministic FP32 dw.
 //
-// Stage 1 (bwd_partials_kernel): one block per fixed chunk of rows; chunk c of C holds rows
-// c, c + C, c + 2C, ... (C = min(rows, 256)), so at any moment the blocks stream
-// neighbouring rows (HBM serves interleaved streams better than C separate contiguous
-// ranges).  Every thread owns a fixed set of 16-byte column vectors for the whole chunk, so
-// its slice of dw stays in FP64 registers while the block streams the chunk's rows:
+// Producers (one block per fixed chunk of rows): chunk c of C holds rows c, c + C, c + 2C,
+// ... (C = min(rows, 256)), so at any moment the blocks stream neighbouring rows (HBM
+// serves interleaved streams better than C separate contiguous ranges).  Every thread owns
+// a fixed set of 16-byte column vectors for the whole chunk, so its slice of dw stays in
+// FP64 registers while the block streams the chunk's rows:
 //     per row t:  c_t  = (1/H) sum_j g*w_eff*x         (lane partials in FP32, then FP64)
 //                 dx   = BF16(r*g*w_eff - x*(r^3*c_t) [+ g_residual])
 //     per column: P[chunk][j] += (g*x) * r              (exact products, FP64 sums)
@@ -12,10 +12,21 @@
 // narrow rows several row groups run side by side and their FP64 sums are added in group
 // order at the end.  The chunk's FP64 column sums are written as one workspace row.
 //
-// Stage 2 (bwd_reduce_kernel): dw_j = FP32(sum over chunks of P[chunk][j]) in a fixed
-// order -- each wave adds a fixed contiguous range of chunk rows, then the waves' sums are
-// added in wave order.  The chunk table depends only on (rows, hidden), never on the
-// device, so dw is bitwise reproducible on any MI355X.
+// Reduction: dw_j = FP32(sum over chunks of P[chunk][j]) in a fixed order -- the chunk
+// rows are cut into eight contiguous ranges, each range is added in chunk order, then the
+// eight range sums in range order.  The chunk table depends only on (rows, hidden), never
+// on the device, so dw is bitwise reproducible on any MI355X.
+//
+// The reduction is a second launch.  The pages' design finishes it inside the first one
+// (the block that completes last reduces the partials), which needs every block's chunk
+// row visible to another block within the kernel.  On MI355X the eight XCDs' L2 caches
+// are not coherent with one another, so that takes a release (an L2 write-back) in every
+// producing block and an acquire (an L2 invalidation) in every reducing block.  Measured
+// at [2048, 8192] and [16384, 8192], with blocks taking producer or reducer roles by a
+// ticket: 56 / 165 us with one release per producing block and one acquire per reducing
+// block (138 / 244 us with a release in every wave; 49 / 156 us with no release at all,
+// which is unsafe), against 30.5 / 139 us for two launches, whose boundary does the same
+// cache maintenance once.
 #pragma once
 
 #include "dn_device.h"
@@ -25,6 +36,10 @@ namespace dn {
 // Fixed upper bound on the number of row chunks (the workspace holds this many rows of
 // FP64 column sums).  chunks = min(rows, kMaxChunks).
 constexpr int kMaxChunks = 256;
+// Columns one reduction block adds per 512 threads (one per lane of a wave), and the
+// contiguous chunk ranges whose sums are added last, in range order.
+constexpr int kReduceCols = 64;
+constexpr int kReduceRanges = 8;
 
 struct BwdParams {
   uint16_t* dx;          int64_t sdx;
@@ -40,6 +55,66 @@ struct BwdParams {
   int chunks;
 };
 
+// Columns one reduction block of NT threads covers.
+__host__ __device__ constexpr int reduce_cols(int nt) {
+  return nt >= 1024 ? 2 * kReduceCols : kReduceCols;
+}
+
+// dw of `slice`'s columns from the chunk rows: each lane adds the chunk rows of one range
+// for one column (all its loads issued before the first add), the ranges meet in LDS and
+// are added in range order; one rounding to FP32 (then to BF16 when dw_bf16, as a BF16
+// weight's gradient is the FP32 value rounded once more).
+template <int NT>
+__device__ __forceinline__ void reduce_columns(const double* __restrict__ part, int hidden,
+                                               int chunks, int slice, void* dw, int dw_bf16,
+                                               double* red) {
+  constexpr int NW = NT / 64;
+  constexpr int COLS = reduce_cols(NT);
+  constexpr int PASSES = NW >= 8 ? 1 : kReduceRanges / NW;   // ranges per wave
+  static_assert(NW == 4 || NW == 8 || NW == 16, "reduction blocks of 256, 512 or 1024 threads");
+  constexpr int kMaxLen = kMaxChunks / kReduceRanges;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int half = NW >= 16 ? wv / 8 : 0;
+  const int c_local = half * 64 + lane;
+  const int col = slice * COLS + c_local;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int range = NW >= 8 ? (wv & 7) : wv + ps * NW;
+    const int cb = range * chunks / kReduceRanges, ce = (range + 1) * chunks / kReduceRanges;
+    const int len = ce - cb;
+    // Every load is issued unconditionally, at an index clamped into the chunk rows (no
+    // branch between a load and the next, so all of them are in flight before the first
+    // add); the range's own values are then added in chunk order and the others dropped
+    // by a select (adding +0.0 to a sum that started at +0.0 changes no bit).
+    const int cc = col < hidden ? col : hidden - 1;
+    double v[kMaxLen];
+#pragma unroll
+    for (int i = 0; i < kMaxLen; ++i) {
+      const int c = cb + i < chunks ? cb + i : chunks - 1;
+      v[i] = part[(int64_t)c * hidden + cc];
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kMaxLen; ++i) s += i < len ? v[i] : 0.0;
+    red[range * COLS + c_local] = s;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < COLS) {
+    const int c = slice * COLS + (int)threadIdx.x;
+    if (c < hidden) {
+      double t = 0.0;
+#pragma unroll
+      for (int r = 0; r < kReduceRanges; ++r) t += red[r * COLS + threadIdx.x];
+      const float f = (float)t;
+      if (dw_bf16)
+        static_cast<uint16_t*>(dw)[c] = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+      else
+        static_cast<float*>(dw)[c] = f;
+    }
+  }
+}
+
 __device__ __forceinline__ void bwd_weff8(const BwdParams& p, int vec, float e[8]) {
   if (p.w_f32) {
     const float4* w = reinterpret_cast<const float4*>(p.w) + 2 * vec;
@@ -53,6 +128,8 @@ __device__ __forceinline__ void bwd_weff8(const BwdParams& p, int vec, float e[8
   for (int k = 0; k < 8; ++k) e[k] += p.w_bias;
 }
 
+// Dynamic LDS of a producer launch: the double-buffered dot-product slots, and the row
+// groups' column sums when they meet at the end.
 __host__ __device__ inline size_t bwd_lds_bytes(int g, int wpr, int rb, int nt, int vb) {
   const size_t red = (size_t)2 * g * wpr * rb * sizeof(double);
   const size_t comb = g > 1 ? (size_t)nt * vb * 8 * sizeof(double) : 0;
@@ -93,12 +170,12 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
   double* red = reinterpret_cast<double*>(dn_lds);
 
   const Geom geo;
+  const int chunk = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = geo.lane;
   const int nvec = p.nvec;
   const bool lane_ok = TPR >= 64 || lane < nvec;
   const uint32_t row_bf16 = 2u * (uint32_t)p.hidden;
-  const int chunk = blockIdx.x;
   // The chunk's rows as a strided matrix: logical row j is row chunk + j*C of the inputs.
   const int64_t C = p.chunks;
   const int64_t re = (p.rows - chunk + C - 1) / C;     // rows in this chunk
@@ -255,46 +332,36 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
     }
   } else {
     __syncthreads();                       // the dot-product slots are reused below
-    const int cols = TPR * VB * 8;         // columns held by one row group
-    double* comb = red;                    // [G][cols]
+    constexpr int GV = TPR * VB;           // column vectors held by one row group
+    double* comb = red;                    // [G][8][GV]: lanes write consecutive doubles
 #pragma unroll
     for (int v = 0; v < VB; ++v)
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        comb[(size_t)geo.grp * cols + (v * TPR + lane) * 8 + k] = acc[v][k];
+        comb[((size_t)geo.grp * 8 + k) * GV + v * TPR + lane] = acc[v][k];
     __syncthreads();
-    for (int col = tid; col < cols && col < p.hidden; col += NT) {
-      double s = 0.0;
-      for (int gg = 0; gg < G; ++gg) s += comb[(size_t)gg * cols + col];
-      out[col] = s;
+    for (int vec = tid; vec < nvec; vec += NT) {
+      double s[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s[k] = 0.0;
+        for (int gg = 0; gg < G; ++gg) s[k] += comb[((size_t)gg * 8 + k) * GV + vec];
+      }
+      double2* o = reinterpret_cast<double2*>(out + 8 * (int64_t)vec);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = make_double2(s[2 * k], s[2 * k + 1]);
     }
   }
+
 }
 
-// Stage 2: one block per 64 columns; wave wv adds chunk rows [wv*C/NW, (wv+1)*C/NW) in
-// order, then wave 0 adds the NW wave sums in order and rounds once to FP32.
+// The reduction launch: one block of 512 threads per 64 columns.
 template <int NT>
-__global__ void __launch_bounds__(NT) bwd_reduce_kernel(float* dw, const double* part,
-                                                        int hidden, int chunks) {
-  constexpr int NW = NT / 64;
-  __shared__ double red[NW][64];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + lane;
-  const int cb = wv * chunks / NW, ce = (wv + 1) * chunks / NW;
-  double s = 0.0;
-  if (col < hidden) {
-#pragma unroll 8
-    for (int c = cb; c < ce; ++c) s += part[(int64_t)c * hidden + col];
-  }
-  red[wv][lane] = s;
-  __syncthreads();
-  if (wv == 0 && col < hidden) {
-    double t = 0.0;
-#pragma unroll
-    for (int w8 = 0; w8 < NW; ++w8) t += red[w8][lane];
-    dw[col] = (float)t;
-  }
+__global__ void __launch_bounds__(NT) bwd_reduce_kernel(void* dw, int dw_bf16,
+                                                        const double* part, int hidden,
+                                                        int chunks) {
+  __shared__ double red[kReduceRanges * reduce_cols(NT)];
+  reduce_columns<NT>(part, hidden, chunks, blockIdx.x, dw, dw_bf16, red);
 }
 
 // (threads per row, vectors per thread, rows per group per step, threads per block).

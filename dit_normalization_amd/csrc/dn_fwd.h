@@ -169,6 +169,17 @@ constexpr bool fwd_double_buffer(int in, int epi, int vmax, int r, int nt) {
   return 2 * step + 96 <= budget;
 }
 
+// The block's place in the row order.  Tuning builds (DN_XCD_ROWS) number the blocks of
+// each XCD consecutively (blocks are dealt to the 8 XCDs round-robin), so that
+// neighbouring rows, and the per-row side arrays they share cache lines with, stay on one
+// XCD's L2.
+__device__ __forceinline__ int row_block(int b, int n) {
+#ifdef DN_XCD_ROWS
+  if ((n & 7) == 0) return (b & 7) * (n >> 3) + (b >> 3);
+#endif
+  return b;
+}
+
 template <int IN, int EPI, int TPR, int VMAX, int R, int NT>
 __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   extern __shared__ __align__(16) unsigned char dn_lds[];
@@ -691,7 +702,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     // Two steps in flight: the next step's loads are issued before the current step's
     // arithmetic, reduction and stores.
     Step s0, s1;
-    int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER;
+    int64_t base = (int64_t)row_block(blockIdx.x, gridDim.x) * Geom::PER_ITER;
     if (base < p.rows) load(s0, base);
     stage();
     while (base < p.rows) {
@@ -709,7 +720,7 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
     // The first step is peeled so that its loads precede the set-up; the steady-state loop
     // keeps the load-then-process shape.
     Step s0;
-    int64_t base = (int64_t)blockIdx.x * Geom::PER_ITER;
+    int64_t base = (int64_t)row_block(blockIdx.x, gridDim.x) * Geom::PER_ITER;
     if (base < p.rows) {
       load(s0, base);
       stage();
@@ -744,10 +755,10 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
   X(9, 256, 3, 1, 256)  X(10, 256, 4, 1, 256) X(11, 512, 3, 1, 512)            \
   X(12, 512, 4, 1, 512) X(13, 1024, 4, 1, 1024)                                \
   X(14, 64, 6, 1, 256)  X(15, 64, 8, 1, 256)  X(16, 64, 12, 1, 256)            \
-  X(17, 64, 16, 1, 256) X(18, 128, 8, 1, 256) X(19, 256, 8, 1, 256)            \
-  X(20, 512, 8, 1, 512)
+  X(17, 64, 16, 1, 256) X(18, 128, 7, 1, 256) X(19, 128, 8, 1, 256)            \
+  X(20, 256, 8, 1, 256) X(21, 512, 8, 1, 512)
 
-constexpr int kFwdTierCount = 21;
+constexpr int kFwdTierCount = 22;
 constexpr int kFwdAutoTiers = 14;   // tiers the automatic choice considers
 
 // Largest VMAX an input/epilogue combination is built with: the Ada, gated and

@@ -65,7 +65,7 @@ hipError_t gres_launch(const GresParams& p, int tier, int grid, size_t lds, hipS
 
 hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStream_t s,
                                const void** kernel_out);
-hipError_t bwd_reduce_launch(float* dw, const double* part, int hidden, int chunks,
-                             hipStream_t s);
+hipError_t bwd_reduce_launch(void* dw, int dw_bf16, const double* part, int hidden,
+                             int chunks, hipStream_t s);
 
 }  // namespace dn

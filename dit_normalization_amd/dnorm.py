@@ -49,12 +49,12 @@ SIGNATURES = {
         [_P, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _I64, _I64, _F32, _P], _I32),
     "dn_train_backward_workspace_bytes": ([_I64], _SZ),
     "dn_train_backward": (
-        [_P, _I64, _P, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
-        _I32),
+        [_P, _I64, _P, _I32, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64,
+         _P], _I32),
     "dn_train_backward_partials": (
         [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
         _I32),
-    "dn_train_backward_reduce": ([_P, _P, _SZ, _I64, _I64, _P], _I32),
+    "dn_train_backward_reduce": ([_P, _I32, _P, _SZ, _I64, _I64, _P], _I32),
     "dn_layernorm": ([_P, _I64, _P, _I64, _P, _P, _I64, _I64, _F32, _P], _I32),
     "dn_layernorm_quant": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _I64, _F32, _P], _I32),
     "dn_fused_dit_gate_residual_layernorm_gamma_beta": (
@@ -403,7 +403,7 @@ def dn_train_backward_workspace_bytes(hidden: int) -> int:
 
 def train_backward_workspace(hidden: int, device) -> torch.Tensor:
     """A zeroed uint8 workspace of dn_train_backward_workspace_bytes(hidden) bytes (torch's
-    allocator returns 256-byte aligned blocks)."""
+    allocator returns 256-byte aligned blocks); it needs no zeroing."""
     n = dn_train_backward_workspace_bytes(hidden)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
@@ -424,11 +424,24 @@ def _bwd_common(g, x, w, rstd, g_residual, dx):
     return gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr
 
 
+def _dw_buffer(dw, hidden: int, device, dtype):
+    """A dw output: `hidden` contiguous values of FP32 or BF16 on the device (allocated when
+    None, in `dtype`); returns (tensor, dtype code)."""
+    if dw is None:
+        dw = torch.empty(hidden, dtype=dtype, device=device)
+    if dw.dtype not in (torch.float32, torch.bfloat16) or not dw.is_contiguous() or \
+            dw.numel() != hidden or dw.device != device:
+        raise DnormError(f"dw must be a contiguous float32 or bfloat16 tensor of {hidden} values "
+                         f"on {device} (got {dw.dtype}, {tuple(dw.shape)}, {dw.device})")
+    return dw, DN_WEIGHT_F32 if dw.dtype == torch.float32 else DN_WEIGHT_BF16
+
+
 def dn_train_backward(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, workspace=None,
-                      dx=None, dw=None, deterministic: bool = True):
-    """(dx, dw): dx BF16 like x, dw FP32 [hidden], bitwise deterministic.  Only the
-    deterministic dw reduction exists; deterministic=False is rejected (cake bwd docs,
-    Parameters: deterministic)."""
+                      dx=None, dw=None, dw_dtype=torch.float32, deterministic: bool = True):
+    """(dx, dw): dx BF16 like x, dw [hidden] bitwise deterministic, FP32 (or BF16 when
+    dw_dtype is torch.bfloat16 or `dw` is a BF16 tensor: the FP32 value rounded once more).
+    Only the deterministic dw reduction exists; deterministic=False is rejected (cake bwd
+    docs, Parameters: deterministic)."""
     if not deterministic:
         raise DnormError("deterministic=False is not supported: dw is always reduced in a "
                          "fixed order (bitwise reproducible)")
@@ -436,12 +449,12 @@ def dn_train_backward(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, wo
     H = xr.size(-1)
     if workspace is None:
         workspace = train_backward_workspace(H, x.device)
-    if dw is None:
-        dw = torch.empty(H, dtype=torch.float32, device=x.device)
-    _check(lib.dn_train_backward(dr.data_ptr(), sd, dw.data_ptr(), gr.data_ptr(), sg, xr.data_ptr(),
-                                 sx, w.data_ptr(), wcode, w_bias, rstd.data_ptr(), _ptr(grr), sgr,
-                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                 rows, H, _stream(x)), "dn_train_backward")
+    dw, dcode = _dw_buffer(dw, H, x.device, dw_dtype)
+    _check(lib.dn_train_backward(dr.data_ptr(), sd, dw.data_ptr(), dcode, gr.data_ptr(), sg,
+                                 xr.data_ptr(), sx, w.data_ptr(), wcode, w_bias, rstd.data_ptr(),
+                                 _ptr(grr), sgr, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), rows, H,
+                                 _stream(x)), "dn_train_backward")
     _writeback(d, dr)
     return d, dw
 
@@ -460,11 +473,12 @@ def dn_train_backward_partials(g, x, w, rstd, workspace, *, w_bias: float = 0.0,
     return d
 
 
-def dn_train_backward_reduce(workspace, rows: int, hidden: int, *, dw=None):
-    """Stage 2 of the backward: dw from the chunk sums of a partials call with `rows`."""
-    if dw is None:
-        dw = torch.empty(hidden, dtype=torch.float32, device=workspace.device)
-    _check(lib.dn_train_backward_reduce(dw.data_ptr(), workspace.data_ptr(),
+def dn_train_backward_reduce(workspace, rows: int, hidden: int, *, dw=None,
+                             dw_dtype=torch.float32):
+    """dw from the chunk rows of a partials call with `rows` (FP32, or BF16 as in
+    dn_train_backward)."""
+    dw, dcode = _dw_buffer(dw, hidden, workspace.device, dw_dtype)
+    _check(lib.dn_train_backward_reduce(dw.data_ptr(), dcode, workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), rows, hidden,
                                         _stream(workspace)), "dn_train_backward_reduce")
     return dw

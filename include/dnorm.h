@@ -196,26 +196,32 @@ dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd,
 
 /* ---------------------------------------------------------------------------------------
  * Training backward   ([norm docs] cake_rmsnorm_train_backward, ..._workspace_bytes;
- *                      [norm guide] §6.1-6.3)
+ *                      [norm guide] §6.1-6.4)
  *   dx = BF16(r*g*w_eff - x*r^3*mean_j(g*w_eff*x) [+ g_residual])
  *   dw = FP32(sum_t g*x*r)     -- the gradient with respect to w_eff (= w + w_bias)
  *   x is the tensor the forward normalised (h_new on the residual route) and rstd the FP32
  *   tensor the forward returned.  g_residual (nullable) is the gradient reaching h_new
  *   directly; dx is then the gradient of both residual inputs.
+ *   dw_dtype: DN_WEIGHT_F32 writes FP32 dw [hidden]; DN_WEIGHT_BF16 writes BF16 dw
+ *   [hidden], the FP32 value rounded once more ([norm guide] §6.4: dw is accumulated in
+ *   FP32 and cast to the weight's dtype).
  *
  *   dw is bitwise deterministic: rows are cut into min(rows, 256) fixed chunks that depend
  *   on rows only (not on the device); each chunk's column sums are carried in FP64 from
- *   exact products into one workspace row, and a second kernel adds the chunk rows in a
- *   fixed order before one rounding to FP32.
+ *   exact products into one workspace row, and a second launch on the same stream adds the
+ *   chunk rows in a fixed order (eight contiguous ranges of chunks, each in chunk order,
+ *   then the ranges in order) before one rounding to FP32.
  *
  *   workspace: caller-owned device memory of at least
- *   dn_train_backward_workspace_bytes(hidden) bytes, 256-byte aligned.  It needs no
- *   zeroing; every call rewrites what it reads, so one buffer serves every call, token
- *   count and stream-ordered replay.  Calls sharing a workspace must be stream-ordered.
+ *   dn_train_backward_workspace_bytes(hidden) = 256 * hidden * 8 bytes (FP64 chunk rows),
+ *   256-byte aligned.  It needs no zeroing: every call rewrites the chunk rows it reads, so
+ *   one buffer serves every call, token count and stream-ordered replay.  Calls sharing a
+ *   workspace must be stream-ordered.  (The pages' workspace-size call also takes a
+ *   residual flag; the size here depends on neither it nor rows, so only hidden is passed.)
  */
 size_t dn_train_backward_workspace_bytes(int64_t hidden);
 
-dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw,
+dn_status dn_train_backward(void* dx, int64_t dx_stride, void* dw, int dw_dtype,
                             const void* g, int64_t g_stride,
                             const void* x, int64_t x_stride,
                             const void* w, int w_dtype, float w_bias, const float* rstd,
@@ -223,12 +229,13 @@ dn_status dn_train_backward(void* dx, int64_t dx_stride, float* dw,
                             void* workspace, size_t workspace_bytes,
                             int64_t rows, int64_t hidden, dn_stream_t stream);
 
-/* The two stages of dn_train_backward, exposed so a caller can place the dw reduction
- * elsewhere (e.g. after exchanging chunk rows between data-parallel ranks) or time the
- * stages apart.  dn_train_backward == partials followed by reduce on the same stream.
+/* The two launches of dn_train_backward, exposed so a caller can place the dw reduction
+ * elsewhere (e.g. after exchanging chunk rows between data-parallel ranks) or time them
+ * apart.  partials followed by reduce on the same stream is dn_train_backward.
  *   partials: dx, and the FP64 per-chunk column sums in the workspace.
- *   reduce:   dw[j] = FP32(sum over the chunk rows of column j, in chunk order); `rows`
- *             must equal the rows given to the partials call (it fixes the chunk count). */
+ *   reduce:   dw[j] = the fixed-order sum of the chunk rows of column j, rounded to FP32
+ *             (and to BF16 for DN_WEIGHT_BF16); `rows` must equal the rows given to the
+ *             partials call (it fixes the chunk count). */
 dn_status dn_train_backward_partials(void* dx, int64_t dx_stride,
                                      const void* g, int64_t g_stride,
                                      const void* x, int64_t x_stride,
@@ -238,8 +245,9 @@ dn_status dn_train_backward_partials(void* dx, int64_t dx_stride,
                                      void* workspace, size_t workspace_bytes,
                                      int64_t rows, int64_t hidden, dn_stream_t stream);
 
-dn_status dn_train_backward_reduce(float* dw, const void* workspace, size_t workspace_bytes,
-                                   int64_t rows, int64_t hidden, dn_stream_t stream);
+dn_status dn_train_backward_reduce(void* dw, int dw_dtype, const void* workspace,
+                                   size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                   dn_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * LayerNorm family   ([norm docs] API table: layernorm, layernorm_quant and the three

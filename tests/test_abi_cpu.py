@@ -157,15 +157,24 @@ def test_train_checks(lib):
     assert f(A, 8192, B, 0, 8192, D, 8192, E, 8192, A, 1, 1.0, 5, 8192, 1e-6, None) == E_NULL
     ws = 256 * 8192 * 8
     b = lib.dn_train_backward
-    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 0, 8192, None) == OK
-    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws - 8, 5, 8192,
+    F32, BF = 1, 0
+    assert b(A, 8192, B, F32, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 0, 8192, None) == OK
+    assert b(A, 8192, B, F32, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws - 8, 5, 8192,
              None) == E_WS
-    assert b(A, 8192, B, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B + 64, ws, 5, 8192,
+    assert b(A, 8192, B, F32, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B + 64, ws, 5, 8192,
              None) == E_WS
-    assert b(A, 8192, 0, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192, None) == E_NULL
+    assert b(A, 8192, 0, F32, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192,
+             None) == E_NULL
+    assert b(A, 8192, B, 7, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192,
+             None) == E_DTYPE
+    assert b(A, 8192, B + 2, F32, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192,
+             None) == E_ALIGN                                   # FP32 dw: 4-byte aligned
+    assert b(A, 8192, B + 1, BF, C, 8192, D, 8192, E, 1, 1.0, A, 0, 0, B, ws, 5, 8192,
+             None) == E_ALIGN                                   # BF16 dw: 2-byte aligned
     r = lib.dn_train_backward_reduce
-    assert r(A, B, ws, 0, 8192, None) == OK
-    assert r(A, B, ws // 2, 5, 8192, None) == E_WS
+    assert r(A, F32, B, ws, 0, 8192, None) == OK
+    assert r(A, F32, B, ws // 2, 5, 8192, None) == E_WS
+    assert r(A, 3, B, ws, 5, 8192, None) == E_DTYPE
 
 
 def test_binding_rejects_a_nondeterministic_backward(dn):

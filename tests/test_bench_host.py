@@ -26,8 +26,15 @@ def test_step_bytes_are_each_tensor_once():
     # + static FP8: e4m3 out instead of y, and the FP32 scale
     assert ab["fused_add_rmsnorm_quant"] == 7 * t2 * h2 + 2 * h2 + 4 == 234_889_220
     assert ab["train_forward"] == 8 * t4 * h4 + 4 * t4 + 4 * h4 == 1_073_840_128
-    assert ab["train_backward_partials"] + ab["train_backward_reduce"] == 805_437_440
+    # backward: g, x (h_new) in, dx out (BF16); rstd, FP32 weight; FP32 dw out
+    assert ab["train_backward"] == 6 * t4 * h4 + 4 * t4 + 4 * h4 + 4 * h4 == 805_437_440
     assert set(ab) == set(bench.STEP_KERNELS)
+    assert set(bench.PAIR_KERNELS) == {"fused_add_rmsnorm", "train_backward"}
+    # the counter summary maps dispatches: the backward's two launches share its bytes
+    db = bench.step_dispatch_bytes()
+    assert list(db) == bench.STEP_DISPATCHES
+    assert db["train_backward_partials"] + db["train_backward_reduce"] == ab["train_backward"]
+    assert db["train_backward_reduce"] == 4 * h4
 
 
 def test_family_tables_cover_every_family():

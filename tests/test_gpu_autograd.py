@@ -8,7 +8,7 @@ import torch
 import workloads as W
 from oracle import formats as F
 from oracle import rmsnorm as O
-from tests.conftest import values
+from tests.conftest import bits16, values
 from tests.parity import assert_bf16, assert_bits_equal, assert_dx
 
 pytestmark = pytest.mark.gpu
@@ -71,6 +71,12 @@ def test_autograd_residual_route(ag):
     got = values(w.grad.detach())
     spread = np.sum(np.abs(values(t["g"]) * fwd.h_new * fwd.rstd[:, None]), axis=0)
     assert np.all(np.abs(got - ref.dw_exact) <= 2.0 ** -8 * np.abs(ref.dw_exact) + 4e-7 * spread)
+    # ... and bit for bit the FP32 dw of the same call rounded to BF16 by the oracle's codec
+    # (the forward is deterministic, so it gives the saved rstd again)
+    from dit_normalization_amd import dnorm as dn
+    _, rs, hn = dn.dn_train_forward(dev(t["h"]), dev(wb), 1e-6, residual=dev(t["residual"]))
+    _, dw32 = dn.dn_train_backward(dev(t["g"]), hn, dev(wb), rs, g_residual=dev(gh))
+    assert (bits16(w.grad) == F.f64_to_bf16_bits(dw32.cpu().double().numpy())).all()
 
 
 def test_autograd_3d_input(ag):

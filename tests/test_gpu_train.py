@@ -167,3 +167,28 @@ def test_train_16384x8192(dn):
     assert_dw(dw, dw_oracle(t["g"], h, rs, t["w"]), "dw [16384,8192]")
     dw_again = dn.dn_train_backward(gd, hd, wd, rsd, w_bias=1.0)[1]
     assert torch.equal(dw.view(torch.int32), dw_again.view(torch.int32))
+
+
+@pytest.mark.parametrize("rows,hidden", [(2048, 8192), (1, 520), (255, 64), (257, 8192),
+                                         (3000, 4096), (40, 24576)])
+def test_backward_equals_its_two_launches_and_bf16_dw(dn, rows, hidden):
+    """dn_train_backward gives the bits of its two launches called apart (partials, then the
+    reduction), FP32 and BF16 dw (the BF16 dw is the FP32 dw rounded once more, checked with
+    the oracle's codec); dw against the oracle."""
+    wl = W.train(rows=rows, hidden=hidden)
+    t = wl.tensors
+    h, rstd = backward_inputs(t)
+    g, hd, w, rs = dev(t["g"]), dev(h), dev(t["w"]), dev(rstd)
+    dx1, dw1 = dn.dn_train_backward(g, hd, w, rs, w_bias=1.0)
+    ws2 = dn.train_backward_workspace(hidden, "cuda")
+    dx2 = dn.dn_train_backward_partials(g, hd, w, rs, ws2, w_bias=1.0)
+    dw2 = dn.dn_train_backward_reduce(ws2, rows, hidden)
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dw1.view(torch.int32), dw2.view(torch.int32))
+    ref = O.train_backward(values(t["g"]), values(h), values(t["w"]), rstd.double().numpy(), 1.0)
+    assert_dw(dw1, ref.dw_exact, f"dw [{rows},{hidden}]")
+    _, dwb = dn.dn_train_backward(g, hd, w, rs, w_bias=1.0, dw_dtype=torch.bfloat16)
+    assert dwb.dtype == torch.bfloat16
+    assert (bits16(dwb) == F.f64_to_bf16_bits(dw1.cpu().double().numpy())).all()
+    dwb2 = dn.dn_train_backward_reduce(ws2, rows, hidden, dw_dtype=torch.bfloat16)
+    assert torch.equal(dwb.view(torch.int16), dwb2.view(torch.int16))
