@@ -9,7 +9,8 @@ library raises ImportError: there is no CPU fallback.
 __all__ = [
     "dn_rmsnorm", "dn_rmsnorm_quant", "dn_fused_add_rmsnorm", "dn_fused_add_rmsnorm_quant",
     "dn_fused_add_rmsnorm_fp8_block_quant", "dn_ada_rms_norm", "dn_gate_residual_ada_norm_fp8",
-    "dn_train_forward", "dn_train_backward", "dn_train_backward_partials",
+    "dn_train_forward", "dn_train_backward", "dn_train_backward_noalloc",
+    "dn_train_backward_partials",
     "dn_train_backward_reduce", "dn_train_backward_workspace_bytes", "train_backward_workspace",
     "dn_layernorm", "dn_layernorm_quant", "dn_fused_dit_gate_residual_layernorm_gamma_beta",
     "dn_fused_dit_gate_residual_layernorm_scale_shift",

@@ -629,6 +629,72 @@ dn_status dn_train_backward(void* dx, int64_t dx_stride, void* dw, int dw_dtype,
   return bwd_launch(p, tier, dw, dw_dtype, static_cast<hipStream_t>(stream));
 }
 
+// ------------------------------------------------------------------ allocation-free backward
+
+namespace {
+
+// Scratch of dn_train_backward_noalloc: the FP64 chunk rows for hidden up to
+// kNoAllocMaxHidden.  Every GPU the library runs on holds its own copy (16 MiB) until the
+// process ends.
+constexpr int64_t kNoAllocMaxHidden = 8192;
+constexpr size_t kScratchBytes = (size_t)kMaxChunks * kNoAllocMaxHidden * sizeof(double);
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The device address of `scratch` on the current device, looked up once per device (the
+// host-side name is only a stand-in for it).  Nothing in it needs clearing: every call
+// rewrites the chunk rows it reads.
+dn_status scratch_address(unsigned char** out) {
+  static std::mutex mu;
+  static std::map<int, unsigned char*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DN_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it != ptrs.end()) {
+    *out = it->second;
+    return DN_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(DN_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+  *out = static_cast<unsigned char*>(ptr);
+  ptrs.emplace(dev, *out);
+  return DN_OK;
+}
+
+}  // namespace
+
+dn_status dn_train_backward_noalloc(void* dx, int64_t dx_stride, void* dw, int dw_dtype,
+                                    const void* g, int64_t g_stride, const void* x,
+                                    int64_t x_stride, const void* w, int w_dtype, float w_bias,
+                                    const float* rstd, const void* g_residual,
+                                    int64_t g_residual_stride, int64_t rows, int64_t hidden,
+                                    dn_stream_t stream) {
+  DN_CHECK(check_shape(rows, hidden, 8, "hidden"));
+  if (hidden > kNoAllocMaxHidden)
+    return fail(DN_ERR_UNSUPPORTED,
+                "hidden %lld exceeds the allocation-free scratch (hidden <= %lld); use "
+                "dn_train_backward with a workspace", (long long)hidden,
+                (long long)kNoAllocMaxHidden);
+  if (rows == 0) return DN_OK;  // empty tensors may carry NULL pointers
+  DN_CHECK(check_dw(dw, dw_dtype));
+  BwdParams p;
+  int tier = 0;
+  DN_CHECK(bwd_prepare(&p, &tier, dx, dx_stride, g, g_stride, x, x_stride, w, w_dtype, w_bias,
+                       rstd, g_residual, g_residual_stride, rows, hidden));
+  unsigned char* base = nullptr;
+  DN_CHECK(scratch_address(&base));
+  p.part = reinterpret_cast<double*>(base);
+  return bwd_launch(p, tier, dw, dw_dtype, static_cast<hipStream_t>(stream));
+}
+
 // ------------------------------------------------------------------ LayerNorm family
 
 dn_status dn_layernorm(void* y, int64_t y_stride, const void* x, int64_t x_stride,

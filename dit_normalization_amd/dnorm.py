@@ -51,6 +51,8 @@ SIGNATURES = {
     "dn_train_backward": (
         [_P, _I64, _P, _I32, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64,
          _P], _I32),
+    "dn_train_backward_noalloc": (
+        [_P, _I64, _P, _I32, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _I64, _I64, _P], _I32),
     "dn_train_backward_partials": (
         [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _F32, _P, _P, _I64, _P, _SZ, _I64, _I64, _P],
         _I32),
@@ -455,6 +457,23 @@ def dn_train_backward(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, wo
                                  _ptr(grr), sgr, workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), rows, H,
                                  _stream(x)), "dn_train_backward")
+    _writeback(d, dr)
+    return d, dw
+
+
+def dn_train_backward_noalloc(g, x, w, rstd, *, w_bias: float = 0.0, g_residual=None, dx=None,
+                              dw=None, dw_dtype=torch.float32):
+    """dn_train_backward without a workspace: the library's static per-GPU scratch (hidden up
+    to 8192) holds the chunk rows.  Calls that overlap on one GPU race; stream-ordered calls
+    are safe.  The binding still allocates dx and dw when they are omitted; pass both for an
+    allocation-free call."""
+    gr, rows, sg, xr, sx, w, wcode, d, dr, sd, grr, sgr = _bwd_common(g, x, w, rstd, g_residual, dx)
+    H = xr.size(-1)
+    dw, dcode = _dw_buffer(dw, H, x.device, dw_dtype)
+    _check(lib.dn_train_backward_noalloc(dr.data_ptr(), sd, dw.data_ptr(), dcode, gr.data_ptr(),
+                                         sg, xr.data_ptr(), sx, w.data_ptr(), wcode, w_bias,
+                                         rstd.data_ptr(), _ptr(grr), sgr, rows, H, _stream(x)),
+           "dn_train_backward_noalloc")
     _writeback(d, dr)
     return d, dw
 

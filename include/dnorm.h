@@ -229,6 +229,23 @@ dn_status dn_train_backward(void* dx, int64_t dx_stride, void* dw, int dw_dtype,
                             void* workspace, size_t workspace_bytes,
                             int64_t rows, int64_t hidden, dn_stream_t stream);
 
+/* dn_train_backward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and bits as dn_train_backward, for hidden up to 8192
+ * (DN_ERR_UNSUPPORTED beyond).  The chunk rows live in a static device array of the
+ * library (16 MiB per GPU, held until the process ends; nothing in it needs clearing); the
+ * first call on a device looks its address up.  The call allocates nothing.  Every call on
+ * one GPU shares that array: calls that overlap on one GPU (different streams without
+ * ordering, or several host threads) race and give wrong dw; stream-ordered calls are
+ * safe. */
+dn_status dn_train_backward_noalloc(void* dx, int64_t dx_stride, void* dw, int dw_dtype,
+                                    const void* g, int64_t g_stride,
+                                    const void* x, int64_t x_stride,
+                                    const void* w, int w_dtype, float w_bias,
+                                    const float* rstd,
+                                    const void* g_residual, int64_t g_residual_stride,
+                                    int64_t rows, int64_t hidden, dn_stream_t stream);
+
 /* The two launches of dn_train_backward, exposed so a caller can place the dw reduction
  * elsewhere (e.g. after exchanging chunk rows between data-parallel ranks) or time them
  * apart.  partials followed by reduce on the same stream is dn_train_backward.
