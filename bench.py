@@ -361,6 +361,50 @@ def print_kernel_resources(match: str = "") -> int:
     return 0
 
 
+def summarize_sq(lds_csv: str, occ_csv: str, family: str = "rmsnorm", cus: int = 256,
+                 xcds: int = 8) -> int:
+    """Per-call LDS and occupancy figures from two rocprofv3 --pmc runs of one bench family
+    (SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_INSTS_LDS, GRBM_GUI_ACTIVE; SQ_WAVE_CYCLES,
+    SQ_WAVES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE), next to the registers of each kernel from the
+    code objects.  Bank conflicts per LDS access = conflict cycles / (active cycles -
+    conflict cycles) (rocprofv3's LdsBankConflict); mean waves per CU = 4 * SQ_WAVE_CYCLES /
+    (GRBM_GUI_ACTIVE / xcds * cus) (rocprofv3's OccupancyPercent * 32 / 100; the CSV sums
+    GRBM_GUI_ACTIVE over the XCDs)."""
+    names = STEP_DISPATCHES if family == "rmsnorm" else list(FAMILY_BYTES[family]())
+
+    def per_call(path):
+        rows = _read_csv(path)
+        counters = sorted({r["Counter_Name"] for r in rows})
+        out, sym = {}, {}
+        for c in counters:
+            per = _library_dispatches([r for r in rows if r["Counter_Name"] == c], names)
+            for n, (sy, rs) in per.items():
+                out.setdefault(n, {})[c] = sum(float(r["Counter_Value"]) for r in rs) / len(rs)
+                sym[n] = sy
+        return out, sym
+
+    lds, sym = per_call(lds_csv)
+    occ, sym2 = per_call(occ_csv)
+    if sym != sym2:
+        raise SystemExit("the two counter runs dispatched different kernels")
+    res = {r["name"]: r for r in kernel_resources()}
+    print("| call | kernel | VGPR | SGPR | scratch B | waves/SIMD by registers | mean waves "
+          "per CU | LDS instructions | LDS bank conflicts per access | LDS busy |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for n in names:
+        short = sym[n].replace("void ", "").split("(")[0]
+        r = res.get(short, {})
+        lm, om = lds[n], occ[n]
+        grbm = lm["GRBM_GUI_ACTIVE"] / xcds
+        act, conf = lm["SQ_LDS_IDX_ACTIVE"], lm["SQ_LDS_BANK_CONFLICT"]
+        ratio = conf / (act - conf) if act > conf else 0.0
+        waves = 4 * om["SQ_WAVE_CYCLES"] / (om["GRBM_GUI_ACTIVE"] / xcds * cus)
+        print(f"| {n} | `{short}` | {r.get('vgpr', '?')} | {r.get('sgpr', '?')} | "
+              f"{r.get('scratch', '?')} | {r.get('waves_per_simd', '?')} | {waves:.2f} | "
+              f"{lm['SQ_INSTS_LDS']:,.0f} | {ratio:.4f} | {act / (grbm * cus):.2%} |")
+    return 0
+
+
 def summarize_trace(stats_csv: str) -> int:
     rows = _read_csv(stats_csv)
     print("| kernel | calls | average ns | min ns | max ns | share |")
@@ -1119,6 +1163,9 @@ def main(argv=None) -> int:
                          "library dispatch is then a bench-step kernel)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", metavar="STATS_CSV")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("LDS_CSV", "OCC_CSV"),
+                    help="LDS bank conflicts and occupancy per call from two rocprofv3 --pmc "
+                         "runs (see summarize_sq)")
     ap.add_argument("--kernel-resources", nargs="?", const="", metavar="MATCH",
                     help="print the registers, scratch and LDS of the library's kernels "
                          "(those whose name contains MATCH) from the code objects; no GPU")
@@ -1137,6 +1184,8 @@ def main(argv=None) -> int:
         return summarize_counters(*a.summarize_counters, family=a.family)
     if a.summarize_trace:
         return summarize_trace(a.summarize_trace)
+    if a.summarize_sq:
+        return summarize_sq(*a.summarize_sq, family=a.family)
     if a.kernel_resources is not None:
         return print_kernel_resources(a.kernel_resources)
     if a.gpus != 1:
