@@ -701,11 +701,16 @@ def probe_library(rebuild: bool = False) -> str:
     return PROBE_LIB
 
 
+PROBE_MODES = {0: "grid-stride", 1: "contiguous chunk per block", 2: "XCD partition",
+               3: "LDS pipeline (loads straight into LDS)", 4: "block read/write phases"}
+
+
 def stream_ceilings(torch, dev, reps: int = 5):
-    """Measured HBM stream ceilings (libdnprobe.so): plain kernels with the norm kernels'
-    16-byte non-temporal buffer loads and stores at their read:write mixes, 256 MiB per
-    stream, each mix at 1 and 2 blocks of 256 threads per CU, chunked and grid-stride; the
-    best configuration's median GB/s of bytes moved per mix."""
+    """Measured HBM stream ceilings (probe/stream_probe.hip): plain kernels with the norm
+    kernels' 16-byte non-temporal buffer loads and stores at their read:write mixes, 256 MiB
+    per stream, caches flushed before every launch, under five access strategies (PROBE_MODES)
+    at 1 and 2 blocks of 256 threads per CU.  Returns the best median GB/s (bytes moved) per
+    mix over every strategy, and the best per strategy under `strategies`."""
     import ctypes
     lib = ctypes.CDLL(probe_library())
     f = lib.dn_probe_stream
@@ -716,26 +721,31 @@ def stream_ceilings(torch, dev, reps: int = 5):
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     st = torch.cuda.current_stream(dev).cuda_stream
-    out = {}
+    out, strategies = {}, {}
     for reads, writes in ((1, 1), (2, 2), (2, 1), (3, 1)):
+        mix = f"{reads}r{writes}w"
         best = 0.0
-        for blocks in (cus, 2 * cus):
-            for blocked in (0, 1):
+        for mode in PROBE_MODES:
+            mbest = 0.0
+            for blocks in (cus, 2 * cus):
                 ts = []
                 for _ in range(reps):
                     flush.fill_(1.0)
                     e0 = timing_event(torch)
                     e1 = timing_event(torch)
                     e0.record()
-                    rc = f(*(b.data_ptr() for b in bufs), n, reads, writes, blocks, blocked, st)
+                    rc = f(*(b.data_ptr() for b in bufs), n, reads, writes, blocks, mode, st)
                     e1.record()
                     e1.synchronize()
                     if rc != 0:
                         raise RuntimeError(f"stream probe failed ({rc})")
                     ts.append(e0.elapsed_time(e1) * 1e-3)
                 gbs = (reads + writes) * n / sorted(ts)[len(ts) // 2] / 1e9
-                best = max(best, gbs)
-        out[f"stream_{reads}r{writes}w_GB/s"] = round(best, 1)
+                mbest = max(mbest, gbs)
+            strategies.setdefault(PROBE_MODES[mode], {})[mix] = round(mbest, 1)
+            best = max(best, mbest)
+        out[f"stream_{mix}_GB/s"] = round(best, 1)
+    out["strategies"] = strategies
     del bufs, flush
     return out
 

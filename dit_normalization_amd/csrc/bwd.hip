@@ -27,10 +27,9 @@ hipError_t bwd_partials_launch(const BwdParams& p, int tier, size_t lds, hipStre
 
 hipError_t bwd_reduce_launch(void* dw, int dw_bf16, const double* part, int hidden,
                              int chunks, hipStream_t s) {
-  constexpr int NT = 512;
-  const int grid = (hidden + reduce_cols(NT) - 1) / reduce_cols(NT);
-  hipLaunchKernelGGL(bwd_reduce_kernel<NT>, dim3(grid), dim3(NT), 0, s, dw, dw_bf16, part,
-                     hidden, chunks);
+  const int grid = (hidden + kReduceCols - 1) / kReduceCols;
+  hipLaunchKernelGGL(bwd_reduce_kernel<kReduceThreads>, dim3(grid), dim3(kReduceThreads), 0, s, dw, dw_bf16,
+                     part, hidden, chunks);
   return hipGetLastError();
 }
 

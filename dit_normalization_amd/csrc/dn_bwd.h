@@ -36,10 +36,13 @@ namespace dn {
 // Fixed upper bound on the number of row chunks (the workspace holds this many rows of
 // FP64 column sums).  chunks = min(rows, kMaxChunks).
 constexpr int kMaxChunks = 256;
-// Columns one reduction block adds per 512 threads (one per lane of a wave), and the
-// contiguous chunk ranges whose sums are added last, in range order.
-constexpr int kReduceCols = 64;
+// The reduction: one block of 256 threads per 32 columns (so a hidden of 8192 keeps every
+// CU of the chip busy), thread t adding chunk range t / 32 of column t % 32.  The chunk
+// rows are cut into kReduceRanges contiguous ranges whose sums are added last, in range
+// order.
+constexpr int kReduceThreads = 256;
 constexpr int kReduceRanges = 8;
+constexpr int kReduceCols = kReduceThreads / kReduceRanges;
 
 struct BwdParams {
   uint16_t* dx;          int64_t sdx;
@@ -55,63 +58,46 @@ struct BwdParams {
   int chunks;
 };
 
-// Columns one reduction block of NT threads covers.
-__host__ __device__ constexpr int reduce_cols(int nt) {
-  return nt >= 1024 ? 2 * kReduceCols : kReduceCols;
-}
-
-// dw of `slice`'s columns from the chunk rows: each lane adds the chunk rows of one range
-// for one column (all its loads issued before the first add), the ranges meet in LDS and
-// are added in range order; one rounding to FP32 (then to BF16 when dw_bf16, as a BF16
-// weight's gradient is the FP32 value rounded once more).
+// dw of the reduction block's 32 columns from the chunk rows: each thread adds one range of
+// chunk rows of one column (all its loads issued before the first add), the ranges meet in
+// LDS and are added in range order; one rounding to FP32 (then to BF16 when dw_bf16, as a
+// BF16 weight's gradient is the FP32 value rounded once more).
 template <int NT>
-__device__ __forceinline__ void reduce_columns(const double* __restrict__ part, int hidden,
-                                               int chunks, int slice, void* dw, int dw_bf16,
-                                               double* red) {
-  constexpr int NW = NT / 64;
-  constexpr int COLS = reduce_cols(NT);
-  constexpr int PASSES = NW >= 8 ? 1 : kReduceRanges / NW;   // ranges per wave
-  static_assert(NW == 4 || NW == 8 || NW == 16, "reduction blocks of 256, 512 or 1024 threads");
+__global__ void __launch_bounds__(NT) bwd_reduce_kernel(void* dw, int dw_bf16, const double* part,
+                                                        int hidden, int chunks) {
+  static_assert(NT == kReduceThreads, "one thread per (range, column)");
   constexpr int kMaxLen = kMaxChunks / kReduceRanges;
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int half = NW >= 16 ? wv / 8 : 0;
-  const int c_local = half * 64 + lane;
-  const int col = slice * COLS + c_local;
+  __shared__ double red[kReduceRanges][kReduceCols];
+  const int c_local = threadIdx.x % kReduceCols;
+  const int range = threadIdx.x / kReduceCols;
+  const int col = blockIdx.x * kReduceCols + c_local;
+  const int cb = range * chunks / kReduceRanges, ce = (range + 1) * chunks / kReduceRanges;
+  const int len = ce - cb;
+  // Every load is issued unconditionally, at an index clamped into the chunk rows (no branch
+  // between a load and the next, so all of them are in flight before the first add); the
+  // range's own values are then added in chunk order and the others dropped by a select
+  // (adding +0.0 to a sum that started at +0.0 changes no bit).
+  const int cc = col < hidden ? col : hidden - 1;
+  double v[kMaxLen];
 #pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int range = NW >= 8 ? (wv & 7) : wv + ps * NW;
-    const int cb = range * chunks / kReduceRanges, ce = (range + 1) * chunks / kReduceRanges;
-    const int len = ce - cb;
-    // Every load is issued unconditionally, at an index clamped into the chunk rows (no
-    // branch between a load and the next, so all of them are in flight before the first
-    // add); the range's own values are then added in chunk order and the others dropped
-    // by a select (adding +0.0 to a sum that started at +0.0 changes no bit).
-    const int cc = col < hidden ? col : hidden - 1;
-    double v[kMaxLen];
-#pragma unroll
-    for (int i = 0; i < kMaxLen; ++i) {
-      const int c = cb + i < chunks ? cb + i : chunks - 1;
-      v[i] = part[(int64_t)c * hidden + cc];
-    }
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < kMaxLen; ++i) s += i < len ? v[i] : 0.0;
-    red[range * COLS + c_local] = s;
+  for (int i = 0; i < kMaxLen; ++i) {
+    const int c = cb + i < chunks ? cb + i : chunks - 1;
+    v[i] = part[(int64_t)c * hidden + cc];
   }
-  __syncthreads();
-  if ((int)threadIdx.x < COLS) {
-    const int c = slice * COLS + (int)threadIdx.x;
-    if (c < hidden) {
-      double t = 0.0;
+  double s = 0.0;
 #pragma unroll
-      for (int r = 0; r < kReduceRanges; ++r) t += red[r * COLS + threadIdx.x];
-      const float f = (float)t;
-      if (dw_bf16)
-        static_cast<uint16_t*>(dw)[c] = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
-      else
-        static_cast<float*>(dw)[c] = f;
-    }
+  for (int i = 0; i < kMaxLen; ++i) s += i < len ? v[i] : 0.0;
+  red[range][c_local] = s;
+  __syncthreads();
+  if ((int)threadIdx.x < kReduceCols && col < hidden) {
+    double t = 0.0;
+#pragma unroll
+    for (int r = 0; r < kReduceRanges; ++r) t += red[r][threadIdx.x];
+    const float f = (float)t;
+    if (dw_bf16)
+      static_cast<uint16_t*>(dw)[col] = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+    else
+      static_cast<float*>(dw)[col] = f;
   }
 }
 
@@ -128,11 +114,17 @@ __device__ __forceinline__ void bwd_weff8(const BwdParams& p, int vec, float e[8
   for (int k = 0; k < 8; ++k) e[k] += p.w_bias;
 }
 
+// The row groups' column sums meet in LDS with a pitch of 9 doubles per 16-byte column
+// vector: a wave writing one sum of 64 consecutive vectors then touches every bank once
+// (72-byte lane stride), and consecutive threads reading consecutive columns read
+// consecutive doubles.
+constexpr int kCombPitch = 9;
+
 // Dynamic LDS of a producer launch: the double-buffered dot-product slots, and the row
 // groups' column sums when they meet at the end.
 __host__ __device__ inline size_t bwd_lds_bytes(int g, int wpr, int rb, int nt, int vb) {
   const size_t red = (size_t)2 * g * wpr * rb * sizeof(double);
-  const size_t comb = g > 1 ? (size_t)nt * vb * 8 * sizeof(double) : 0;
+  const size_t comb = g > 1 ? (size_t)nt * vb * kCombPitch * sizeof(double) : 0;
   return red > comb ? red : comb;
 }
 
@@ -333,35 +325,20 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
   } else {
     __syncthreads();                       // the dot-product slots are reused below
     constexpr int GV = TPR * VB;           // column vectors held by one row group
-    double* comb = red;                    // [G][8][GV]: lanes write consecutive doubles
+    double* comb = red;                    // [G][GV][kCombPitch]
 #pragma unroll
     for (int v = 0; v < VB; ++v)
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        comb[((size_t)geo.grp * 8 + k) * GV + v * TPR + lane] = acc[v][k];
+        comb[((size_t)geo.grp * GV + v * TPR + lane) * kCombPitch + k] = acc[v][k];
     __syncthreads();
-    for (int vec = tid; vec < nvec; vec += NT) {
-      double s[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        s[k] = 0.0;
-        for (int gg = 0; gg < G; ++gg) s[k] += comb[((size_t)gg * 8 + k) * GV + vec];
-      }
-      double2* o = reinterpret_cast<double2*>(out + 8 * (int64_t)vec);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = make_double2(s[2 * k], s[2 * k + 1]);
+    for (int col = tid; col < p.hidden; col += NT) {
+      double s = 0.0;
+      for (int gg = 0; gg < G; ++gg) s += comb[((size_t)gg * GV + (col >> 3)) * kCombPitch + (col & 7)];
+      out[col] = s;
     }
   }
 
-}
-
-// The reduction launch: one block of 512 threads per 64 columns.
-template <int NT>
-__global__ void __launch_bounds__(NT) bwd_reduce_kernel(void* dw, int dw_bf16,
-                                                        const double* part, int hidden,
-                                                        int chunks) {
-  __shared__ double red[kReduceRanges * reduce_cols(NT)];
-  reduce_columns<NT>(part, hidden, chunks, blockIdx.x, dw, dw_bf16, red);
 }
 
 // (threads per row, vectors per thread, rows per group per step, threads per block).
