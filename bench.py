@@ -710,7 +710,8 @@ def stream_ceilings(torch, dev, reps: int = 5):
     kernels' 16-byte non-temporal buffer loads and stores at their read:write mixes, 256 MiB
     per stream, caches flushed before every launch, under five access strategies (PROBE_MODES)
     at 1 and 2 blocks of 256 threads per CU.  Returns the best median GB/s (bytes moved) per
-    mix over every strategy, and the best per strategy under `strategies`."""
+    mix over every strategy, the best per strategy under `strategies`, and 2R:2W at 64 MiB and
+    2R:1W at 32 MiB per stream (the fused add's and the backward shard's own sizes)."""
     import ctypes
     lib = ctypes.CDLL(probe_library())
     f = lib.dn_probe_stream
@@ -746,6 +747,28 @@ def stream_ceilings(torch, dev, reps: int = 5):
             best = max(best, mbest)
         out[f"stream_{mix}_GB/s"] = round(best, 1)
     out["strategies"] = strategies
+    # The same mixes at the per-stream sizes of the shorter launches (fused add [8192,4096]:
+    # 64 MiB per stream; the backward at [2048,8192]: 32 MiB), where the ramp and the last
+    # partial round weigh as they do on the kernel; the two launch shapes that win above.
+    for reads, writes, mib in ((2, 2, 64), (2, 1, 32)):
+        m = mib << 20
+        best = 0.0
+        for mode in (0, 1):
+            for blocks in (cus, 2 * cus):
+                ts = []
+                for _ in range(reps):
+                    flush.fill_(1.0)
+                    e0 = timing_event(torch)
+                    e1 = timing_event(torch)
+                    e0.record()
+                    rc = f(*(b.data_ptr() for b in bufs), m, reads, writes, blocks, mode, st)
+                    e1.record()
+                    e1.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe failed ({rc})")
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+                best = max(best, (reads + writes) * m / sorted(ts)[len(ts) // 2] / 1e9)
+        out[f"stream_{reads}r{writes}w_{mib}MiB_GB/s"] = round(best, 1)
     del bufs, flush
     return out
 
@@ -1350,7 +1373,14 @@ def main(argv=None) -> int:
                "train_backward": "stream_2r1w_GB/s"}
         for k, m in mix.items():
             kernels[k]["of_stream_ceiling"] = round(kernels[k]["GB/s"] / ceiling[m], 4)
+        # against a stream of the kernel's own size (256 MiB per stream is the training
+        # shapes' own: [16384,8192] BF16)
+        matched = dict(mix, fused_add_rmsnorm="stream_2r2w_64MiB_GB/s")
+        for k, m in matched.items():
+            kernels[k]["of_size_matched_ceiling"] = round(kernels[k]["GB/s"] / ceiling[m], 4)
         shard = shard_measurement(torch, dev, dn, W)
+        sb = shard["kernels"]["train_backward"]
+        sb["of_size_matched_ceiling"] = round(sb["GB/s"] / ceiling["stream_2r1w_32MiB_GB/s"], 4)
         print("[bench] the other configurations, isolated", file=sys.stderr, flush=True)
         configs = config_measurements(torch, dev, dn, W)
 
