@@ -307,11 +307,13 @@ const char* dn_version(void) { return "dnorm 0.1 (gfx950)"; }
 
 dn_status dn_force_threads_per_row(int threads) {
   switch (threads) {
-    case 0: case 8: case 16: case 32: case 64: case 128: case 256: case 512: case 1024:
+    case 0: case 8: case 16: case 32: case 64: case 128: case 256: case 320: case 448:
+    case 512: case 1024:
       g_force_tpr.store(threads);
       return DN_OK;
     default:
-      return fail(DN_ERR_SHAPE, "threads per row must be 0 or a power of two in [8, 1024]");
+      return fail(DN_ERR_SHAPE,
+                  "threads per row must be 0, a power of two in [8, 1024], 320 or 448");
   }
 }
 

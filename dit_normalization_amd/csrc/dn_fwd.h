@@ -766,20 +766,26 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 //  the 4-vector tiers, a 3-vector tier of the same width takes rows of up to 3*TPR
 //  vectors: no slot left empty, fewer registers, more waves resident (measured at H=3072,
 //  5120, 6144, 10240 and 12288: +1-20 %, the most for plain RMSNorm and the Ada FP8 route,
-//  none slower).  The tiers after the first fourteen are reachable only through
-//  dn_force_threads_per_row.
+//  none slower).  Two tiers of 5 and 7 waves fit the rows of 640 and 896 vectors exactly
+//  (H = 5120, 7168), which a 256-lane tier fills to 83 and 88 %: the empty slots still
+//  cost each wave its epilogue instructions, which weighs on the VALU-heavy 1x128 block FP8
+//  (measured against the 256-lane tiers: block FP8 [22936,5120] +7.6 %, [16384,7168]
+//  +5.5-5.9 %; the plain fused add -0.8 % and +1.4-2.2 %, within noise; 320 x 4 and
+//  448 x 3 at H = 10240 and 448 x 4 at H = 14336 measured -5 to +3 %, not adopted).  The
+//  tiers after the first sixteen are reachable only through dn_force_threads_per_row.
 #define DN_FWD_TIERS(X)                                                         \
   X(0, 8, 1, 4, 256)    X(1, 16, 1, 4, 256)   X(2, 32, 1, 2, 256)              \
   X(3, 64, 1, 2, 256)   X(4, 64, 2, 1, 256)   X(5, 64, 3, 1, 256)              \
   X(6, 64, 4, 1, 256)   X(7, 128, 3, 1, 256)  X(8, 128, 4, 1, 256)             \
-  X(9, 256, 3, 1, 256)  X(10, 256, 4, 1, 256) X(11, 512, 3, 1, 512)            \
-  X(12, 512, 4, 1, 512) X(13, 1024, 4, 1, 1024)                                \
-  X(14, 64, 6, 1, 256)  X(15, 64, 8, 1, 256)  X(16, 64, 12, 1, 256)            \
-  X(17, 64, 16, 1, 256) X(18, 128, 7, 1, 256) X(19, 128, 8, 1, 256)            \
-  X(20, 256, 8, 1, 256) X(21, 512, 8, 1, 512)
+  X(9, 320, 2, 1, 320)  X(10, 256, 3, 1, 256) X(11, 448, 2, 1, 448)            \
+  X(12, 256, 4, 1, 256) X(13, 512, 3, 1, 512) X(14, 512, 4, 1, 512)            \
+  X(15, 1024, 4, 1, 1024)                                                      \
+  X(16, 64, 6, 1, 256)  X(17, 64, 8, 1, 256)  X(18, 64, 12, 1, 256)            \
+  X(19, 64, 16, 1, 256) X(20, 128, 7, 1, 256) X(21, 128, 8, 1, 256)            \
+  X(22, 256, 8, 1, 256) X(23, 512, 8, 1, 512)
 
-constexpr int kFwdTierCount = 22;
-constexpr int kFwdAutoTiers = 14;   // tiers the automatic choice considers
+constexpr int kFwdTierCount = 24;
+constexpr int kFwdAutoTiers = 16;   // tiers the automatic choice considers
 
 // Largest VMAX an input/epilogue combination is built with: the Ada, gated and
 // modulation routes keep five or six 16-byte vectors per column in flight, so they stop

@@ -435,7 +435,7 @@ dn_status dn_fused_qk_rmsnorm_rope(
 
 /* ---------------------------------------------------------------------------------------
  * Test and tuning hook: force the threads that share one row (8, 16, 32, 64, 128, 256,
- * 512 or 1024) in every forward launch of this process; 0 restores the automatic choice
+ * 320, 448, 512 or 1024) in every forward launch of this process; 0 restores the automatic choice
  * by hidden size.  Returns DN_ERR_SHAPE for other values or when the forced count cannot
  * cover hidden in registers (then the automatic choice is used).  Results stay within
  * the documented tolerances either way; bits may change with the row mapping.

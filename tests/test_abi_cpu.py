@@ -281,5 +281,7 @@ def test_gated_residual_checks(lib):
 
 def test_force_threads_per_row(lib):
     assert lib.dn_force_threads_per_row(3) == E_SHAPE
+    assert lib.dn_force_threads_per_row(384) == E_SHAPE
     assert lib.dn_force_threads_per_row(128) == OK
+    assert lib.dn_force_threads_per_row(448) == OK
     assert lib.dn_force_threads_per_row(0) == OK

@@ -144,7 +144,7 @@ def test_kernel_resources_of_the_hot_path():
            "dn::fwd_kernel<1, 0, 256, 4, 1, 256>",      # train_forward [16384,8192]
            "dn::fwd_kernel<1, 1, 128, 4, 1, 256>",      # fused add + static FP8 [8192,4096]
            "dn::fwd_kernel<1, 1, 16, 1, 4, 256>",       # ... per head [8192,32,128]
-           "dn::fwd_kernel<1, 2, 256, 4, 1, 256>",      # block FP8 [16384,7168]
+           "dn::fwd_kernel<1, 2, 448, 2, 1, 448>",      # block FP8 [16384,7168]
            "dn::fwd_kernel<2, 4, 128, 3, 1, 256>",      # gated Ada + FP8 [2520,3072]
            "dn::fwd_kernel<0, 0, 128, 4, 1, 256>",      # rmsnorm [32,4096]
            "dn::bwd_partials_kernel<256, 4, 1, 512, false>",   # backward [16384,8192]

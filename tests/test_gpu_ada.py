@@ -42,7 +42,7 @@ def test_gate_residual_ada_fp8_2520x3072(dn, broadcast):
 
 @pytest.mark.parametrize("broadcast", [False, True])
 @pytest.mark.parametrize("rows,dim", [(2520, 3072), (37, 64), (9, 264), (65, 1024), (5, 4096),
-                                      (3, 8192)])
+                                      (9, 4608), (7, 7168), (3, 8192)])
 def test_ada_rms_norm_bf16(dn, rows, dim, broadcast):
     wl = W.ada(rows=rows, dim=dim, broadcast=broadcast)
     t = wl.tensors

@@ -34,7 +34,7 @@ def check_block(gpu_q, gpu_scale_t, gpu_normed, ref: O.BlockQuant, what: str):
 
 
 @pytest.mark.parametrize("rows,hidden", [(301, 7168), (64, 128), (33, 256), (130, 4096),
-                                         (5, 8192), (17, 16384)])
+                                         (97, 5120), (45, 6656), (5, 8192), (17, 16384)])
 def test_block_quant_against_oracle(dn, rows, hidden):
     wl = W.block_quant(rows=rows, hidden=hidden)
     x, r, w = wl.tensors["x"], wl.tensors["residual"], wl.tensors["w"]

@@ -45,16 +45,17 @@ def test_rmsnorm_32x4096(dn):
 
 
 @pytest.mark.parametrize("hidden", [8, 16, 24, 64, 72, 128, 136, 256, 264, 512, 520, 1000, 1024,
-                                    1536, 2048, 2056, 3072, 4096, 4104, 5120, 6144, 7168, 8192,
-                                    8200, 10240, 12288, 12296, 16384, 24576, 32768])
+                                    1536, 2048, 2056, 3072, 4096, 4104, 5120, 5128, 6144, 6152,
+                                    7168, 7176, 8192, 8200, 10240, 12288, 12296, 16384, 24576,
+                                    32768])
 def test_rmsnorm_every_row_tier(dn, hidden):
     x = W.normal((67, hidden), 11, hidden)
     w = W.normal((hidden,), 12, hidden, mean=1.0, std=0.2)
     check_rmsnorm(dn, x, w, what=f"rmsnorm H={hidden}")
 
 
-@pytest.mark.parametrize("hidden", [128, 1024, 4096, 8192])
-@pytest.mark.parametrize("tpr", [8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("hidden", [128, 1024, 4096, 5120, 7168, 8192])
+@pytest.mark.parametrize("tpr", [8, 16, 32, 64, 128, 256, 320, 448, 512, 1024])
 def test_rmsnorm_forced_row_mapping(dn, hidden, tpr):
     x = W.normal((45, hidden), 13, hidden)
     w = W.normal((hidden,), 14, hidden, mean=1.0, std=0.2)

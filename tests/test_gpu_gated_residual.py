@@ -29,7 +29,7 @@ def dev(t):
 @pytest.mark.parametrize("next_norm", [False, True])
 @pytest.mark.parametrize("per_token", [True, False])
 @pytest.mark.parametrize("rows,hidden", [(37, 8192), (5, 4096), (65, 64), (9, 264), (3, 1024),
-                                         (2, 16384), (2, 24576)])
+                                         (6, 5120), (5, 7168), (2, 16384), (2, 24576)])
 def test_gated_residual(dn, rows, hidden, per_token, next_norm):
     wl = W.gated_residual(rows, hidden, per_token_gate=per_token)
     t = wl.tensors

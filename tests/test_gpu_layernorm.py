@@ -18,8 +18,8 @@ from tests.parity import assert_bf16, assert_bits_equal, assert_fp8, rows_of, sa
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(2520, 3072), (37, 64), (9, 264), (65, 1024), (5, 4096), (3, 8192), (2, 16384),
-          (2, 24576), (1, 32768), (1, 8), (300, 128)]
+SHAPES = [(2520, 3072), (37, 64), (9, 264), (65, 1024), (5, 4096), (11, 4616), (7, 7168),
+          (3, 8192), (2, 16384), (2, 24576), (1, 32768), (1, 8), (300, 128)]
 
 
 @pytest.fixture(scope="module")

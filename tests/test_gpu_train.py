@@ -55,7 +55,8 @@ def dw_oracle(g, x, rstd, w, chunk: int = 1024):
 
 
 @pytest.mark.parametrize("rows,hidden", [(257, 8192), (1, 512), (2, 2048), (7, 6144), (63, 64),
-                                         (129, 1024), (65, 128), (31, 16384)])
+                                         (129, 1024), (65, 128), (31, 16384), (9, 5120),
+                                         (11, 7168)])
 def test_train_forward_residual_fp32_weight(dn, rows, hidden):
     wl = W.train(rows=rows, hidden=hidden)
     t = wl.tensors
