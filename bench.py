@@ -4,12 +4,16 @@
 The metric is the pair the target names: the fused_add_rmsnorm forward and the training
 backward.  One timed round is
   1. fused_add_rmsnorm forward, in place, x/residual BF16 [8192, 4096]      (plain BF16 y)
-  2. training backward, BF16 [16384, 8192]: dx and the deterministic FP32 dw, in one
-     launch, on the h_new and rstd of a training forward with residual (FP32 w = 1 + w0)
-     run once before anything is timed
+  2. training backward, BF16 [16384, 8192]: dx and the deterministic FP32 dw, in one call
+     (two launches: the producers, then the fixed-order reduction), on the h_new and rstd
+     of a training forward with residual (FP32 w = 1 + w0) run once before anything is
+     timed
 and `value` = algorithmic bytes of a round / wall time of a round (K rounds between device
 synchronisations; inputs resident in HBM).  The two shapes alternate, so each kernel's
-inputs have been pushed out of the 256 MB Infinity Cache by the other's traffic.
+inputs have been pushed out of the 256 MB Infinity Cache by the other's traffic.  K is 200
+by default: the first round after a synchronisation waits ~0.1 ms for the queue to start,
+which K = 20 would spread as ~5 us over every round (measured: 194.0, 188.2 and 185.3 us
+per round at K = 20, 100 and 400, without events).
 
 `whole_step` times the whole hot-path step the same way: the pair plus the training
 forward with residual [16384, 8192] and the fused add + static FP8 forward [8192, 4096]
@@ -18,13 +22,14 @@ forward with residual [16384, 8192] and the fused add + static FP8 forward [8192
 Algorithmic bytes count each tensor the definition reads or writes once; the backward's
 FP64 chunk rows in the workspace are not counted.  Inside the timed region only the
 dominant kernel (the backward, the roofline's kernel) is bracketed by HIP events (created
-without the system-scope fence, see HipTimingEvent) on the kernels' stream; the per-kernel
+without the system-scope fence, see HipTimingEvent) on the kernels' stream, in every fourth
+round (50 of the default 200 launches are timed live); the per-kernel
 tables come from K more rounds with an event between every two kernels (each record still
 costs the stream about a microsecond, which the tables' durations include).
 `cpu_baseline` times the FP64 numpy oracle on a bounded sample of the same workload on
 this host's cores.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
 
 Profiler runs pass --step-only (no copy ceiling, no shard shape), so that every library
 dispatch belongs to the step.  Profiler summaries (host only, no GPU):
@@ -112,6 +117,9 @@ def measured_traffic(kernel: str, family: str = "rmsnorm"):
     k = ks.get(kernel)
     return None if k is None else k["traffic_bytes"]
 
+
+# The roofline kernel's live events bracket its launch in every LIVE_EVERY-th timed round.
+LIVE_EVERY = 4
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
 _EVENT_KIND = {"kind": None}
@@ -1188,8 +1196,8 @@ def run_fixed_width_family(a) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
                     help="skip the copy ceiling and the shard shape (profiler runs: every "
@@ -1282,15 +1290,18 @@ def main(argv=None) -> int:
             calls[n]()
         mark(len(names))
 
-    def rounds(names, k, events_per_round=False, only=None):
-        evs = [[timing_event(torch) for _ in range(len(names) + 1)] for _ in range(k)] \
-            if events_per_round else [None] * k
+    def rounds(names, k, events_per_round=False, only=None, every=1):
+        """K rounds between synchronisations; with events_per_round, every `every`-th round
+        carries events (the others none).  Returns the wall time and the sampled rounds'
+        events."""
+        evs = [[timing_event(torch) for _ in range(len(names) + 1)]
+               if events_per_round and i % every == 0 else None for i in range(k)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e in evs:
             run(names, e, only)
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, evs
+        return time.perf_counter() - t0, [e for e in evs if e is not None]
 
     def durations(names, evs):
         return {n: [e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs] for j, n in enumerate(names)}
@@ -1318,11 +1329,11 @@ def main(argv=None) -> int:
     dom = "train_backward"
     if not a.step_only:
         # Timed region: K rounds of the metric's pair between synchronisations (wall clock);
-        # only the dominant kernel (the backward) is bracketed by events, since even a
-        # fence-free event record costs the stream about a microsecond.
+        # only the dominant kernel (the backward) is bracketed by events, in every fourth
+        # round, since even a fence-free event record costs the stream about a microsecond.
         print(f"[bench] timing {a.steps} rounds of the pair", file=sys.stderr, flush=True)
         di = PAIR_KERNELS.index(dom)
-        wall, evs = rounds(PAIR_KERNELS, a.steps, True, only=(di, di + 1))
+        wall, evs = rounds(PAIR_KERNELS, a.steps, True, only=(di, di + 1), every=LIVE_EVERY)
         dom_live = [e[di].elapsed_time(e[di + 1]) * 1e-3 for e in evs]
         # The pair's per-kernel breakdown: K more rounds with an event between the kernels.
         _, evs = rounds(PAIR_KERNELS, a.steps, True)
