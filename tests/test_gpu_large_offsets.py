@@ -123,3 +123,30 @@ def test_training_forward_and_backward_beyond_4gib(dn):
     assert torch.equal(bits_of(dh), bits_of(dt)), "dx past 2^32 bytes differs"
     assert_dx(dt, bref, "dx past 2^32 bytes")
     assert_dw(dw, REPS * bref.dw_exact, f"dw over {ROWS} rows")
+
+
+@pytest.mark.parametrize("hidden", [64, 4096])
+def test_rmsnorm_and_fused_add_at_the_largest_row_stride(dn, hidden):
+    """Row strides of 2^24 elements, the most the boundary accepts: 32 rows of a narrow tier
+    share one buffer descriptor spanning 1 GiB, and a 40-row matrix spans 1.25 GiB."""
+    stride, rows = 1 << 24, 40
+    xb = W.normal((rows, hidden), 93, hidden)
+    rb = W.normal((rows, hidden), 94, hidden)
+    w = W.normal((hidden,), 95, hidden, mean=1.0, std=0.1)
+    wd = w.to("cuda")
+
+    def strided(t):
+        big = torch.zeros((rows, stride), dtype=torch.bfloat16, device="cuda")
+        big[:, :hidden] = t.to("cuda")
+        return big[:, :hidden]
+
+    x, y = strided(xb), strided(torch.zeros_like(xb))
+    dn.dn_rmsnorm(x, wd, 1e-6, out=y)
+    ref = O.rmsnorm(values(xb), values(w), 0.0, 1e-6)
+    assert_bf16(y.cpu(), ref.y_exact, f"rmsnorm at stride 2^24, H={hidden}")
+    del x, y
+    x, r = strided(xb), strided(rb)
+    dn.dn_fused_add_rmsnorm(x, r, wd, 1e-6)
+    fref = O.fused_add_rmsnorm(values(xb), values(rb), values(w), 0.0, 1e-6)
+    assert_bits_equal(r.cpu(), fref.h_new, f"h_new at stride 2^24, H={hidden}")
+    assert_bf16(x.cpu(), fref.norm.y_exact, f"fused add y at stride 2^24, H={hidden}")
