@@ -427,7 +427,7 @@ def summarize_trace(stats_csv: str) -> int:
 
 def host_cores() -> int:
     """Host threads the CPU baseline uses: the CPUs this process may run on, at most 16 (one
-    GPU's share of the GPU machine's host)."""
+    GPU's share of an 8-GPU node's host cores)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
