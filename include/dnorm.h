@@ -350,8 +350,9 @@ dn_status dn_fused_rmsnorm_silu(void* out, int64_t out_stride, int output_fp8,
 
 /* ---------------------------------------------------------------------------------------
  * gated_residual_rmsnorm / gated_residual_next_rmsnorm
- *   ([norm docs] Fixed-Width Fused Norms: "blend a normalized branch into the stream";
- *    "plus the next RMSNorm in one launch")
+ *   ([norm docs] Fixed-Width Fused Norms: a normalised branch is blended into the
+ *    residual stream; the second call also normalises the result for the next layer, in
+ *    the same launch)
  *   The pages give no formula; the reading implemented:
  *     n = (branch * r_b) * FP32(w + w_bias)            (rmsnorm of the branch, unrounded)
  *     residual <- h = BF16(FMA(gate, n, residual))     (one FP32 rounding, then BF16)
@@ -380,7 +381,8 @@ dn_status dn_gated_residual_next_rmsnorm(void* out, int64_t out_stride,
 
 /* ---------------------------------------------------------------------------------------
  * rmsnorm_sigmoid_gate   ([norm docs] Fixed-Width Fused Norms: rmsnorm_sigmoid_gate)
- *   The pages name only "per-head RMSNorm and sigmoid gate, in place, for head dim 64";
+ *   The pages name only a per-head RMSNorm followed by a sigmoid gate, done in place, at
+ *   head dim 64;
  *   the reading implemented: rows are heads (a [tokens, heads, head_dim] tensor passed as
  *   rows = tokens*heads), y = (x * r) * FP32(w + w_bias) as rmsnorm, then
  *   x <- BF16(y * sigmoid(gate)), gate BF16 of x's shape (own row stride).  w: BF16 or FP32
