@@ -784,7 +784,7 @@ def stream_ceilings(torch, dev, reps: int = 5):
 SHARD = (2048, 8192)
 
 
-def shard_measurement(torch, dev, dn, W, reps: int = 10):
+def shard_measurement(torch, dev, dn, W, reps: int = 50):
     """The training forward + backward at one GPU's share of an 8-way data-parallel C4
     batch ([2048, 8192]); a 1 GiB buffer is overwritten before every launch so that the
     32 MiB tensors come from HBM, not from the Infinity Cache."""
@@ -824,7 +824,7 @@ def shard_measurement(torch, dev, dn, W, reps: int = 10):
                                           f"{reps} cold launches", "kernels": out}
 
 
-def isolated(torch, fn, nbytes: int, flush, reps: int = 20):
+def isolated(torch, fn, nbytes: int, flush, reps: int = 50):
     """Median/p10/p90 of `reps` launches of `fn`, each after a 1 GiB write that evicts L2 and
     the 256 MB Infinity Cache, so every launch streams its inputs from HBM."""
     fn()
@@ -842,7 +842,7 @@ def isolated(torch, fn, nbytes: int, flush, reps: int = 20):
     return dict(st, bytes=nbytes, **{"GB/s": round(gbs, 1)}, frac=round(gbs / HBM_PEAK_GBS, 4))
 
 
-def config_measurements(torch, dev, dn, W, reps: int = 20):
+def config_measurements(torch, dev, dn, W, reps: int = 50):
     """The other configurations of the hot path, each launch isolated (caches evicted):
     rmsnorm [32,4096] (launch-bound), fused add + static FP8 per head [8192,32,128] and with
     the Gemma weight offset, 1x128 block FP8 [16384,7168] (with and without normed_out), and
