@@ -695,8 +695,12 @@ PROBE_LIB = os.path.join(ROOT, "probe", "libdnprobe.so")
 
 def probe_library(rebuild: bool = False) -> str:
     """Path of the stream-ceiling probe library (probe/stream_probe.hip, a measurement aid
-    outside the norm library), compiled with hipcc for gfx950 when it is missing."""
-    if rebuild or not os.path.exists(PROBE_LIB):
+    outside the norm library), compiled with hipcc for gfx950 when it is missing or older
+    than its sources (the probe shares the norm kernels' memory helpers, dn_device.h)."""
+    srcs = [PROBE_SRC, os.path.join(ROOT, "dit_normalization_amd", "csrc", "dn_device.h")]
+    stale = not os.path.exists(PROBE_LIB) or \
+        os.path.getmtime(PROBE_LIB) < max(os.path.getmtime(s) for s in srcs)
+    if rebuild or stale:
         import subprocess
 
         from dit_normalization_amd import build as B
