@@ -120,6 +120,13 @@ __device__ __forceinline__ void bwd_weff8(const BwdParams& p, int vec, float e[8
 // consecutive doubles.
 constexpr int kCombPitch = 9;
 
+// Cache policy of the chunk-row stores: device scope (sc1), so the rows are written through
+// to memory as they are stored rather than left dirty in the XCD's L2 for the kernel's end
+// to write back; not non-temporal, which kept them from the cache the reduction reads
+// through.  Measured against the default policy: [2048, 8192] +2.9 %, [4096, 8192] +2.7 %,
+// [16384, 8192] +1.2 % (80 interleaved launches); non-temporal as well -4 % and -1 %.
+constexpr int kChunkStorePolicy = 16;
+
 // Dynamic LDS of a producer launch: the double-buffered dot-product slots, and the row
 // groups' column sums when they meet at the end.
 __host__ __device__ inline size_t bwd_lds_bytes(int g, int wpr, int rb, int nt, int vb) {
@@ -312,14 +319,17 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
 
   // The chunk's column sums: add the row groups' sums in group order, write one row.
   double* out = p.part + (int64_t)chunk * p.hidden;
+  const rsrc_t orsrc = make_rsrc(out, (uint32_t)p.hidden * 8u);
   if constexpr (G == 1) {
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int idx = v * TPR + lane;
       if (idx < nvec) {
-        double2* o = reinterpret_cast<double2*>(out + 8 * (int64_t)idx);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = make_double2(acc[v][2 * k], acc[v][2 * k + 1]);
+        for (int k = 0; k < 4; ++k)
+          bstore16_p<kChunkStorePolicy>(
+              orsrc, (uint32_t)(idx * 64 + 16 * k),
+              __builtin_bit_cast(v4u, make_double2(acc[v][2 * k], acc[v][2 * k + 1])));
       }
     }
   } else {
@@ -335,7 +345,7 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
     for (int col = tid; col < p.hidden; col += NT) {
       double s = 0.0;
       for (int gg = 0; gg < G; ++gg) s += comb[((size_t)gg * GV + (col >> 3)) * kCombPitch + (col & 7)];
-      out[col] = s;
+      bstore8_p<kChunkStorePolicy>(orsrc, (uint32_t)col * 8u, __builtin_bit_cast(v2u, s));
     }
   }
 

@@ -127,8 +127,8 @@ constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 // measured +4.7 % on the fused add [8192,4096], +3.2 % with its static FP8 output, +1.3 %
 // on the training backward and on block FP8, -0.6 % on the training forward, and within
 // +-1.2 % on the other families (60 and 40 interleaved launches).  Side arrays written a
-// few bytes at a time (rstd, block scales, the backward's chunk rows) keep the default
-// policy: their lines fill in L2 from many stores.
+// few bytes at a time (rstd, block scales) keep the default policy: their lines fill in L2
+// from many stores; the backward's chunk rows take device scope alone (dn_bwd.h).
 #ifndef DN_LOAD_POLICY
 #define DN_LOAD_POLICY 2
 #endif
@@ -154,6 +154,19 @@ __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const v4u& v) {
   __builtin_amdgcn_raw_buffer_store_b128(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off,
       0, kStorePolicy);
+}
+// Stores with an explicit cache policy (the backward's chunk rows, see dn_bwd.h).
+template <int POLICY>
+__device__ __forceinline__ void bstore16_p(rsrc_t r, uint32_t off, const v4u& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off,
+      0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ void bstore8_p(rsrc_t r, uint32_t off, const v2u& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(
+      __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, off,
+      0, POLICY);
 }
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, const v2u& v) {
   __builtin_amdgcn_raw_buffer_store_b64(
