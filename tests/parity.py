@@ -168,3 +168,26 @@ def assert_block_quant(gpu_codes: torch.Tensor, gpu_scale_t, ref, what: str):
                            f"{ref.scale[tuple(np.argwhere(~scale_ok)[0])]!r})"
     assert codes_ok.all(), f"{what}: {(~codes_ok).sum()} FP8 codes off " \
                            f"(first at {np.argwhere(~codes_ok)[0]})"
+
+
+def assert_bf16_nonfinite(gpu, ref_exact, what, mag=None):
+    """NaN and infinities exactly where the oracle's IEEE evaluation has them; every finite
+    element through assert_bf16."""
+    g = values(gpu).reshape(ref_exact.shape)
+    r = ref_exact
+    assert (np.isnan(g) == np.isnan(r)).all(), f"{what}: NaN positions differ"
+    inf = np.isinf(r)
+    assert (g[inf] == r[inf]).all() and (np.isinf(g) == inf).all(), f"{what}: infinities differ"
+    fin = np.isfinite(r)
+    assert_bf16(gpu.reshape(-1)[torch.as_tensor(np.flatnonzero(fin), device=gpu.device)],
+                r[fin], what, mag=None if mag is None else mag[fin])
+
+
+def assert_fp8_nonfinite(q, ref, what):
+    """NaN codes exactly where the oracle's value is NaN; every other code equal (or a
+    neighbour at a flagged tie), infinities saturating to +-448."""
+    g = bits8(q).reshape(ref.q.shape)
+    nan_ref = np.isnan(ref.v)
+    assert (((g & 0x7F) == 0x7F) == nan_ref).all(), f"{what}: e4m3 NaN codes"
+    ok = F.codes_equal_e4m3(g, ref.q) | ref.tie
+    assert ok[~nan_ref].all(), f"{what}: e4m3 codes"

@@ -15,7 +15,7 @@ from oracle import layernorm as L
 from oracle import rmsnorm as O
 from oracle import silu as S
 from tests.conftest import bits8, values
-from tests.parity import assert_bf16, block_quant_ok
+from tests.parity import assert_bf16_nonfinite, assert_fp8_nonfinite, block_quant_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -39,27 +39,6 @@ def with_specials(rows, hidden, seed):
     x[3, hidden // 2] = float("nan")
     x[4, 0], x[4, 1] = float("inf"), float("-inf")
     return x.to(torch.bfloat16)
-
-
-def assert_bf16_nonfinite(gpu, ref_exact, what, mag=None):
-    g = values(gpu).reshape(ref_exact.shape)
-    r = ref_exact
-    assert (np.isnan(g) == np.isnan(r)).all(), f"{what}: NaN positions differ"
-    inf = np.isinf(r)
-    assert (g[inf] == r[inf]).all() and (np.isinf(g) == inf).all(), f"{what}: infinities differ"
-    fin = np.isfinite(r)
-    assert_bf16(gpu.reshape(-1)[torch.as_tensor(np.flatnonzero(fin), device=gpu.device)],
-                r[fin], what, mag=None if mag is None else mag[fin])
-
-
-def assert_fp8_nonfinite(q, ref, what):
-    """NaN codes exactly where the oracle's value is NaN; every other code equal (or a
-    neighbour at a flagged tie), infinities saturating to +-448."""
-    g = bits8(q).reshape(ref.q.shape)
-    nan_ref = np.isnan(ref.v)
-    assert (((g & 0x7F) == 0x7F) == nan_ref).all(), f"{what}: e4m3 NaN codes"
-    ok = F.codes_equal_e4m3(g, ref.q) | ref.tie
-    assert ok[~nan_ref].all(), f"{what}: e4m3 codes"
 
 
 @pytest.mark.parametrize("hidden", [128, 4096])
