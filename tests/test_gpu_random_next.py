@@ -1,0 +1,249 @@
+"""Seeded random shapes for the other row engines: block FP8, the Ada calls, the gated residual
+(+ next), RMSNorm + SiLU, the per-head sigmoid gate, the three DiT modes and the QK RMSNorm +
+3-D RoPE.  Each seed draws the shape (and the call's options), builds the inputs from the
+workload generators and checks the kernel against the FP64 oracle with the standard gates.
+DN_RANDOM_SHAPES_NEXT (default 8) sets the number of seeds per test."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import gated as G
+from oracle import layernorm as L
+from oracle import qk_rope as Q
+from oracle import rmsnorm as O
+from oracle import silu as S
+from tests.conftest import values
+from tests.parity import assert_bf16, assert_bits_equal, assert_block_quant, assert_fp8
+
+pytestmark = pytest.mark.gpu
+
+CASES = list(range(int(os.environ.get("DN_RANDOM_SHAPES_NEXT", "8"))))
+MAX_ELEMS = 1 << 20           # per tensor, so the oracle stays quick
+
+
+@pytest.fixture(scope="module")
+def dn():
+    from dit_normalization_amd import dnorm
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return dnorm
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def rng_of(test: int, case: int):
+    return np.random.default_rng(7000 + 1000 * test + case)
+
+
+def rows_for(rng, hidden: int, cap: int = 300) -> int:
+    return int(rng.integers(1, max(2, min(cap, MAX_ELEMS // hidden)) + 1))
+
+
+def padded(t, pad):
+    """A device view of t with `pad` extra elements at the end of every row."""
+    if pad == 0:
+        return dev(t)
+    big = torch.zeros((t.shape[0], t.shape[1] + pad), dtype=t.dtype, device="cuda")
+    big[:, :t.shape[1]] = dev(t)
+    return big[:, :t.shape[1]]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_block_quant(dn, case):
+    rng = rng_of(0, case)
+    hidden = 128 * int(rng.integers(1, 129))
+    rows = rows_for(rng, hidden)
+    pad = 8 * int(rng.integers(0, 3))
+    with_normed = bool(rng.integers(0, 2))
+    wl = W.block_quant(rows=rows, hidden=hidden, seed=100 + case)
+    x, r, w = wl.tensors["x"], wl.tensors["residual"], wl.tensors["w"]
+    xd, rd = padded(x, pad), padded(r, pad)
+    normed = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda") \
+        if with_normed else None
+    q, bs = dn.dn_fused_add_rmsnorm_fp8_block_quant(xd, rd, dev(w), 1e-6, normed_out=normed)
+    ref = O.fused_add_rmsnorm_fp8_block_quant(values(x), values(r), values(w), 0.0, 1e-6)
+    what = f"block quant case {case}: [{rows},{hidden}] pad {pad}"
+    assert_bits_equal(rd, ref.h_new, f"h_new {what}")
+    assert_block_quant(q, bs.t()[:rows], ref, what)
+    assert (bs[:, rows:].cpu() == 0).all(), f"scale padding {what}"
+    if with_normed:
+        assert_bf16(normed, ref.normed_exact, f"normed_out {what}")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_ada(dn, case):
+    rng = rng_of(1, case)
+    dim = 8 * int(rng.integers(1, 1025))
+    rows = rows_for(rng, dim, cap=200)
+    broadcast = bool(rng.integers(0, 2))
+    wl = W.ada(rows=rows, dim=dim, seed=200 + case, broadcast=broadcast)
+    t = wl.tensors
+    what = f"Ada case {case}: [{rows},{dim}] broadcast {broadcast}"
+    w = W.normal((dim,), 200 + case, 9, mean=1.0, std=0.1)
+    out, gout = dn.dn_ada_rms_norm(dev(t["x"]), dev(w), dev(t["style"]), 1e-6)
+    a, _ = O.ada_rms_norm(values(t["x"]), values(w), values(t["style"]), 1e-6)
+    assert_bf16(out, a.o_exact, f"BF16 {what}", mag=a.o_mag)
+    assert_bits_equal(gout, a.gate_out, f"gate_out {what}")
+    rd = dev(t["residual"])
+    _, q, gout8 = dn.dn_gate_residual_ada_norm_fp8(rd, dev(t["x"]), dev(t["gate"]), dev(t["w"]),
+                                                    dev(t["style"]), 0.04, 1e-6)
+    g, ref = O.gate_residual_ada_norm_fp8(values(t["residual"]), values(t["x"]),
+                                          values(t["gate"]), values(t["w"]), values(t["style"]),
+                                          0.04, 1e-6)
+    assert_bits_equal(rd, g.h, f"residual {what}")
+    assert_bits_equal(gout8, g.gate_out, f"gated gate_out {what}")
+    assert_fp8(q, ref.q, ref.tie, f"FP8 {what}")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_gated_residual(dn, case):
+    rng = rng_of(2, case)
+    hidden = 8 * int(rng.integers(1, 4097))
+    rows = rows_for(rng, hidden, cap=200)
+    per_token = bool(rng.integers(0, 2))
+    next_norm = bool(rng.integers(0, 2))
+    wl = W.gated_residual(rows, hidden, seed=300 + case, per_token_gate=per_token)
+    t = wl.tensors
+    r = dev(t["residual"])
+    gate = dev(t["gate"]) if per_token else dev(t["gate"][0])
+    if next_norm:
+        _, y = dn.dn_gated_residual_next_rmsnorm(dev(t["branch"]), r, gate, dev(t["w"]),
+                                                 dev(t["w_next"]), 1e-6)
+    else:
+        dn.dn_gated_residual_rmsnorm(dev(t["branch"]), r, gate, dev(t["w"]), 1e-6)
+    ref = G.gated_residual_rmsnorm(values(t["branch"]), values(t["residual"]), values(t["gate"]),
+                                   values(t["w"]), 1e-6,
+                                   next_w=values(t["w_next"]) if next_norm else None)
+    what = f"gated residual case {case}: [{rows},{hidden}] per-token {per_token} next {next_norm}"
+    assert_bf16(r, ref.h_exact, f"h {what}", mag=ref.h_mag)
+    if next_norm:
+        assert_bf16(y, ref.y_exact, f"next {what}", mag=ref.y_mag)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_silu(dn, case):
+    rng = rng_of(3, case)
+    hidden = 8 * int(rng.integers(1, 513))
+    tokens = rows_for(rng, hidden, cap=2000)
+    wl = W.rmsnorm_silu(tokens, hidden, seed=400 + case)
+    t = wl.tensors
+    what = f"silu case {case}: [{tokens},{hidden}]"
+    out = dn.dn_fused_rmsnorm_silu(dev(t["x"]), dev(t["w"]), 1e-6)
+    r = S.fused_rmsnorm_silu(values(t["x"]), values(t["w"]), 1e-6)
+    assert_bf16(out, r.s_exact, f"BF16 {what}", mag=r.mag)
+    q = dn.dn_fused_rmsnorm_silu(dev(t["x"]), dev(t["w"]), 1e-6, output_fp8=True,
+                                 scale=wl.params["scale"])
+    _, ref = S.fused_rmsnorm_silu_fp8(values(t["x"]), values(t["w"]), wl.params["scale"], 1e-6)
+    assert_fp8(q, ref.q, ref.tie, f"e4m3 {what}")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_sigmoid_gate(dn, case):
+    rng = rng_of(4, case)
+    head_dim = 8 * int(rng.integers(1, 129))
+    heads = int(rng.integers(1, 17))
+    tokens = rows_for(rng, heads * head_dim, cap=200)
+    with_weight = bool(rng.integers(0, 2))
+    wl = W.sigmoid_gate(tokens, heads, head_dim, seed=500 + case)
+    t = wl.tensors
+    x = dev(t["x"]).reshape(tokens, heads, head_dim)
+    dn.dn_rmsnorm_sigmoid_gate(x, dev(t["gate"]).reshape(tokens, heads, head_dim), 1e-6,
+                               weight=dev(t["w"]) if with_weight else None)
+    r = S.rmsnorm_sigmoid_gate(values(t["x"]).reshape(-1, head_dim),
+                               values(t["gate"]).reshape(-1, head_dim),
+                               values(t["w"]) if with_weight else None, 1e-6)
+    assert_bf16(x.reshape(-1, head_dim), r.o_exact,
+                f"sigmoid gate case {case}: [{tokens},{heads},{head_dim}] weight {with_weight}",
+                mag=r.mag)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_dit_modes(dn, case):
+    rng = rng_of(5, case)
+    hidden = 8 * int(rng.integers(1, 1025))
+    rows = rows_for(rng, 6 * hidden, cap=200)
+    wl = W.dit(rows=rows, hidden=hidden, seed=600 + case)
+    t, p = wl.tensors, wl.params
+    temb = dev(t["temb"])
+    ch = {name: temb[:, k * hidden:(k + 1) * hidden] for k, name in enumerate(W.DIT_CHUNKS)}
+    x, res = dev(t["x"]), dev(t["residual"])
+    what = f"DiT case {case}: [{rows},{hidden}]"
+
+    ro, no = dn.dn_fused_dit_gate_residual_layernorm_gamma_beta(
+        x, res, ch["gate"], dev(t["gamma"]), dev(t["beta"]), 1e-6, gate_bias=p["gate_bias"])
+    ref = L.dit_gate_residual_layernorm_gamma_beta(
+        values(t["residual"]), values(t["x"]), values(t["gate"]), values(t["gamma"]),
+        values(t["beta"]), p["gate_bias"], 1e-6)
+    assert_bits_equal(ro, ref.residual_out, f"gamma/beta residual_out {what}")
+    assert_bf16(no, ref.o_exact, f"gamma/beta {what}", mag=ref.mag)
+
+    ro, no = dn.dn_fused_dit_gate_residual_layernorm_scale_shift(
+        x, res, ch["gate"], ch["scale"], ch["shift"], 1e-6, gate_bias=p["gate_bias"],
+        scale_bias=p["scale_bias"], shift_bias=p["shift_bias"])
+    ref = L.dit_gate_residual_layernorm_scale_shift(
+        values(t["residual"]), values(t["x"]), values(t["gate"]), values(t["scale"]),
+        values(t["shift"]), p["gate_bias"], p["scale_bias"], p["shift_bias"], 1e-6)
+    assert_bits_equal(ro, ref.residual_out, f"scale/shift residual_out {what}")
+    assert_bf16(no, ref.o_exact, f"scale/shift {what}", mag=ref.mag)
+
+    ro, no = dn.dn_fused_dit_residual_layernorm_scale_shift(
+        x, ch["scale"], ch["shift"], res, 1e-6, scale_bias=p["scale_bias"],
+        shift_bias=p["shift_bias"])
+    ref = L.dit_residual_layernorm_scale_shift(
+        values(t["x"]), values(t["scale"]), values(t["shift"]), values(t["residual"]),
+        p["scale_bias"], p["shift_bias"], 1e-6)
+    assert_bits_equal(ro, ref.residual_out, f"residual residual_out {what}")
+    assert_bf16(no, ref.o_exact, f"residual scale/shift {what}", mag=ref.mag)
+
+
+def draw_rope(rng):
+    head_dim = int(rng.choice([64, 128, 256]))
+    half = head_dim // 2
+    a = int(rng.integers(0, half + 1))
+    b = int(rng.integers(0, half - a + 1))
+    channels = (2 * a, 2 * b, head_dim - 2 * a - 2 * b)
+    heads = [int(rng.integers(1, 33)) for _ in range(3)]
+    ppf, pph, ppw = (int(rng.integers(1, 6)) for _ in range(3))
+    seq = ppf * pph * ppw
+    width = sum(heads) * head_dim
+    batch = int(rng.integers(1, max(2, min(4, MAX_ELEMS // (seq * width)) + 1)))
+    return ppf, pph, ppw, batch, heads, head_dim, channels
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_qk_rope(dn, case):
+    rng = rng_of(6, case)
+    ppf, pph, ppw, batch, (nq, nk, nv), hd, chn = draw_rope(rng)
+    interleave = bool(rng.integers(0, 2))
+    yarn = bool(rng.integers(0, 2))
+    factor, low, high, af = (4.0, 2.0, 10.0, 1.2) if yarn else (1.0, 0.0, 0.0, 1.0)
+    wl = W.qk_rope(ppf, pph, ppw, batch, nq, nk, nv, hd, chn, seed=700 + case)
+    t, p = wl.tensors, wl.params
+    what = (f"qk rope case {case}: grid {ppf}x{pph}x{ppw} batch {batch} heads {nq}/{nk}/{nv} "
+            f"hd {hd} channels {chn} interleave {interleave} yarn {yarn}")
+
+    def call(fp8):
+        return dn.dn_fused_qk_rmsnorm_rope(
+            dev(t["qkv"]), dev(t["q_weight"]), dev(t["k_weight"]), nq, nk, nv, hd, ppf, pph, ppw,
+            chn, p["eps"], base=p["base"], interleave=interleave, yarn_factor=factor,
+            yarn_low=low, yarn_high=high, attention_factor=af, output_fp8=fp8,
+            output_quant_scale=p["output_scale"], v_quant_scale=p["v_scale"])
+
+    r = Q.qk_rmsnorm_rope(values(t["qkv"]), values(t["q_weight"]), values(t["k_weight"]), nq, nk,
+                          nv, hd, chn, ppf, pph, ppw, p["eps"], p["base"], interleave, factor,
+                          low, high, af, True)
+    qo, ko, vo = call(False)
+    assert_bits_equal(vo, r.v, f"V copy {what}")
+    assert_bf16(qo, r.q_exact, f"Q {what}", mag=r.q_mag)
+    assert_bf16(ko, r.k_exact, f"K {what}", mag=r.k_mag)
+    q8, k8, v8 = Q.qk_rmsnorm_rope_fp8(r, p["output_scale"], p["v_scale"])
+    qo, ko, vo = call(True)
+    assert_fp8(qo, q8.q, q8.tie, f"Q e4m3 {what}")
+    assert_fp8(ko, k8.q, k8.tie, f"K e4m3 {what}")
+    assert_fp8(vo, v8.q, v8.tie, f"V e4m3 {what}")
