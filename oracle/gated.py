@@ -12,6 +12,9 @@ The pages give no formula.  Reading implemented (the plainest that the names sup
                                                   shared by every token)
     residual <- BF16(h)
     next:  y = RMSNorm(BF16(h), w_next)          (the norm sees the stored BF16 stream)
+Tolerances (h_mag, y_mag feed the cancellation-aware BF16 gate: one ulp, or within 2^-21 of
+the magnitude): h_mag = |residual| + |gate * n|; y_mag = |y|, widened where h's band crosses
+a BF16 rounding midpoint (below).
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import bf16_round
-from .rmsnorm import rmsnorm
+from .rmsnorm import effective_weight, rmsnorm
 
 
 @dataclass
@@ -48,13 +51,17 @@ def gated_residual_rmsnorm(branch, residual, gate, w, eps: float = 1e-6, bias: f
     if next_w is not None:
         nx = rmsnorm(h, next_w, next_bias, eps)
         y_exact, rn = nx.y_exact, nx.rstd
-        # An FP32 evaluation of h may round to the other BF16 neighbour where h sits within
-        # 2^-20 of its term magnitude from a rounding midpoint; the next norm then sees a
-        # stream one ulp away there, which moves that element's y by one more ulp.  Such
-        # elements get a magnitude that admits two ulps; the others one.
+        # An FP32 evaluation of h lands within 2^-20 of its term magnitude h_mag of the exact
+        # value (the h gate admits that much).  Where that band reaches past a BF16 rounding
+        # midpoint, the stored h may be another BF16 number than the oracle's -- one ulp
+        # away next to a midpoint, several where the sum cancels far below its terms -- and
+        # the next norm sees that stream.  Such elements admit the band carried through the
+        # next norm (h_mag * r * |w_eff|, the deviation of h times the factor the norm
+        # applies) plus two ulps of y; the others one ulp.
         band = 2.0 ** -20 * h_mag
         near = bf16_round(h_exact - band) != bf16_round(h_exact + band)
-        y_mag = np.abs(y_exact) * np.where(near, 2.0 ** 15, 1.0)
+        carried = 2.0 * h_mag * nx.r64[:, None] * np.abs(effective_weight(next_w, next_bias))
+        y_mag = np.where(near, np.abs(y_exact) * 2.0 ** 15 + carried, np.abs(y_exact))
     return GatedResidual(h_exact, h, h_mag, y_exact, y_mag, nb.rstd, rn)
 
 

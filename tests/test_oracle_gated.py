@@ -3,6 +3,7 @@ the gate = 0 and gate = 1 reductions, and broadcast gate == repeated gate rows."
 from __future__ import annotations
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import formats as F
@@ -64,3 +65,52 @@ def test_next_norm_band_marks_only_elements_at_rounding_ties():
     _, e = np.frexp(np.abs(out.h_exact))
     ulp = np.ldexp(1.0, e - 8)                 # BF16 spacing in |h|'s binade
     assert (np.abs(mid_dist - ulp / 2)[wide] <= 2.0 ** -19 * out.h_mag[wide] + 1e-30).all()
+
+
+def _bf16_tensor(v):
+    return torch.from_numpy(F.f64_to_bf16_bits(v).view(np.int16)).view(torch.bfloat16)
+
+
+def _fp32_gated_next(b, r, g, w, w2, eps):
+    """An FP32 evaluation of the gated residual + next norm, in the order a kernel takes:
+    rstd of the branch rounded to FP32, n = FP32(FP32(b * rstd) * w), h = BF16(FMA(g, n, r))
+    (the FMA's product is exact in FP64, its sum rounded to FP64 and then to FP32), the next
+    rstd from the BF16 h, y = BF16(FP32(FP32(h * rstd2) * w2))."""
+    f32 = np.float32
+    e = float(f32(eps))
+    rs = (1.0 / np.sqrt(np.mean(b * b, axis=1) + e)).astype(f32)
+    n = ((b.astype(f32) * rs[:, None]).astype(f32) * w.astype(f32)).astype(f32)
+    h = F.bf16_round((g * n.astype(np.float64) + r).astype(f32).astype(np.float64))
+    r2 = (1.0 / np.sqrt(np.mean(h * h, axis=1) + e)).astype(f32)
+    y = ((h.astype(f32) * r2[:, None]).astype(f32) * w2.astype(f32)).astype(f32)
+    return h, F.bf16_round(y.astype(np.float64))
+
+
+def test_next_norm_gate_admits_an_fp32_evaluation_where_h_cancels():
+    """Residuals set to -BF16(gate * n) make h = residual + gate * n cancel far below its
+    terms on many elements.  There an FP32 evaluation of h is off by many of h's ulps (within
+    h's own gate), and the next norm carries that into y.  The oracle's y band must admit
+    such an evaluation, which the band of a one-ulp neighbour alone does not; it must still
+    reject y moved by eight times the carried band."""
+    from tests.parity import assert_bf16
+    b, r, g = bf((64, 1024)), bf((64, 1024)), bf((64, 1024), 0.5)
+    w, w2 = bf(1024, 0.1, 1.0), bf(1024, 0.1, 1.0)
+    n = O.rmsnorm(b, w, 0.0, 1e-6).y_exact
+    r[:, :512] = F.bf16_round(-g[:, :512] * n[:, :512])
+    out = G.gated_residual_rmsnorm(b, r, g, w, 1e-6, next_w=w2)
+    cancel = np.abs(out.h_exact) < 2.0 ** -14 * out.h_mag
+    assert cancel.sum() >= 100
+    h, y = _fp32_gated_next(b, r, g, w, w2, 1e-6)
+    assert (h != out.h)[cancel].sum() >= 50           # h itself moved there
+    assert_bf16(_bf16_tensor(h), out.h_exact, "FP32 h", mag=out.h_mag)
+    assert_bf16(_bf16_tensor(y), out.y_exact, "FP32 next-norm y", mag=out.y_mag)
+    band = 2.0 ** -20 * out.h_mag
+    near = F.bf16_round(out.h_exact - band) != F.bf16_round(out.h_exact + band)
+    one_ulp_only = np.abs(out.y_exact) * np.where(near, 2.0 ** 15, 1.0)
+    with pytest.raises(AssertionError):
+        assert_bf16(_bf16_tensor(y), out.y_exact, "one-ulp band", mag=one_ulp_only)
+    r2 = O.rmsnorm(out.h, w2, 0.0, 1e-6).r64
+    carried = 2.0 ** -20 * out.h_mag * r2[:, None] * np.abs(w2)
+    moved = np.where(cancel, y + 8.0 * carried, y)
+    with pytest.raises(AssertionError):
+        assert_bf16(_bf16_tensor(moved), out.y_exact, "moved y", mag=out.y_mag)
