@@ -476,8 +476,12 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
 
     // 4) RMSNorm: rstd = 1/sqrt(mean square + eps).  LayerNorm: mean = sum/H, variance =
     //    (sum of squares)/H - mean^2 (population variance), rstd = 1/sqrt(var + eps).
-    //    FP64 throughout (rsqrt_f64: within 2^-52), one FP32 rounding of each result.
-    float rs[R], mu[R];
+    //    FP64 throughout (rsqrt_f64: within 2^-52), one FP32 rounding of each result.  The
+    //    LayerNorm mean is kept as an FP32 pair, mu = FP32(mean) and the rest (mean - mu)
+    //    carried through the FMA that scales by rstd: (h - mean) * rstd is then formed within
+    //    two FP32 roundings of its own value rather than of |mean|, so rows far from zero
+    //    keep their centred values (and outputs near zero) to FP32 accuracy.
+    float rs[R], mu[R], mu_lo[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       double r64;
@@ -487,9 +491,13 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         var = var < 0.0 ? 0.0 : var;   // rounding can leave -0.x ulp; NaN stays NaN
         r64 = rsqrt_f64(var + eps);
         mu[rr] = (float)mean;
+        // The rest of the mean, times -rstd: n = FMA(h - mu, rstd, mu_lo).  NaN when the mean
+        // or rstd is not finite, as n is then.
+        mu_lo[rr] = (float)(-(mean - (double)mu[rr]) * (double)(float)r64);
       } else {
         r64 = rsqrt_f64(ss[rr] * inv_hidden + eps);
         mu[rr] = 0.0f;
+        mu_lo[rr] = 0.0f;
       }
       rs[rr] = (float)r64;
       if (p.rstd && lane == 0 && st.rok[rr]) p.rstd[st.row[rr]] = rs[rr];
@@ -537,11 +545,11 @@ __global__ void __launch_bounds__(NT) fwd_kernel(const FwdParams p) {
         float silu_amax = 0.0f;   // largest |z| of the vector (SiLU)
         unpack8(st.a[rr][v], fh);
         if constexpr (kLN) {
-          // n = (h - mean) * rstd in FP32, then one FMA with gamma and beta (or with the
+          // n = FMA(h - mu, rstd, mu_lo) in FP32, then one FMA with gamma and beta (or with the
           // modulation's 1 + scale + scale_bias and shift + shift_bias).
           float nv[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) nv[k] = (fh[k] - mu[rr]) * rs[rr];
+          for (int k = 0; k < 8; ++k) nv[k] = fmaf(fh[k] - mu[rr], rs[rr], mu_lo[rr]);
           if constexpr (kMod) {
             float fsc[8], fsh[8];
             unpack8(st.ssc[rr][v], fsc);

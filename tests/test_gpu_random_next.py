@@ -1,8 +1,10 @@
 """Seeded random shapes for the other row engines: block FP8, the Ada calls, the gated residual
 (+ next), RMSNorm + SiLU, the per-head sigmoid gate, the three DiT modes and the QK RMSNorm +
-3-D RoPE.  Each seed draws the shape (and the call's options), builds the inputs from the
-workload generators and checks the kernel against the FP64 oracle with the standard gates.
-DN_RANDOM_SHAPES_NEXT (default 8) sets the number of seeds per test."""
+3-D RoPE, and seeded random value ranges (row scales, eps, outliers, LayerNorm offsets, FP8
+scales) for the plain and quantised norms.  Each seed draws the shape (and the call's
+options), builds the inputs from the workload generators and checks the kernel against the
+FP64 oracle with the standard gates.  DN_RANDOM_SHAPES_NEXT (default 8) sets the number of
+seeds per test."""
 from __future__ import annotations
 
 import os
@@ -247,3 +249,84 @@ def test_random_qk_rope(dn, case):
     assert_fp8(qo, q8.q, q8.tie, f"Q e4m3 {what}")
     assert_fp8(ko, k8.q, k8.tie, f"K e4m3 {what}")
     assert_fp8(vo, v8.q, v8.tie, f"V e4m3 {what}")
+
+
+NUMERIC_OPS = ("rmsnorm", "rmsnorm_quant", "fused_add_quant", "block_quant", "layernorm",
+               "layernorm_quant", "silu", "silu_fp8")
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("op", NUMERIC_OPS)
+def test_random_numerics(dn, op, case):
+    """Random value ranges on the plain and quantised norms: rows scaled by 10^U(-25, 25),
+    1 % outliers at 50x on half the seeds, eps in {0, 1e-6, 1e-3, 1}, LayerNorm rows offset
+    by up to 100 of their scale, FP8 scales 10^U(-3, 1) (saturating and not).  These drive
+    the kernels' FP64 re-sum path for squares that leave FP32, the fast and NaN-safe FP8
+    paths and the tiny-block-scale path."""
+    rng = rng_of(10 + NUMERIC_OPS.index(op), case)
+    hidden = 128 * int(rng.integers(1, 65)) if op == "block_quant" else 8 * int(rng.integers(1, 2049))
+    rows = rows_for(rng, hidden, cap=100)
+    scale_x = float(10.0 ** rng.uniform(-25, 25))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
+    fp8_scale = float(np.float32(10.0 ** rng.uniform(-3, 1)))
+    outliers = bool(rng.integers(0, 2))
+    seed = 900 + 10 * NUMERIC_OPS.index(op) + case
+
+    def act(tid, offset=0.0):
+        t = W.normal((rows, hidden), seed, tid)
+        if outliers:
+            t = W.with_outliers(t, seed, 50 + tid)
+        return ((t.double() + offset) * scale_x).to(torch.bfloat16)
+
+    w = W.normal((hidden,), seed, 9, mean=1.0, std=0.1)
+    what = (f"{op} case {case}: [{rows},{hidden}] scale {scale_x:.2e} eps {eps} "
+            f"fp8 scale {fp8_scale:.3e} outliers {outliers}")
+    if op == "rmsnorm":
+        x = act(0)
+        y, rstd = dn.dn_rmsnorm(dev(x), dev(w), eps, return_rstd=True)
+        ref = O.rmsnorm(values(x), values(w), 0.0, eps)
+        assert_bf16(y, ref.y_exact, what)
+        g = rstd.cpu().double().numpy()
+        assert np.all(np.abs(g - ref.r64) <= 2e-7 * ref.r64), f"rstd {what}"
+    elif op == "rmsnorm_quant":
+        x = act(0)
+        q = dn.dn_rmsnorm_quant(dev(x), dev(w), fp8_scale, eps)
+        _, ref = O.rmsnorm_quant(values(x), values(w), fp8_scale, 0.0, eps)
+        assert_fp8(q, ref.q, ref.tie, what)
+    elif op == "fused_add_quant":
+        x, r = act(0), act(1)
+        rd = dev(r)
+        q = dn.dn_fused_add_rmsnorm_quant(dev(x), rd, dev(w), fp8_scale, eps)
+        fa, ref = O.fused_add_rmsnorm_quant(values(x), values(r), values(w), fp8_scale, 0.0, eps)
+        assert_bits_equal(rd, fa.h_new, f"h_new {what}")
+        assert_fp8(q, ref.q, ref.tie, what)
+    elif op == "block_quant":
+        x, r = act(0), act(1)
+        rd = dev(r)
+        q, bs = dn.dn_fused_add_rmsnorm_fp8_block_quant(dev(x), rd, dev(w), eps)
+        ref = O.fused_add_rmsnorm_fp8_block_quant(values(x), values(r), values(w), 0.0, eps)
+        assert_bits_equal(rd, ref.h_new, f"h_new {what}")
+        assert_block_quant(q, bs.t()[:rows], ref, what)
+    elif op in ("layernorm", "layernorm_quant"):
+        x = act(0, offset=float(rng.uniform(-100, 100)))
+        ga = W.normal((hidden,), seed, 7, std=0.1, dtype=torch.float32) + 1.0
+        be = W.normal((hidden,), seed, 8, std=0.1, dtype=torch.float32)
+        if op == "layernorm":
+            y = dn.dn_layernorm(dev(x), dev(ga), dev(be), eps)
+            ln = L.layernorm(values(x), ga.double().numpy(), be.double().numpy(), eps)
+            assert_bf16(y, ln.y_exact, what, mag=ln.mag)
+        else:
+            q = dn.dn_layernorm_quant(dev(x), dev(ga), dev(be), fp8_scale, eps)
+            _, ref = L.layernorm_quant(values(x), ga.double().numpy(), be.double().numpy(),
+                                       fp8_scale, eps)
+            assert_fp8(q, ref.q, ref.tie, what)
+    else:
+        x = act(0)
+        if op == "silu":
+            y = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), eps)
+            r = S.fused_rmsnorm_silu(values(x), values(w), eps)
+            assert_bf16(y, r.s_exact, what, mag=r.mag)
+        else:
+            q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), eps, output_fp8=True, scale=fp8_scale)
+            _, ref = S.fused_rmsnorm_silu_fp8(values(x), values(w), fp8_scale, eps)
+            assert_fp8(q, ref.q, ref.tie, what)

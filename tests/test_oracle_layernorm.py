@@ -128,3 +128,51 @@ def test_dit_gamma_beta_matches_torch_and_reduces_to_layernorm():
     s = L.dit_gate_residual_layernorm_scale_shift(r, x, g, zero, zero, 0.0, 0.0, 0.0, 1e-6)
     plain = L.layernorm(s.residual_out, None, None, 1e-6)
     assert (s.o_exact == plain.y_exact).all()
+
+
+
+def _fp32_layernorm_quant(h, gamma, beta, scale, eps, compensated=True):
+    """An FP32 evaluation of layernorm_quant in the kernel's order: FP64 statistics; mu =
+    FP32(mean) and rstd rounded once to FP32; n = FMA(FP32(h - mu), rstd, lo) with lo =
+    FP32(-(mean - mu) * rstd) (uncompensated: lo = 0); gamma and beta multiplied by FP32(1/scale);
+    y = FMA(n, gamma', beta') (its product exact in FP64, the sum rounded to FP64 and then to
+    FP32); then the e4m3 conversion."""
+    f32 = np.float32
+    hidden = h.shape[1]
+    mean = h.sum(axis=1) / hidden
+    var = np.maximum((h * h).sum(axis=1) / hidden - mean * mean, 0.0)
+    rs = (1.0 / np.sqrt(var + float(f32(eps)))).astype(f32)
+    mu = mean.astype(f32)
+    lo = (-(mean - mu.astype(np.float64)) * rs).astype(f32) if compensated else np.zeros_like(mu)
+    d = (h.astype(f32) - mu[:, None]).astype(f32)
+    n = (d.astype(np.float64) * rs[:, None].astype(np.float64) + lo[:, None]).astype(f32)
+    inv = f32(1.0) / f32(scale)
+    g = (gamma.astype(f32) * inv).astype(f32)
+    b = (beta.astype(f32) * inv).astype(f32)
+    y = (n.astype(np.float64) * g.astype(np.float64) + b.astype(np.float64)).astype(f32)
+    return F.f64_to_e4m3_code(y.astype(np.float64))
+
+
+def test_quant_gate_sees_the_mean_rounding_where_the_output_cancels():
+    """Rows of width 1000 sitting 1000 of their spreads away from zero, and a beta that
+    cancels row 0's n*gamma on 256 columns, quantised at a scale of 1e-3: those outputs lie
+    next to zero, in e4m3's subnormals.  The kernel's evaluation, which carries the mean as
+    an FP32 pair, passes the one-step gate; the same evaluation with the mean rounded once to
+    FP32 (whose error there is 2^-25 of the mean) moves them by several subnormal steps and
+    fails it."""
+    from tests.parity import assert_fp8
+    h = bf16_values((16, 1000), 1.0, 1000.0)     # a width whose mean FP32 cannot hold exactly
+    gamma = 1.0 + RNG.normal(0, 0.1, 1000)
+    ln0 = L.layernorm(h, gamma, np.zeros(1000), 1e-6)
+    beta = RNG.normal(0, 0.1, 1000)
+    beta[:256] = -ln0.y_exact[0, :256]
+    gamma = gamma.astype(np.float32).astype(np.float64)
+    beta = beta.astype(np.float32).astype(np.float64)
+    _, q = L.layernorm_quant(h, gamma, beta, 1e-3, 1e-6)
+    as_t = lambda c: torch.from_numpy(np.ascontiguousarray(c, dtype=np.uint8))
+    codes = _fp32_layernorm_quant(h, gamma, beta, 1e-3, 1e-6)
+    assert_fp8(as_t(codes), q.q, q.tie, "FP32 evaluation, mean as an FP32 pair")
+    plain = _fp32_layernorm_quant(h, gamma, beta, 1e-3, 1e-6, compensated=False)
+    assert (F.e4m3_code_steps(plain, q.q)[0, :256] >= 2).sum() >= 10
+    with pytest.raises(AssertionError):
+        assert_fp8(as_t(plain), q.q, q.tie, "FP32 evaluation, mean rounded once")
