@@ -6,7 +6,7 @@
 // a fixed set of 16-byte column vectors for the whole chunk, so its slice of dw stays in
 // FP64 registers while the block streams the chunk's rows:
 //     per row t:  c_t  = (1/H) sum_j g*w_eff*x         (lane partials in FP32, then FP64)
-//                 dx   = BF16(r*g*w_eff - x*(r^3*c_t) [+ g_residual])
+//                 dx   = BF16(r*(g*w_eff - x*(r^2*c_t)) [+ g_residual])
 //     per column: P[chunk][j] += (g*x) * r              (exact products, FP64 sums)
 // A row is split over TPR threads (over several waves for wide rows, meeting in LDS); for
 // narrow rows several row groups run side by side and their FP64 sums are added in group
@@ -270,20 +270,28 @@ __global__ void __launch_bounds__(NT) bwd_partials_kernel(const BwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       // Rows past the chunk carry r = 0 and add nothing; their dx stores are dropped.
+      // dx = r * FMA(-x, r^2 * c_t, g * w_eff) [+ g_res]: the coupled coefficient carries
+      // r^2, not r^3, so no factor leaves FP32's range when the row's scale is far from 1
+      // (r^3 * c_t underflows FP32 for rows of RMS ~1e17 with gradients ~1e-13, and
+      // overflows for rows of RMS ~1e-17 with gradients ~1e12, where dx itself is an
+      // ordinary FP32 number).
       const double r64 = (double)st.rs[rr];
-      const float coef = (float)(r64 * r64 * r64 * (dot[rr] * inv_hidden));
+      const float coef = (float)(r64 * r64 * (dot[rr] * inv_hidden));
 #pragma unroll
       for (int v = 0; v < VB; ++v) {
         float fg[8], fx[8], d[8];
         unpack8(st.g[rr][v], fg);
         unpack8(st.x[rr][v], fx);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = fmaf(-fx[k], coef, (fg[k] * we[v][k]) * st.rs[rr]);
+        for (int k = 0; k < 8; ++k) d[k] = fmaf(-fx[k], coef, fg[k] * we[v][k]);
         if constexpr (GRES) {
           float fr[8];
           unpack8(st.r[rr][v], fr);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) d[k] += fr[k];
+          for (int k = 0; k < 8; ++k) d[k] = fmaf(d[k], st.rs[rr], fr[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) d[k] *= st.rs[rr];
         }
         bstore16(rdx[rr], odx[rr] + (uint32_t)(v * TPR * 16), pack8(d));
 #pragma unroll

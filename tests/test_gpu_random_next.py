@@ -14,13 +14,15 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import formats as F
 from oracle import gated as G
 from oracle import layernorm as L
 from oracle import qk_rope as Q
 from oracle import rmsnorm as O
 from oracle import silu as S
 from tests.conftest import values
-from tests.parity import assert_bf16, assert_bits_equal, assert_block_quant, assert_fp8
+from tests.parity import (assert_bf16, assert_bits_equal, assert_block_quant, assert_dw,
+                          assert_dx, assert_fp8, assert_rstd)
 
 pytestmark = pytest.mark.gpu
 
@@ -330,3 +332,171 @@ def test_random_numerics(dn, op, case):
             q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), eps, output_fp8=True, scale=fp8_scale)
             _, ref = S.fused_rmsnorm_silu_fp8(values(x), values(w), fp8_scale, eps)
             assert_fp8(q, ref.q, ref.tie, what)
+
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_numerics_train(dn, case):
+    """The training pair over random value ranges: the residual stream scaled by
+    10^U(-20, 20), the gradient by 10^U(-20, 20), eps in {0, 1e-6, 1e-3, 1}, FP32 or BF16
+    weights (bias 1 or 0), with or without the residual route and a residual gradient."""
+    rng = rng_of(30, case)
+    hidden = 8 * int(rng.integers(1, 2049))
+    rows = rows_for(rng, hidden, cap=150)
+    sx, sg = (float(10.0 ** rng.uniform(-20, 20)) for _ in range(2))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
+    sg = min(sg, 1e30 * max(sx, eps ** 0.5))      # dx ~ g * r stays inside BF16's range
+    f32w, residual, gres = (bool(rng.integers(0, 2)) for _ in range(3))
+    seed = 1900 + case
+    sc = lambda t, s: (t.double() * s).to(torch.bfloat16)
+    x = sc(W.normal((rows, hidden), seed, 0), sx)
+    u = sc(W.normal((rows, hidden), seed, 1), sx) if residual else None
+    g = sc(W.normal((rows, hidden), seed, 2), sg)
+    gr = sc(W.normal((rows, hidden), seed, 3), sg) if gres else None
+    w = W.normal((hidden,), seed, 4, std=0.02, dtype=torch.float32) if f32w else \
+        W.normal((hidden,), seed, 4, mean=1.0, std=0.1)
+    bias = 1.0 if f32w else 0.0
+    what = (f"train case {case}: [{rows},{hidden}] x {sx:.1e} g {sg:.1e} eps {eps} f32w {f32w} "
+            f"residual {residual} g_residual {gres}")
+    out = dn.dn_train_forward(dev(x), dev(w), eps, w_bias=bias,
+                              residual=None if u is None else dev(u))
+    fwd = O.train_forward(values(x), values(w), bias, eps,
+                          residual=None if u is None else values(u))
+    if residual:
+        assert_bits_equal(out[2], fwd.h_new, f"h_new {what}")
+    assert_bf16(out[0], fwd.y_exact, f"y {what}")
+    assert_rstd(out[1], fwd.r64, f"rstd {what}")
+    # the backward runs on the oracle's forward results (never on GPU outputs)
+    xb = torch.from_numpy(F.f64_to_bf16_bits(fwd.h_new).view(np.int16)).view(torch.bfloat16) \
+        if residual else x
+    rstd = torch.from_numpy(fwd.rstd.astype(np.float32))
+    dx, dw = dn.dn_train_backward(dev(g), dev(xb), dev(w), dev(rstd), w_bias=bias,
+                                  g_residual=None if gr is None else dev(gr))
+    ref = O.train_backward(values(g), values(xb), values(w), rstd.double().numpy(), bias,
+                           None if gr is None else values(gr))
+    assert_dx(dx, ref, f"dx {what}")
+    assert_dw(dw, ref.dw_exact, f"dw {what}")
+
+
+
+def scaled(t, s):
+    return (t.double() * s).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_numerics_ada(dn, case):
+    """The Ada calls over random value ranges: x and the residual scaled by 10^U(-20, 20),
+    the style rows (scale, shift, gate) by 10^U(-3, 3), eps in {0, 1e-6, 1e-3, 1}, static
+    FP8 scales 10^U(-3, 1)."""
+    rng = rng_of(31, case)
+    dim = 8 * int(rng.integers(1, 1025))
+    rows = rows_for(rng, dim, cap=100)
+    broadcast = bool(rng.integers(0, 2))
+    sx, ss = float(10.0 ** rng.uniform(-20, 20)), float(10.0 ** rng.uniform(-3, 3))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
+    fp8_scale = float(np.float32(10.0 ** rng.uniform(-3, 1)))
+    wl = W.ada(rows=rows, dim=dim, seed=2000 + case, broadcast=broadcast)
+    t = wl.tensors
+    x, res = scaled(t["x"], sx), scaled(t["residual"], sx)
+    style = scaled(t["style"], ss)
+    w = W.normal((dim,), 2000 + case, 9, mean=1.0, std=0.1)
+    what = (f"Ada numerics case {case}: [{rows},{dim}] broadcast {broadcast} x {sx:.1e} "
+            f"style {ss:.1e} eps {eps} fp8 scale {fp8_scale:.2e}")
+    out, gout = dn.dn_ada_rms_norm(dev(x), dev(w), dev(style), eps)
+    a, _ = O.ada_rms_norm(values(x), values(w), values(style), eps)
+    assert_bf16(out, a.o_exact, f"BF16 {what}", mag=a.o_mag)
+    assert_bits_equal(gout, a.gate_out, f"gate_out {what}")
+    rd = dev(res)
+    _, q, _ = dn.dn_gate_residual_ada_norm_fp8(rd, dev(x), dev(t["gate"]), dev(t["w"]),
+                                               dev(style), fp8_scale, eps)
+    g, ref = O.gate_residual_ada_norm_fp8(values(res), values(x), values(t["gate"]),
+                                          values(t["w"]), values(style), fp8_scale, eps)
+    assert_bits_equal(rd, g.h, f"residual {what}")
+    assert_fp8(q, ref.q, ref.tie, f"FP8 {what}")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_numerics_gates(dn, case):
+    """The gated residual (+ next) and the sigmoid gate over random value ranges: streams
+    scaled by 10^U(-20, 20), gates by 10^U(-3, 3) (past the |gate| > 80 path of the
+    sigmoid), eps in {0, 1e-6, 1e-3, 1}."""
+    rng = rng_of(32, case)
+    hidden = 8 * int(rng.integers(1, 1025))
+    rows = rows_for(rng, hidden, cap=100)
+    sb, sr, sgt = (float(10.0 ** rng.uniform(lo, hi)) for lo, hi in ((-20, 20), (-20, 20), (-3, 3)))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
+    per_token = bool(rng.integers(0, 2))
+    wl = W.gated_residual(rows, hidden, seed=2100 + case, per_token_gate=per_token)
+    t = wl.tensors
+    br, res, gate = scaled(t["branch"], sb), scaled(t["residual"], sr), scaled(t["gate"], sgt)
+    what = (f"gates numerics case {case}: [{rows},{hidden}] branch {sb:.1e} residual {sr:.1e} "
+            f"gate {sgt:.1e} eps {eps} per-token {per_token}")
+    r = dev(res)
+    _, y = dn.dn_gated_residual_next_rmsnorm(dev(br), r, dev(gate) if per_token else dev(gate[0]),
+                                             dev(t["w"]), dev(t["w_next"]), eps)
+    ref = G.gated_residual_rmsnorm(values(br), values(res), values(gate), values(t["w"]), eps,
+                                   next_w=values(t["w_next"]))
+    assert_bf16(r, ref.h_exact, f"h {what}", mag=ref.h_mag)
+    assert_bf16(y, ref.y_exact, f"next {what}", mag=ref.y_mag)
+    heads = int(rng.integers(1, 9))
+    hd = 8 * int(rng.integers(1, 65))
+    tokens = rows_for(rng, heads * hd, cap=100)
+    sw = W.sigmoid_gate(tokens, heads, hd, seed=2200 + case)
+    xs, gs = scaled(sw.tensors["x"], sb), scaled(sw.tensors["gate"], sgt)
+    xd = dev(xs).reshape(tokens, heads, hd)
+    dn.dn_rmsnorm_sigmoid_gate(xd, dev(gs).reshape(tokens, heads, hd), eps,
+                               weight=dev(sw.tensors["w"]))
+    s = S.rmsnorm_sigmoid_gate(values(xs).reshape(-1, hd), values(gs).reshape(-1, hd),
+                               values(sw.tensors["w"]), eps)
+    assert_bf16(xd.reshape(-1, hd), s.o_exact, f"sigmoid gate [{tokens},{heads},{hd}] {what}",
+                mag=s.mag)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_numerics_rope(dn, case):
+    """QK RMSNorm + 3-D RoPE over random parameters: qkv scaled by 10^U(-20, 20), base
+    10^U(2, 6), eps in {0, 1e-6, 1e-3, 1}, YaRN factor U(1, 16) with random ramp bounds and
+    attention factor (plain RoPE on half the seeds), both pairings, with and without the
+    norm, BF16 and FP8 outputs at random scales."""
+    rng = rng_of(33, case)
+    ppf, pph, ppw, batch, (nq, nk, nv), hd, chn = draw_rope(rng)
+    interleave, norm = bool(rng.integers(0, 2)), bool(rng.integers(0, 4) > 0)
+    sq = float(10.0 ** rng.uniform(-20, 20))
+    base = float(10.0 ** rng.uniform(2, 6))
+    eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
+    if rng.integers(0, 2):
+        factor = float(rng.uniform(1.0, 16.0))
+        low = float(rng.uniform(0.0, hd / 4))
+        high = float(low + rng.choice([0.0, rng.uniform(0.0, hd / 4)]))
+        af = float(rng.uniform(0.5, 2.0))
+    else:
+        factor, low, high, af = 1.0, 0.0, 0.0, 1.0
+    oscale, vscale = (float(np.float32(10.0 ** rng.uniform(-3, 0))) for _ in range(2))
+    if not norm:
+        sq = float(10.0 ** rng.uniform(-3, 2))      # no norm: values pass through, keep them finite
+    wl = W.qk_rope(ppf, pph, ppw, batch, nq, nk, nv, hd, chn, seed=2300 + case)
+    t = wl.tensors
+    qkv = scaled(t["qkv"], sq)
+    what = (f"rope numerics case {case}: grid {ppf}x{pph}x{ppw}x{batch} heads {nq}/{nk}/{nv} "
+            f"hd {hd} ch {chn} il {interleave} norm {norm} x {sq:.1e} base {base:.1e} eps {eps} "
+            f"yarn ({factor:.2f}, {low:.1f}, {high:.1f}, {af:.2f}) scales {oscale:.2e}/{vscale:.2e}")
+
+    def call(fp8):
+        return dn.dn_fused_qk_rmsnorm_rope(
+            dev(qkv), dev(t["q_weight"]), dev(t["k_weight"]), nq, nk, nv, hd, ppf, pph, ppw, chn,
+            eps, base=base, interleave=interleave, yarn_factor=factor, yarn_low=low,
+            yarn_high=high, attention_factor=af, is_qk_norm=norm, output_fp8=fp8,
+            output_quant_scale=oscale, v_quant_scale=vscale)
+
+    r = Q.qk_rmsnorm_rope(values(qkv), values(t["q_weight"]), values(t["k_weight"]), nq, nk, nv,
+                          hd, chn, ppf, pph, ppw, eps, base, interleave, factor, low, high, af,
+                          norm)
+    qo, ko, vo = call(False)
+    assert_bits_equal(vo, r.v, f"V copy {what}")
+    assert_bf16(qo, r.q_exact, f"Q {what}", mag=r.q_mag)
+    assert_bf16(ko, r.k_exact, f"K {what}", mag=r.k_mag)
+    q8, k8, v8 = Q.qk_rmsnorm_rope_fp8(r, oscale, vscale)
+    qo, ko, vo = call(True)
+    assert_fp8(qo, q8.q, q8.tie, f"Q e4m3 {what}")
+    assert_fp8(ko, k8.q, k8.tie, f"K e4m3 {what}")
+    assert_fp8(vo, v8.q, v8.tie, f"V e4m3 {what}")

@@ -560,10 +560,12 @@ def test_train_forward_residual_route_is_fused_add():
     assert (t.h_new == F.bf16_round(h + u)).all()
 
 
-def _dx_fp32_model(g, x, w_eff, r, coef_error: float = 0.0):
+def _dx_fp32_model(g, x, w_eff, r, coef_error: float = 0.0, r_cubed: bool = False):
     """dx as an FP32 kernel evaluates it (lane partials of g*w*x over 32 terms, the row sum
-    in FP64, coef = FP32(r^3*c), dx = FMA(-x, coef, (g*w)*r)), rounded to BF16; coef_error
-    perturbs the coupled coefficient."""
+    in FP64, k = FP32(r^2*c), dx = FP32(FMA(-x, k, g*w) * r)), rounded to BF16; coef_error
+    perturbs the coupled coefficient.  r_cubed evaluates the other order, coef = FP32(r^3*c)
+    and dx = FMA(-x, coef, (g*w)*r), whose coefficient leaves FP32's range for rows whose
+    scale is far from 1."""
     f32 = np.float32
     H = x.shape[1]
     gw = (g.astype(f32) * w_eff.astype(f32)).astype(f32)
@@ -575,9 +577,15 @@ def _dx_fp32_model(g, x, w_eff, r, coef_error: float = 0.0):
                 j = ln + k * (H // 32)
                 lanes[ln] = f32(float(gw[t, j]) * float(x[t, j]) + float(lanes[ln]))
         c = sum(float(v) for v in lanes) / H
-        coef = f32(float(r[t]) ** 3 * c * (1.0 + coef_error))
-        first = f32(gw[t] * f32(r[t]))
-        out[t] = (-x[t] * float(coef) + first.astype(np.float64)).astype(f32)
+        with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+            if r_cubed:
+                coef = f32(float(r[t]) ** 3 * c * (1.0 + coef_error))
+                first = f32(gw[t] * f32(r[t]))
+                out[t] = (-x[t] * float(coef) + first.astype(np.float64)).astype(f32)
+            else:
+                k2 = f32(float(r[t]) ** 2 * c * (1.0 + coef_error))
+                inner = (-x[t] * float(k2) + gw[t].astype(np.float64)).astype(f32)
+                out[t] = (inner * f32(r[t])).astype(f32)
     return F.bf16_round(out)
 
 
@@ -594,3 +602,21 @@ def test_dx_gate_admits_fp32_evaluation_and_rejects_a_wrong_coefficient():
     assert_dx(to_t(_dx_fp32_model(g, x, w, r)), ref, "fp32 model")
     with pytest.raises(AssertionError, match="per-element"):
         assert_dx(to_t(_dx_fp32_model(g, x, w, r, 1e-3)), ref, "perturbed model")
+
+
+def test_dx_gate_sees_the_coupled_coefficient_leave_fp32():
+    """Rows of RMS ~1e17 with gradients ~1e-13 (and the mirror case, RMS ~1e-17 with
+    gradients ~1e12): dx is an ordinary FP32 number, but r^3*c underflows (overflows) FP32.
+    The kernel's order, r*(g*w - x*(r^2*c)), passes the dx gate; the r^3 order fails it."""
+    from tests.parity import assert_dx
+    to_t = lambda v: torch.from_numpy(F.f64_to_bf16_bits(v).view(np.int16)).view(torch.bfloat16)
+    w = bf16_values((1024,), mean=1.0, std=0.1)
+    for sx, sg in ((1e17, 1e-13), (1e-17, 1e12)):
+        x = F.bf16_round(bf16_values((4, 1024)) * sx)
+        g = F.bf16_round(bf16_values((4, 1024)) * sg)
+        r = F.f32_round(1.0 / np.sqrt(np.mean(x * x, axis=1)))
+        ref = O.train_backward(g, x, w, r, 0.0)
+        assert np.isfinite(ref.dx_exact).all() and (np.abs(ref.dx_exact) > 1e-37).mean() > 0.9
+        assert_dx(to_t(_dx_fp32_model(g, x, w, r)), ref, f"kernel order at {sx:g}")
+        with pytest.raises(AssertionError):
+            assert_dx(to_t(_dx_fp32_model(g, x, w, r, r_cubed=True)), ref, f"r^3 order at {sx:g}")
