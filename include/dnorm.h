@@ -198,8 +198,11 @@ dn_status dn_train_forward(void* y, int64_t y_stride, float* rstd,
  * Training backward   ([norm docs] cake_rmsnorm_train_backward, ..._workspace_bytes;
  *                      [norm guide] §6.1-6.4)
  *   dx = BF16(r*g*w_eff - x*r^3*mean_j(g*w_eff*x) [+ g_residual]), evaluated in FP32 as
- *        r*(g*w_eff - x*(r^2*mean)) so that no factor leaves FP32's range for rows whose
- *        scale is far from 1 (mean_j and r^2*mean in FP64)
+ *        r*(g*w_eff - x*(r^2*mean)) so that the coefficient stays in FP32's range for rows
+ *        whose scale is far from 1 (mean_j and r^2*mean in FP64)
+ *   Range: the products g*x (the row's dot product and dw's terms) are formed in FP32, so
+ *   the stated accuracy needs |g|*|x| inside FP32's normal range (about 1e-38 .. 3e38);
+ *   beyond it dx and dw lose accuracy (dw stays bitwise deterministic).
  *   dw = FP32(sum_t g*x*r)     -- the gradient with respect to w_eff (= w + w_bias)
  *   x is the tensor the forward normalised (h_new on the residual route) and rstd the FP32
  *   tensor the forward returned.  g_residual (nullable) is the gradient reaching h_new

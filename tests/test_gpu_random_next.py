@@ -338,14 +338,19 @@ def test_random_numerics(dn, op, case):
 @pytest.mark.parametrize("case", CASES)
 def test_random_numerics_train(dn, case):
     """The training pair over random value ranges: the residual stream scaled by
-    10^U(-20, 20), the gradient by 10^U(-20, 20), eps in {0, 1e-6, 1e-3, 1}, FP32 or BF16
-    weights (bias 1 or 0), with or without the residual route and a residual gradient."""
+    10^U(-20, 20), the gradient by 10^U(-20, 20) (kept where dx is a normal BF16 number and
+    g * x a normal FP32 one), eps in {0, 1e-6, 1e-3, 1}, FP32 or BF16 weights (bias 1 or
+    0), with or without the residual route and a residual gradient."""
     rng = rng_of(30, case)
     hidden = 8 * int(rng.integers(1, 2049))
     rows = rows_for(rng, hidden, cap=150)
     sx, sg = (float(10.0 ** rng.uniform(-20, 20)) for _ in range(2))
     eps = float(rng.choice([0.0, 1e-6, 1e-3, 1.0]))
-    sg = min(sg, 1e30 * max(sx, eps ** 0.5))      # dx ~ g * r stays inside BF16's range
+    # dx ~ g * r stays inside BF16's normal range (the unit-scaled dx gate has no absolute
+    # floor, and BF16 subnormals are coarser than it), and the products g * x, which the
+    # backward forms in FP32, inside FP32's (the operating range the header states)
+    s = max(sx, eps ** 0.5)
+    sg = min(max(sg, 1e-30 * s, 1e-30 / sx), 1e30 * s, 1e30 / sx)
     f32w, residual, gres = (bool(rng.integers(0, 2)) for _ in range(3))
     seed = 1900 + case
     sc = lambda t, s: (t.double() * s).to(torch.bfloat16)
