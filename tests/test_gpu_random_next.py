@@ -505,3 +505,84 @@ def test_random_numerics_rope(dn, case):
     assert_fp8(qo, q8.q, q8.tie, f"Q e4m3 {what}")
     assert_fp8(ko, k8.q, k8.tie, f"K e4m3 {what}")
     assert_fp8(vo, v8.q, v8.tie, f"V e4m3 {what}")
+
+
+FORCED_TPR = (8, 16, 32, 64, 128, 256, 320, 448, 512, 1024)
+FORCED_OPS = ("rmsnorm", "rmsnorm_quant", "fused_add", "fused_add_quant", "block_quant",
+              "layernorm", "layernorm_quant", "silu_fp8", "ada", "train_forward")
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_forced_row_mappings(dn, case):
+    """Every forward row mapping (the test hook that forces threads per row; a mapping whose
+    lanes cannot cover the row falls back to the automatic one) on a random row-engine call,
+    hidden and row count, against the oracle."""
+    rng = rng_of(40, case)
+    tpr = int(rng.choice(FORCED_TPR))
+    op = FORCED_OPS[int(rng.integers(0, len(FORCED_OPS)))]
+    hidden = 128 * int(rng.integers(1, 65)) if op == "block_quant" else 8 * int(rng.integers(1, 1025))
+    rows = rows_for(rng, hidden, cap=120)
+    seed = 3000 + case
+    x, r = W.normal((rows, hidden), seed, 0), W.normal((rows, hidden), seed, 1)
+    w = W.normal((hidden,), seed, 2, mean=1.0, std=0.1)
+    what = f"forced tpr {tpr} {op} case {case}: [{rows},{hidden}]"
+    dn.dn_force_threads_per_row(tpr)
+    try:
+        if op == "rmsnorm":
+            y, rstd = dn.dn_rmsnorm(dev(x), dev(w), 1e-6, return_rstd=True)
+            ref = O.rmsnorm(values(x), values(w), 0.0, 1e-6)
+            assert_bf16(y, ref.y_exact, what)
+            assert_rstd(rstd, ref.r64, what)
+        elif op == "rmsnorm_quant":
+            q = dn.dn_rmsnorm_quant(dev(x), dev(w), 0.04, 1e-6)
+            _, ref = O.rmsnorm_quant(values(x), values(w), 0.04, 0.0, 1e-6)
+            assert_fp8(q, ref.q, ref.tie, what)
+        elif op in ("fused_add", "fused_add_quant"):
+            xd, rd = dev(x), dev(r)
+            if op == "fused_add":
+                dn.dn_fused_add_rmsnorm(xd, rd, dev(w), 1e-6)
+                ref = O.fused_add_rmsnorm(values(x), values(r), values(w), 0.0, 1e-6)
+                assert_bf16(xd, ref.norm.y_exact, what)
+                assert_bits_equal(rd, ref.h_new, what)
+            else:
+                q = dn.dn_fused_add_rmsnorm_quant(xd, rd, dev(w), 0.04, 1e-6)
+                fa, ref = O.fused_add_rmsnorm_quant(values(x), values(r), values(w), 0.04, 0.0, 1e-6)
+                assert_bits_equal(rd, fa.h_new, what)
+                assert_fp8(q, ref.q, ref.tie, what)
+        elif op == "block_quant":
+            rd = dev(r)
+            q, bs = dn.dn_fused_add_rmsnorm_fp8_block_quant(dev(x), rd, dev(w), 1e-6)
+            ref = O.fused_add_rmsnorm_fp8_block_quant(values(x), values(r), values(w), 0.0, 1e-6)
+            assert_bits_equal(rd, ref.h_new, what)
+            assert_block_quant(q, bs.t()[:rows], ref, what)
+        elif op in ("layernorm", "layernorm_quant"):
+            ga = W.normal((hidden,), seed, 7, std=0.1, dtype=torch.float32) + 1.0
+            be = W.normal((hidden,), seed, 8, std=0.1, dtype=torch.float32)
+            if op == "layernorm":
+                y = dn.dn_layernorm(dev(x), dev(ga), dev(be), 1e-6)
+                ln = L.layernorm(values(x), ga.double().numpy(), be.double().numpy(), 1e-6)
+                assert_bf16(y, ln.y_exact, what, mag=ln.mag)
+            else:
+                q = dn.dn_layernorm_quant(dev(x), dev(ga), dev(be), 0.04, 1e-6)
+                _, ref = L.layernorm_quant(values(x), ga.double().numpy(), be.double().numpy(),
+                                           0.04, 1e-6)
+                assert_fp8(q, ref.q, ref.tie, what)
+        elif op == "silu_fp8":
+            q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), 1e-6, output_fp8=True, scale=0.02)
+            _, ref = S.fused_rmsnorm_silu_fp8(values(x), values(w), 0.02, 1e-6)
+            assert_fp8(q, ref.q, ref.tie, what)
+        elif op == "ada":
+            style = W.normal((rows, 3 * hidden), seed, 3)
+            out, gout = dn.dn_ada_rms_norm(dev(x), dev(w), dev(style), 1e-6)
+            a, _ = O.ada_rms_norm(values(x), values(w), values(style), 1e-6)
+            assert_bf16(out, a.o_exact, what, mag=a.o_mag)
+            assert_bits_equal(gout, a.gate_out, what)
+        else:
+            wf = W.normal((hidden,), seed, 4, std=0.02, dtype=torch.float32)
+            y, rstd, hn = dn.dn_train_forward(dev(x), dev(wf), 1e-6, w_bias=1.0, residual=dev(r))
+            ref = O.train_forward(values(x), values(wf), 1.0, 1e-6, residual=values(r))
+            assert_bits_equal(hn, ref.h_new, what)
+            assert_bf16(y, ref.y_exact, what)
+            assert_rstd(rstd, ref.r64, what)
+    finally:
+        dn.dn_force_threads_per_row(0)
