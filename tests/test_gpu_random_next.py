@@ -586,3 +586,141 @@ def test_random_forced_row_mappings(dn, case):
             assert_rstd(rstd, ref.r64, what)
     finally:
         dn.dn_force_threads_per_row(0)
+
+
+LAYOUT_OPS = ("layernorm", "silu", "ada", "ada_gated_fp8", "gated_next", "sigmoid_gate",
+              "train", "qk_rope")
+
+
+def padded_out(shape, pad, dtype=torch.bfloat16):
+    """(view, buffer): an output view with `pad` elements after every row of a buffer filled
+    with a sentinel, so writes past a row show up."""
+    rows, h = shape
+    big = torch.full((rows, h + pad), 7.0, dtype=torch.float32, device="cuda").to(dtype)
+    return big[:, :h], big
+
+
+def assert_pads_untouched(buf, h, what):
+    if buf.shape[1] > h:
+        tail = buf[:, h:].float()
+        assert bool((tail == 7.0).all()), f"{what}: a write landed in the row padding"
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_random_layouts(dn, case):
+    """Padded row strides on the inputs and the outputs of the other row engines (and 3-D
+    activations where the call takes them): the results match the oracle and nothing is
+    written into the padding between rows."""
+    rng = rng_of(41, case)
+    op = LAYOUT_OPS[int(rng.integers(0, len(LAYOUT_OPS)))]
+    pad_in, pad_out = (8 * int(rng.integers(0, 5)) for _ in range(2))
+    seed = 3200 + case
+    what = f"layout {op} case {case}: pads {pad_in}/{pad_out}"
+    if op == "qk_rope":
+        ppf, pph, ppw, batch, (nq, nk, nv), hd, chn = draw_rope(rng)
+        wl = W.qk_rope(ppf, pph, ppw, batch, nq, nk, nv, hd, chn, seed=seed)
+        t, p = wl.tensors, wl.params
+        qkv = padded(t["qkv"], pad_in)
+        outs = [padded_out((qkv.shape[0], n * hd), pad_out) for n in (nq, nk, nv)]
+        qo, ko, vo = dn.dn_fused_qk_rmsnorm_rope(
+            qkv, dev(t["q_weight"]), dev(t["k_weight"]), nq, nk, nv, hd, ppf, pph, ppw, chn,
+            p["eps"], base=p["base"], q_out=outs[0][0], k_out=outs[1][0], v_out=outs[2][0])
+        r = Q.qk_rmsnorm_rope(values(t["qkv"]), values(t["q_weight"]), values(t["k_weight"]),
+                              nq, nk, nv, hd, chn, ppf, pph, ppw, p["eps"], p["base"], True,
+                              1.0, 0.0, 0.0, 1.0, True)
+        assert_bf16(outs[0][0], r.q_exact, f"Q {what}", mag=r.q_mag)
+        assert_bf16(outs[1][0], r.k_exact, f"K {what}", mag=r.k_mag)
+        assert_bits_equal(outs[2][0], r.v, f"V {what}")
+        for (v, buf), n in zip(outs, (nq, nk, nv)):
+            assert_pads_untouched(buf, n * hd, what)
+        return
+    hidden = 8 * int(rng.integers(1, 769))
+    rows = rows_for(rng, hidden, cap=96)
+    x = W.normal((rows, hidden), seed, 0)
+    w = W.normal((hidden,), seed, 2, mean=1.0, std=0.1)
+    xd = padded(x, pad_in)
+    if op == "layernorm":
+        ga = W.normal((hidden,), seed, 7, std=0.1, dtype=torch.float32) + 1.0
+        be = W.normal((hidden,), seed, 8, std=0.1, dtype=torch.float32)
+        y, buf = padded_out((rows, hidden), pad_out)
+        dn.dn_layernorm(xd, dev(ga), dev(be), 1e-6, out=y)
+        ln = L.layernorm(values(x), ga.double().numpy(), be.double().numpy(), 1e-6)
+        assert_bf16(y, ln.y_exact, what, mag=ln.mag)
+        assert_pads_untouched(buf, hidden, what)
+    elif op == "silu":
+        y, buf = padded_out((rows, hidden), pad_out)
+        dn.dn_fused_rmsnorm_silu(xd, dev(w), 1e-6, out=y)
+        s = S.fused_rmsnorm_silu(values(x), values(w), 1e-6)
+        assert_bf16(y, s.s_exact, what, mag=s.mag)
+        assert_pads_untouched(buf, hidden, what)
+    elif op in ("ada", "ada_gated_fp8"):
+        style = W.normal((rows, 3 * hidden), seed, 3)
+        sd = padded(style, pad_in)
+        if op == "ada":
+            y, buf = padded_out((rows, hidden), pad_out)
+            go, gbuf = padded_out((rows, hidden), pad_out)
+            dn.dn_ada_rms_norm(xd, dev(w), sd, 1e-6, out=y, gate_out=go)
+            a, _ = O.ada_rms_norm(values(x), values(w), values(style), 1e-6)
+            assert_bf16(y, a.o_exact, what, mag=a.o_mag)
+            assert_bits_equal(go, a.gate_out, what)
+            assert_pads_untouched(buf, hidden, what)
+            assert_pads_untouched(gbuf, hidden, what)
+        else:
+            res = W.normal((rows, hidden), seed, 1)
+            gate = W.normal((rows, hidden), seed, 4)
+            rd = padded(res, pad_in)
+            _, q, go = dn.dn_gate_residual_ada_norm_fp8(rd, xd, padded(gate, pad_in), dev(w), sd,
+                                                        0.04, 1e-6)
+            g, ref = O.gate_residual_ada_norm_fp8(values(res), values(x), values(gate),
+                                                  values(w), values(style), 0.04, 1e-6)
+            assert_bits_equal(rd, g.h, f"residual {what}")
+            assert_bits_equal(go, g.gate_out, what)
+            assert_fp8(q, ref.q, ref.tie, what)
+    elif op == "gated_next":
+        wl = W.gated_residual(rows, hidden, seed=seed, per_token_gate=True)
+        t = wl.tensors
+        r = padded(t["residual"], pad_in)
+        y, buf = padded_out((rows, hidden), pad_out)
+        dn.dn_gated_residual_next_rmsnorm(padded(t["branch"], pad_in), r, padded(t["gate"], pad_in),
+                                          dev(t["w"]), dev(t["w_next"]), 1e-6, out=y)
+        ref = G.gated_residual_rmsnorm(values(t["branch"]), values(t["residual"]),
+                                       values(t["gate"]), values(t["w"]), 1e-6,
+                                       next_w=values(t["w_next"]))
+        assert_bf16(r, ref.h_exact, f"h {what}", mag=ref.h_mag)
+        assert_bf16(y, ref.y_exact, f"next {what}", mag=ref.y_mag)
+        assert_pads_untouched(buf, hidden, what)
+    elif op == "sigmoid_gate":
+        heads = int(rng.integers(1, 5))
+        hd = 8 * int(rng.integers(1, 33))
+        xs = W.normal((rows, heads * hd), seed, 5)
+        gs = W.normal((rows, heads * hd), seed, 6, std=2.0)
+        ws = W.normal((hd,), seed, 9, mean=1.0, std=0.1)
+        xp = padded(xs.reshape(-1, hd), pad_in)          # head rows hd + pad apart
+        dn.dn_rmsnorm_sigmoid_gate(xp, padded(gs.reshape(-1, hd), pad_in), 1e-6, weight=dev(ws))
+        s = S.rmsnorm_sigmoid_gate(values(xs).reshape(-1, hd), values(gs).reshape(-1, hd),
+                                   values(ws), 1e-6)
+        assert_bf16(xp, s.o_exact, what, mag=s.mag)
+    else:
+        res = W.normal((rows, hidden), seed, 1)
+        gr = W.normal((rows, hidden), seed, 3)
+        wf = W.normal((hidden,), seed, 4, std=0.02, dtype=torch.float32)
+        y, ybuf = padded_out((rows, hidden), pad_out)
+        hn, hbuf = padded_out((rows, hidden), pad_out)
+        rs = torch.empty(rows, dtype=torch.float32, device="cuda")
+        dn.dn_train_forward(xd, dev(wf), 1e-6, w_bias=1.0, residual=padded(res, pad_in), out=y,
+                            rstd=rs, residual_out=hn)
+        fwd = O.train_forward(values(x), values(wf), 1.0, 1e-6, residual=values(res))
+        assert_bits_equal(hn, fwd.h_new, f"h_new {what}")
+        assert_bf16(y, fwd.y_exact, f"y {what}")
+        assert_pads_untouched(ybuf, hidden, what)
+        assert_pads_untouched(hbuf, hidden, what)
+        g = W.normal((rows, hidden), seed, 6)
+        hb = torch.from_numpy(F.f64_to_bf16_bits(fwd.h_new).view(np.int16)).view(torch.bfloat16)
+        rsd = torch.from_numpy(fwd.rstd.astype(np.float32))
+        dx, dxbuf = padded_out((rows, hidden), pad_out)
+        dn.dn_train_backward(padded(g, pad_in), padded(hb, pad_in), dev(wf), dev(rsd), w_bias=1.0,
+                             g_residual=padded(gr, pad_in), dx=dx)
+        ref = O.train_backward(values(g), fwd.h_new, values(wf), rsd.double().numpy(), 1.0,
+                               values(gr))
+        assert_dx(dx, ref, f"dx {what}")
+        assert_pads_untouched(dxbuf, hidden, what)
