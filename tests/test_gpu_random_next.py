@@ -288,8 +288,7 @@ def test_random_numerics(dn, op, case):
         y, rstd = dn.dn_rmsnorm(dev(x), dev(w), eps, return_rstd=True)
         ref = O.rmsnorm(values(x), values(w), 0.0, eps)
         assert_bf16(y, ref.y_exact, what)
-        g = rstd.cpu().double().numpy()
-        assert np.all(np.abs(g - ref.r64) <= 2e-7 * ref.r64), f"rstd {what}"
+        assert_rstd(rstd, ref.r64, f"rstd {what}")
     elif op == "rmsnorm_quant":
         x = act(0)
         q = dn.dn_rmsnorm_quant(dev(x), dev(w), fp8_scale, eps)
@@ -332,7 +331,6 @@ def test_random_numerics(dn, op, case):
             q = dn.dn_fused_rmsnorm_silu(dev(x), dev(w), eps, output_fp8=True, scale=fp8_scale)
             _, ref = S.fused_rmsnorm_silu_fp8(values(x), values(w), fp8_scale, eps)
             assert_fp8(q, ref.q, ref.tie, what)
-
 
 
 @pytest.mark.parametrize("case", CASES)
