@@ -153,3 +153,17 @@ def test_kernel_resources_of_the_hot_path():
         r = res[k]
         assert r["scratch"] == 0 and r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, r
         assert r["agpr"] == 0, r
+
+
+def test_committed_counters_belong_to_the_committed_sources():
+    """Every committed HBM-counter summary was taken from the kernel sources in the tree (its
+    fingerprint matches), so bench.py reports the measured traffic rather than withholding
+    it; a kernel change without new counters fails here."""
+    want = bench.kernel_source_sha256()
+    families = ["rmsnorm", "configs", "layernorm", "qk_rope", "silu", "fixed_width"]
+    for fam in families:
+        with open(bench.traffic_path(fam)) as fh:
+            d = json.load(fh)
+        assert d.get("source_sha256") == want, f"{bench.traffic_path(fam)} is stale"
+    assert bench.measured_traffic("train_backward") is not None
+    assert bench.measured_traffic("fused_add_rmsnorm") is not None
