@@ -4,7 +4,7 @@
 scales) for the plain and quantised norms.  Each seed draws the shape (and the call's
 options), builds the inputs from the workload generators and checks the kernel against the
 FP64 oracle with the standard gates.  DN_RANDOM_SHAPES_NEXT (default 8) sets the number of
-seeds per test."""
+seeds per test, DN_RANDOM_FIRST_SEED (default 0) the first."""
 from __future__ import annotations
 
 import os
@@ -26,7 +26,8 @@ from tests.parity import (assert_bf16, assert_bits_equal, assert_block_quant, as
 
 pytestmark = pytest.mark.gpu
 
-CASES = list(range(int(os.environ.get("DN_RANDOM_SHAPES_NEXT", "8"))))
+_FIRST = int(os.environ.get("DN_RANDOM_FIRST_SEED", "0"))
+CASES = list(range(_FIRST, _FIRST + int(os.environ.get("DN_RANDOM_SHAPES_NEXT", "8"))))
 MAX_ELEMS = 1 << 20           # per tensor, so the oracle stays quick
 
 
